@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for the fused attention forward.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product library never imports this
+package, and this package imports nothing from the product.
+
+``attn_fwd_oracle`` runs the plain C implementation in ``attn_oracle.c`` (the
+textbook definition in fp64: scores, two-pass safe softmax over a materialised
+row, then P V; see that file's header for the citations).  ``build_oracle``
+compiles it with gcc.
+"""
+from .oracle import attn_fwd_oracle, build_oracle, oracle_lib_path  # noqa: F401

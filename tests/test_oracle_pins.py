@@ -1,0 +1,387 @@
+"""Pins for the fp64 CPU oracle: facts fixed by the pages and by mathematics,
+checked without trusting the oracle itself.
+
+Each test targets a part of the definition so that a plausible slip in the
+oracle (a dropped scale, a wrong head index, a transposed operand, a sign error
+in the causal offset, a missing max shift) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attn_fwd_oracle
+from exact_attention_19_amd.workloads import WORKLOADS, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_form_cases.json")
+
+
+def _num(x):
+    """Golden values are numbers or short closed-form strings."""
+    if isinstance(x, (int, float)):
+        return float(x)
+    env = {"ln3": math.log(3), "ln4": math.log(4), "sqrt3": math.sqrt(3),
+           "e": math.e, "ln": math.log, "inf": math.inf}
+    table = {"-inf": -math.inf, "ln3": math.log(3), "ln4": math.log(4)}
+    if x in table:
+        return table[x]
+    return float(eval(x.replace("ln(", "ln("), {"__builtins__": {}}, env))
+
+
+def _arr(rows):
+    return np.array([[_num(v) for v in r] for r in rows], dtype=np.float64)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand(seed, B, Sq, Sk, Hq, Hkv, d):
+    r = _rng(seed)
+    q = r.standard_normal((B, Sq, Hq, d))
+    k = r.standard_normal((B, Sk, Hkv, d))
+    v = r.standard_normal((B, Sk, Hkv, d))
+    return q, k, v
+
+
+def _scores(q, k, scale):
+    """Reference scores with numpy only, for the invariant tests:
+    s[b, h, i, j] with the GQA head mapping of the Qwen3-prefill page
+    (section 6), via an explicit repeat of the kv heads."""
+    B, Sq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    kk = np.repeat(k, Hq // Hkv, axis=2)
+    return scale * np.einsum("bihc,bjhc->bhij", q, kk)
+
+
+def _mask(Sq, Sk, causal):
+    j = np.arange(Sk)[None, :]
+    i = np.arange(Sq)[:, None]
+    if not causal:
+        return np.ones((Sq, Sk), bool)
+    return j <= i + (Sk - Sq)
+
+
+# ---------------------------------------------------------------- golden cases
+
+def test_closed_form_golden_cases():
+    data = json.load(open(GOLDEN))
+    for case in data["cases"]:
+        q = _arr(case["q"])[None, :, None, :]
+        k = _arr(case["k"])[None, :, None, :]
+        v = _arr(case["v"])[None, :, None, :]
+        o, lse = attn_fwd_oracle(q, k, v, case["scale"], case["causal"])
+        want_o = _arr(case["o"])
+        want_lse = np.array([_num(x) for x in case["lse"]])
+        np.testing.assert_allclose(o[0, :, 0, :], want_o, rtol=1e-14, atol=1e-14,
+                                   err_msg=case["name"])
+        fin = np.isfinite(want_lse)
+        np.testing.assert_allclose(lse[0, 0][fin], want_lse[fin], rtol=1e-14,
+                                   atol=1e-14, err_msg=case["name"])
+        assert np.all(np.isneginf(lse[0, 0][~fin])), case["name"]
+
+
+def test_gqa_mapping_matches_page_example():
+    """Query heads 2g and 2g+1 read kv head g (Qwen3-0.6B layout, Hq=16,
+    Hkv=8).  Each kv head gets a distinct constant V, so O identifies it."""
+    m = json.load(open(GOLDEN))["gqa_mapping"]
+    Hq, Hkv, d = m["Hq"], m["Hkv"], 4
+    r = _rng(3)
+    q = r.standard_normal((1, 5, Hq, d))
+    k = r.standard_normal((1, 7, Hkv, d))
+    v = np.zeros((1, 7, Hkv, d))
+    for h in range(Hkv):
+        v[:, :, h, :] = 100.0 + h
+    o, _ = attn_fwd_oracle(q, k, v, 0.5, True)
+    got = np.rint(o[0, :, :, 0] - 100.0).astype(int)  # (Sq, Hq)
+    for h in range(Hq):
+        assert np.all(got[:, h] == m["kv_head_of_q_head"][h])
+
+
+# ----------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Sk", [(16, 16), (9, 16), (16, 9), (1, 5), (5, 1)])
+def test_identity_v_gives_probability_rows(causal, Sq, Sk):
+    """With V = I (d = Sk) each output row is the probability row itself:
+    non-negative, zero on masked keys, summing to 1 (safe-softmax
+    normalisation of the personal-notes page, 'Online Softmax')."""
+    d = Sk
+    r = _rng(11)
+    q = r.standard_normal((1, Sq, 1, d))
+    k = r.standard_normal((1, Sk, 1, d))
+    v = np.eye(Sk)[None, :, None, :]
+    o, lse = attn_fwd_oracle(q, k, v, 0.7, causal)
+    P = o[0, :, 0, :]
+    mask = _mask(Sq, Sk, causal)
+    assert np.all(P >= 0)
+    assert np.all(P[~mask] == 0)
+    rows = mask.any(1)
+    np.testing.assert_allclose(P[rows].sum(1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(P[~rows] == 0)
+    # and P itself equals exp(s - lse) on visible keys
+    s = _scores(q, k, 0.7)[0, 0]
+    ref = np.where(mask, np.exp(s - lse[0, 0][:, None]), 0.0)
+    np.testing.assert_allclose(P[rows], ref[rows], rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v(causal):
+    q, k, _ = _rand(5, 2, 13, 21, 4, 2, 8)
+    v = np.full_like(k, -3.25)
+    o, _ = attn_fwd_oracle(q, k, v, 0.3, causal)
+    np.testing.assert_allclose(o, -3.25, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("Sq,Sk", [(12, 12), (7, 12), (12, 7)])
+def test_zero_q_gives_mean_of_visible_v(Sq, Sk):
+    """Q = 0 makes every score 0: O_i is the mean of the visible V rows and
+    LSE_i = ln |visible set|."""
+    _, k, v = _rand(6, 1, Sq, Sk, 2, 1, 4)
+    q = np.zeros((1, Sq, 2, 4))
+    o, lse = attn_fwd_oracle(q, k, v, 1.0, True)
+    for i in range(Sq):
+        n = min(Sk, max(0, i + Sk - Sq + 1))
+        for h in range(2):
+            if n == 0:
+                assert np.all(o[0, i, h] == 0) and np.isneginf(lse[0, h, i])
+            else:
+                np.testing.assert_allclose(o[0, i, h], v[0, :n, 0].mean(0),
+                                           rtol=1e-14, atol=1e-14)
+                assert abs(lse[0, h, i] - math.log(n)) < 1e-14
+
+
+def test_zero_q_noncausal_lse_is_log_sk():
+    _, k, v = _rand(7, 1, 5, 37, 1, 1, 8)
+    q = np.zeros((1, 5, 1, 8))
+    _, lse = attn_fwd_oracle(q, k, v, 1.0, False)
+    np.testing.assert_allclose(lse, math.log(37), rtol=0, atol=1e-14)
+
+
+def test_causal_row0_is_v0():
+    """Offset 0: row 0 sees only key 0, so o_0 = v_0 and lse_0 = s_00."""
+    q, k, v = _rand(8, 2, 10, 10, 4, 2, 16)
+    o, lse = attn_fwd_oracle(q, k, v, 0.25, True)
+    for b in range(2):
+        for h in range(4):
+            kvh = h // 2
+            np.testing.assert_array_equal(o[b, 0, h], v[b, 0, kvh])
+            assert lse[b, h, 0] == pytest.approx(
+                0.25 * float(q[b, 0, h] @ k[b, 0, kvh]), abs=1e-14)
+
+
+def test_single_key_every_row_is_v0():
+    q, k, v = _rand(9, 1, 6, 1, 3, 3, 8)
+    o, _ = attn_fwd_oracle(q, k, v, 0.9, False)
+    for i in range(6):
+        for h in range(3):
+            np.testing.assert_array_equal(o[0, i, h], v[0, 0, h])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_normalises_exp_scores(causal):
+    """sum_j exp(s_ij - lse_i) over visible j equals 1."""
+    q, k, v = _rand(10, 1, 20, 33, 2, 1, 8)
+    _, lse = attn_fwd_oracle(q, k, v, 0.6, causal)
+    s = _scores(q, k, 0.6)[0]
+    mask = _mask(20, 33, causal)
+    tot = np.where(mask[None], np.exp(s - lse[0][:, :, None]), 0).sum(-1)
+    np.testing.assert_allclose(tot, 1.0, rtol=0, atol=1e-13)
+
+
+def test_empty_rows_are_zero_and_minus_inf():
+    q, k, v = _rand(12, 1, 9, 4, 2, 2, 8)
+    o, lse = attn_fwd_oracle(q, k, v, 1.0, True)
+    # offset -5: rows 0..4 see nothing, row 5 sees key 0
+    assert np.all(o[0, :5] == 0) and np.all(np.isneginf(lse[0, :, :5]))
+    assert np.all(np.isfinite(lse[0, :, 5:]))
+    np.testing.assert_array_equal(o[0, 5, 0], v[0, 0, 0])
+
+
+# ---------------------------------------------- independent re-derivations
+
+def _online_softmax_attention(q, k, v, scale, causal, tile):
+    """The tile-by-tile recurrence of 'MiniPaged-Qwen' section 4 (running max
+    m, denominator l, unnormalised accumulator; alpha = exp(m_old - m_new)),
+    written independently of the oracle, with the empty-row guard alpha = 0
+    for m_old = -inf from section 13."""
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    o = np.zeros_like(q)
+    lse = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // g
+            for i in range(Sq):
+                m, l, acc = -np.inf, 0.0, np.zeros(d)
+                for j0 in range(0, Sk, tile):
+                    js = np.arange(j0, min(Sk, j0 + tile))
+                    s = scale * (k[b, js, kh] @ q[b, i, h])
+                    if causal:
+                        s = np.where(js <= i + Sk - Sq, s, -np.inf)
+                    mt = s.max()
+                    m_new = max(m, mt)
+                    if m_new == -np.inf:
+                        continue
+                    alpha = 0.0 if m == -np.inf else math.exp(m - m_new)
+                    p = np.exp(s - m_new)
+                    l = alpha * l + p.sum()
+                    acc = alpha * acc + p @ v[b, js, kh]
+                    m = m_new
+                if l == 0.0:
+                    o[b, i, h] = 0.0
+                    lse[b, h, i] = -np.inf
+                else:
+                    o[b, i, h] = acc / l
+                    lse[b, h, i] = m + math.log(l)
+    return o, lse
+
+
+@pytest.mark.parametrize("tile", [1, 3, 16, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_recurrence_equals_two_pass(tile, causal):
+    q, k, v = _rand(13, 1, 23, 150, 2, 1, 8)
+    o1, l1 = attn_fwd_oracle(q, k, v, 0.8, causal)
+    o2, l2 = _online_softmax_attention(q, k, v, 0.8, causal, tile)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def test_exp2_folding_identity():
+    """exp(x) = 2^(x log2 e): the base change the cuTile write-up folds into
+    the softmax scale."""
+    x = np.linspace(-80, 10, 1001)
+    np.testing.assert_allclose(np.exp(x), np.exp2(x * math.log2(math.e)),
+                               rtol=1e-13)
+
+
+def test_brute_force_python_loops():
+    """Pure-Python loops with math.exp on a tiny case."""
+    q, k, v = _rand(14, 1, 4, 6, 2, 1, 3)
+    scale = 0.9
+    o, lse = attn_fwd_oracle(q, k, v, scale, True)
+    for h in range(2):
+        for i in range(4):
+            vis = [j for j in range(6) if j <= i + 2]
+            s = [scale * sum(q[0, i, h, c] * k[0, j, 0, c] for c in range(3))
+                 for j in vis]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            for c in range(3):
+                want = sum(e[t] / z * v[0, j, 0, c] for t, j in enumerate(vis))
+                assert abs(o[0, i, h, c] - want) < 1e-14
+            assert abs(lse[0, h, i] - (mx + math.log(z))) < 1e-14
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_torch_fp64_cross_check(causal):
+    """torch CPU fp64: softmax(QK^T * scale + mask) @ V with an explicit boolean
+    mask; an independent library path, used as a check."""
+    q, k, v = _rand(15, 2, 37, 45, 4, 2, 16)
+    o, lse = attn_fwd_oracle(q, k, v, 0.3, causal)
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(np.repeat(k, 2, axis=2)).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(np.repeat(v, 2, axis=2)).permute(0, 2, 1, 3)
+    s = torch.matmul(tq, tk.transpose(-1, -2).contiguous()) * 0.3
+    m = torch.from_numpy(_mask(37, 45, causal))
+    s = s.masked_fill(~m, float("-inf"))
+    ref = torch.matmul(torch.softmax(s, dim=-1), tv).permute(0, 2, 1, 3)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(),
+                               rtol=0, atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_heads():
+    q, k, v = _rand(16, 2, 19, 23, 8, 2, 8)
+    o1, l1 = attn_fwd_oracle(q, k, v, 0.4, True)
+    o2, l2 = attn_fwd_oracle(q, np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2),
+                             0.4, True)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_bottom_right_alignment_is_tail_of_square_problem():
+    """Sq < Sk with bottom-right alignment equals the last Sq rows of the
+    square causal problem on Sk queries (the leading queries are arbitrary)."""
+    Sq, Sk = 7, 19
+    q, k, v = _rand(17, 1, Sq, Sk, 2, 1, 8)
+    lead = _rng(99).standard_normal((1, Sk - Sq, 2, 8))
+    qf = np.concatenate([lead, q], axis=1)
+    o1, l1 = attn_fwd_oracle(q, k, v, 0.5, True)
+    o2, l2 = attn_fwd_oracle(qf, k, v, 0.5, True)
+    np.testing.assert_array_equal(o1, o2[:, Sk - Sq:])
+    np.testing.assert_array_equal(l1, l2[:, :, Sk - Sq:])
+
+
+def test_noncausal_key_permutation_invariance():
+    q, k, v = _rand(18, 1, 8, 30, 2, 2, 8)
+    perm = _rng(5).permutation(30)
+    o1, l1 = attn_fwd_oracle(q, k, v, 0.5, False)
+    o2, l2 = attn_fwd_oracle(q, k[:, perm], v[:, perm], 0.5, False)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-14)
+
+
+def test_scale_is_applied_to_scores():
+    """Scaling Q by t with scale 1/t gives the same result (scores identical),
+    while a different scale changes it."""
+    q, k, v = _rand(19, 1, 5, 9, 1, 1, 4)
+    o1, _ = attn_fwd_oracle(q, k, v, 0.25, False)
+    o2, _ = attn_fwd_oracle(4 * q, k, v, 0.0625, False)
+    o3, _ = attn_fwd_oracle(q, k, v, 0.5, False)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    assert np.abs(o1 - o3).max() > 1e-3
+
+
+# ------------------------------------------------------------ API behaviour
+
+def test_row_subset_matches_full():
+    q, k, v = _rand(20, 2, 11, 13, 4, 2, 8)
+    o, lse = attn_fwd_oracle(q, k, v, 0.5, True)
+    rows = np.array([0, 5, 10, 11, 40, 87])  # flat (b*Hq + h)*Sq + i
+    os_, ls = attn_fwd_oracle(q, k, v, 0.5, True, rows=rows)
+    for n, f in enumerate(rows):
+        i, h, b = f % 11, (f // 11) % 4, f // 44
+        np.testing.assert_array_equal(os_[n], o[b, i, h])
+        assert ls[n] == lse[b, h, i]
+
+
+def test_thread_count_does_not_change_bits():
+    q, k, v = _rand(21, 1, 40, 40, 3, 1, 8)
+    o1, l1 = attn_fwd_oracle(q, k, v, 0.5, True, nthreads=1)
+    o2, l2 = attn_fwd_oracle(q, k, v, 0.5, True, nthreads=7)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_bad_arguments_rejected():
+    q, k, v = _rand(22, 1, 4, 4, 3, 2, 8)  # Hq % Hkv != 0
+    with pytest.raises(ValueError):
+        attn_fwd_oracle(q, k, v, 1.0, False)
+
+
+def test_workload_recipe_is_deterministic():
+    w = WORKLOADS["mha_tiny_f16_b1_h2_s128_d64"]
+    a = make_inputs(w, seed=0)
+    b = make_inputs(w, seed=0)
+    c = make_inputs(w, seed=1)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert not torch.equal(a[0], c[0])
+    assert a[0].dtype == torch.float16 and a[0].shape == (1, 128, 2, 64)
+
+
+def test_outlier_recipe_rows():
+    w = WORKLOADS["gqa8_causal_outlier_bf16_b1_hq32_hkv4_s16384_d128"].with_(
+        Sq=500, Sk=500, Hq=8, Hkv=2)
+    q, k, v = make_inputs(w, seed=0)
+    assert float(v.float().abs().max()) <= 1.0
+    # 5 rows per kv head scaled by 8: their norms stand out
+    for h in range(2):
+        nrm = k[0, :, h].float().norm(dim=-1)
+        assert int((nrm > 40).sum()) == 5
