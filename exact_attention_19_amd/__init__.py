@@ -1,0 +1,9 @@
+"""Fused exact-attention forward for AMD Instinct MI355X (gfx950).
+
+``attn_fwd`` runs the HIP kernel of ``libattn.so`` through its C ABI
+(``include/attn.h``).  The library is loaded on first use; if it has not been
+built, that call raises ImportError (there is no fallback path).
+"""
+from .binding import (  # noqa: F401
+    AttnError, attn_abi_version, attn_fwd, attn_fwd_check, attn_fwd_plan,
+    attn_status_str, load_library)

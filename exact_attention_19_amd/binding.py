@@ -1,0 +1,135 @@
+"""Thin ctypes binding of ``libattn.so`` (the C ABI of ``include/attn.h``).
+
+Argument marshalling only: every step of the attention forward runs in the HIP
+kernels of the library.  torch is used for device memory and the current
+stream.  There is no CPU fallback: if the library is missing, loading fails
+with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
+ATTN_DTYPE_F16, ATTN_DTYPE_BF16 = 0, 1
+EXPORTED = ("attn_fwd", "attn_fwd_check", "attn_fwd_plan", "attn_status_str",
+            "attn_abi_version")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {attn_status_str(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m exact_attention_19_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.restype = i
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd_check.restype = i
+    lib.attn_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i]
+    lib.attn_fwd_plan.restype = i
+    lib.attn_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i), i]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_status_str.argtypes = [i]
+    lib.attn_abi_version.restype = i
+    lib.attn_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def attn_status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def attn_abi_version() -> int:
+    return int(load_library().attn_abi_version())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return ATTN_DTYPE_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: q, k, v must be float16 or bfloat16")
+
+
+def attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype_code) -> dict:
+    """The launch attn_fwd would make (no device call)."""
+    out = (ctypes.c_int * 8)()
+    st = load_library().attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), dtype_code, out, 8)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_plan")
+    keys = ("grid", "threads", "rows_per_wg", "keys_per_tile", "heads_per_wg",
+            "rows_per_wave", "lds_bytes", "xcd_ordered")
+    return dict(zip(keys, list(out)))
+
+
+def attn_fwd_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Sq, Sk, Hq, Hkv, d,
+                   scale, causal, dtype_code) -> int:
+    """Validation only, on raw integer addresses; returns the status code."""
+    return int(load_library().attn_fwd_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr,
+                                             B, Sq, Sk, Hq, Hkv, d, float(scale),
+                                             int(causal), dtype_code))
+
+
+def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
+             out=None, lse=None, return_lse: bool = True, stream=None):
+    """O = softmax(scale * Q K^T + M) V and its LSE, on the GPU.
+
+    q: (B, Sq, Hq, d); k, v: (B, Sk, Hkv, d); fp16 or bf16 CUDA tensors, dense.
+    Returns (o, lse) with lse fp32 (B, Hq, Sq), or (o, None) if
+    return_lse is False.  The launch goes to ``stream`` (a torch.cuda.Stream)
+    or the current stream.
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (batch, seq, heads, d_head)")
+    B, Sq, Hq, d = q.shape
+    Bk, Sk, Hkv, dk = k.shape
+    if tuple(v.shape) != (Bk, Sk, Hkv, dk) or Bk != B or dk != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}")
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (batch, seq, heads, d_head)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq, Sq)):
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None,
+        B, Sq, Sk, Hq, Hkv, d, float(scale), int(bool(causal)), code,
+        ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+    return out, lse

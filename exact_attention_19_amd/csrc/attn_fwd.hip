@@ -1,0 +1,658 @@
+// Fused exact-attention forward for AMD Instinct MI355X (gfx950, CDNA4).
+//
+//   O = softmax(scale * Q K^T + M) V,   LSE = log of the softmax denominator
+//
+// The method is the tiled online-softmax evaluation described on the pages
+// ("MiniPaged-Qwen: Qwen3 prefill FlashAttention", sections 3-5 and 13;
+// "FlashAttention personal implementation notes", sections "Online Softmax"
+// and "FlashAttention"; the cuTile write-up's main loop, causal and GQA
+// sections): Q is tiled by query rows, K and V stream through on-chip memory
+// tile by tile, each query row keeps a running max m, a running denominator l
+// and an unnormalised accumulator, and the score matrix never leaves the chip.
+//
+// gfx950 mapping (the pages' CUDA designs are prior art; this is the CDNA4
+// layout):
+//
+// * One wave (64 lanes) owns QB blocks of 32 query rows of one query head.
+//   Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16
+//   (K tile rows as the A operand, Q rows as the B operand).  In the 32x32
+//   accumulator layout lane l holds column l%32, i.e. ONE query row, and 16 of
+//   the 32 keys; lanes l and l+32 hold the other 16 keys of the same row.
+//   Row max and row sum are therefore in-lane plus one v_permlane32_swap, and
+//   the rescale factor of the accumulator is a per-lane scalar.
+// * The K rows of each 32-key block are fed to the MFMA in a permuted order
+//   (sigma below) chosen so that the S^T accumulator, converted to 16 bit, is
+//   already the B operand of the second product O^T += V^T P^T: P never
+//   leaves registers.
+// * V^T fragments come straight from the row-major V tile in LDS through the
+//   gfx950 transpose read ds_read_b64_tr_b16.
+// * K and V tiles are double-buffered in LDS with a 16-byte XOR swizzle that
+//   keeps both the row reads of K and the transposed reads of V free of bank
+//   conflicts.
+// * Online softmax runs in the log2 domain (exp2 with scale*log2(e) folded
+//   into one FMA, as in the cuTile write-up's fast-math step).  The running
+//   max is only moved when a tile's max exceeds it by more than RESCALE_TAU
+//   (2^8): the result is mathematically identical, because numerator and
+//   denominator use the same stale max, and most tiles then skip the
+//   rescaling of the accumulator.
+// * The softmax denominator is accumulated by the matrix cores from the very
+//   16-bit probabilities that multiply V (an extra MFMA against a block of
+//   ones), so the normalisation O = sum P~ V / sum P~ uses one consistent set
+//   of rounded weights; for fp16 inputs P is carried as a hi + lo pair.
+// * Causal masking is applied only on the tiles that straddle the diagonal or
+//   the ragged end of K (the cuTile write-up's K-loop split); tiles above the
+//   diagonal are never visited (its causal loop bound).
+// * GQA: the waves of a workgroup are different query heads of one kv group
+//   (and/or consecutive row blocks), so every K/V tile loaded into LDS serves
+//   all of them.
+// * Work items are ordered heaviest-first (causal row blocks near the end of
+//   the sequence first) and, when the counts allow, grouped per XCD so that
+//   the workgroups sharing a kv head land on the same L2.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn.h"
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+#define LDS_PTR(T) __attribute__((address_space(3))) T*
+
+constexpr int BC = 64;              // keys per K/V tile
+constexpr float RESCALE_TAU = 8.0f; // log2 headroom before the max is moved
+constexpr float LN2 = 0.693147180559945309417f;
+
+// ---------------------------------------------------------------- dtypes
+template <int DT>
+struct Ty;
+
+template <>
+struct Ty<ATTN_DTYPE_BF16> {
+  static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ i16x8 cvt(f32x8 x) {
+    return __builtin_bit_cast(i16x8, __builtin_convertvector(x, bf16x8));
+  }
+  static constexpr short ONE = 0x3F80;  // 1.0 in bf16
+  static constexpr bool SPLIT_P = false;
+  // The sum of the bf16-rounded P normalises O, but one rounded dominant
+  // weight can move it by 2^-9 relative: the LSE uses an fp32 sum of the
+  // unrounded P instead.
+  static constexpr bool LSE_FROM_FP32_SUM = true;
+};
+
+template <>
+struct Ty<ATTN_DTYPE_F16> {
+  static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+        __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // fp32 -> fp16, round to nearest even (v_cvt_pk_f16_f32)
+  static __device__ __forceinline__ i16x8 cvt(f32x8 x) {
+    return __builtin_bit_cast(i16x8, __builtin_convertvector(x, f16x8));
+  }
+  static __device__ __forceinline__ f32x8 widen(i16x8 x) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x8, x), f32x8);
+  }
+  static constexpr short ONE = 0x3C00;  // 1.0 in fp16
+  // fp16 probabilities are carried as hi + lo halves (P = hi + lo to about
+  // 22 bits), so the P V product keeps fp32-level accuracy: the fp16
+  // tolerance leaves almost no room beside the output rounding of |O| >= 4.
+  static constexpr bool SPLIT_P = true;
+  static constexpr bool LSE_FROM_FP32_SUM = false;  // hi + lo sum is exact enough
+};
+
+// ------------------------------------------------------------ parameters
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int B, Sq, Sk, Hq, Hkv;
+  int group;     // Hq / Hkv
+  int gh;        // query heads per workgroup (divides group and the wave count)
+  int hsub;      // group / gh
+  int rows_wg;   // query rows per workgroup (per head)
+  int qtiles;    // ceil(Sq / rows_wg)
+  int ncols;     // B * Hkv * hsub
+  int xcd_cols;  // columns per XCD when the grid is XCD-ordered, else 0
+  int off;       // Sk - Sq
+  float scale_log2;  // scale * log2(e)
+};
+
+// 16-byte-chunk XOR swizzle of a K/V tile row in LDS.  Row r of the tile
+// stores its logical chunk s at physical chunk s ^ swz(r).  For d = 128 (16
+// chunks per 256-byte row) swz permutes the 16 rows of a K fragment onto 16
+// distinct bank groups, and puts the 4 consecutive rows of a V transpose read
+// on 4 disjoint bank-group quads; the d = 64 form does the same with 8 chunks
+// per row (two rows per 256-byte bank cycle).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Position of accumulator row m (of a 32x32 MFMA block) in the key order.
+// m = 8g + 4h + r  ->  key 16(g>>1) + 8h + 4(g&1) + r.  With this order the
+// 8 registers 8t'..8t'+7 of the S^T accumulator hold, in lane half h, keys
+// 16t' + 8h + 0..7: exactly the B-operand layout of a 32x32x16 MFMA over the
+// 16 keys 16t'..16t'+15.
+__device__ __forceinline__ int sigma(int m) {
+  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+}
+
+// Key offset (inside a 32-key block, minus 8*h) of accumulator register
+// 4g + r: the compile-time part of sigma.
+__device__ __forceinline__ constexpr int key_of_reg(int reg) {
+  return 16 * ((reg >> 2) >> 1) + 4 * ((reg >> 2) & 1) + (reg & 3);
+}
+
+__device__ __forceinline__ float other_half_max(float x) {
+  // v_permlane32_swap(x, x) returns {x of lanes 0-31 in both halves,
+  // x of lanes 32-63 in both halves}: their max is the max over the lane pair.
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                            __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// ------------------------------------------------------ the main kernel
+template <int DT, int D, bool CAUSAL, int NW, int QB>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(Params p) {
+  using T = Ty<DT>;
+  constexpr int NT = NW * 64;
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int CPT = BC * CPR / NT;      // chunks per thread per tile
+  constexpr int KB = BC / 32;             // 32-key blocks per tile
+  constexpr int CB = D / 32;              // 32-wide d blocks
+  constexpr int KK = D / 16;              // k-steps of the S^T product
+  constexpr int TILE = BC * D;            // elements per K (or V) tile
+  static_assert(CPT * NT == BC * CPR, "tile must split evenly over threads");
+
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  // [buf][K|V][BC*D]
+  LDS_PTR(uint16_t) lds = (LDS_PTR(uint16_t))smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- work decode: heaviest row blocks first, optionally grouped per XCD
+  int qt, col;
+  {
+    const int L = blockIdx.x;
+    if (p.xcd_cols > 0) {
+      const int xcd = L & 7;
+      const int k = L >> 3;
+      qt = p.qtiles - 1 - k / p.xcd_cols;
+      col = xcd * p.xcd_cols + k % p.xcd_cols;
+    } else {
+      qt = p.qtiles - 1 - L / p.ncols;
+      col = L % p.ncols;
+    }
+  }
+  const int hs = col % p.hsub;
+  const int kvh = (col / p.hsub) % p.Hkv;
+  const int b = col / (p.hsub * p.Hkv);
+  const int head_in_wg = wave % p.gh;
+  const int rowblk = wave / p.gh;
+  const int hq = kvh * p.group + hs * p.gh + head_in_wg;
+  const int q0wg = qt * p.rows_wg;
+  const int q0w = q0wg + rowblk * (32 * QB);
+
+  // ---- KV tile range of the workgroup and of this wave
+  const int q_last_wg = min(q0wg + p.rows_wg, p.Sq) - 1;
+  int kv_end = p.Sk;
+  if (CAUSAL) kv_end = min(p.Sk, q_last_wg + p.off + 1);
+  const int n_end = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  int n_full = p.Sk / BC;
+  if (CAUSAL) {
+    const int lim = q0wg + p.off + 1;
+    n_full = min(n_full, lim > 0 ? lim / BC : 0);
+  }
+  n_full = min(n_full, n_end);
+  int w_end = 0;
+  if (q0w < p.Sq) {
+    const int q_last_w = min(q0w + 32 * QB, p.Sq) - 1;
+    int e = p.Sk;
+    if (CAUSAL) e = min(p.Sk, q_last_w + p.off + 1);
+    w_end = e > 0 ? (e + BC - 1) / BC : 0;
+  }
+
+  const int64_t kv_row_stride = (int64_t)p.Hkv * D;  // elements between keys
+  const uint16_t* kbase = p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
+  const uint16_t* vbase = p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
+  i16x8 qf[QB][KK];
+#pragma unroll
+  for (int nb = 0; nb < QB; ++nb) {
+    const int qi = q0w + nb * 32 + l32;
+    const bool ok = qi < p.Sq;
+    const uint16_t* qrow =
+        p.q + (((int64_t)b * p.Sq + (ok ? qi : 0)) * p.Hq + hq) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (ok) x = *(const u32x4*)(qrow + kk * 16 + hh * 8);
+      qf[nb][kk] = __builtin_bit_cast(i16x8, x);
+    }
+  }
+
+  // ---- online-softmax state and output accumulator (O^T, one query/lane)
+  f32x16 acc_o[CB][QB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int nb = 0; nb < QB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[cb][nb][r] = 0.f;
+  // The running max starts at a finite, very negative value: any finite score
+  // moves it (exp2 of the difference underflows to 0 for the empty
+  // accumulator), and masked scores (-inf) give exp2(-inf) = 0 against it.
+  float m_run[QB];
+  f32x16 acc_l[QB];  // row sums of the rounded P: every register holds it
+  float l_fp32[QB];  // per-lane partial sums of the unrounded P (for the LSE)
+#pragma unroll
+  for (int nb = 0; nb < QB; ++nb) {
+    m_run[nb] = -1e30f;
+    l_fp32[nb] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_l[nb][r] = 0.f;
+  }
+  const i16x8 ones = {T::ONE, T::ONE, T::ONE, T::ONE, T::ONE, T::ONE, T::ONE, T::ONE};
+  // per-lane causal / ragged limit: the last visible key of this lane's rows
+  int lim_row[QB];
+#pragma unroll
+  for (int nb = 0; nb < QB; ++nb) {
+    const int qi = q0w + nb * 32 + l32;
+    int lim = p.Sk - 1;
+    if (CAUSAL) lim = min(lim, qi + p.off);
+    lim_row[nb] = lim;
+  }
+
+  // ---- global -> register -> LDS tile copy
+  u32x4 kreg[CPT], vreg[CPT];
+  auto load_tile = [&](int n) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int ci = u * NT + tid;
+      const int row = ci / CPR;
+      const int s = ci % CPR;
+      const int j = n * BC + row;
+      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+      if (j < p.Sk) {
+        kx = *(const u32x4*)(kbase + (int64_t)j * kv_row_stride + s * 8);
+        vx = *(const u32x4*)(vbase + (int64_t)j * kv_row_stride + s * 8);
+      }
+      kreg[u] = kx;
+      vreg[u] = vx;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    LDS_PTR(uint16_t) kd = lds + buf * 2 * TILE;
+    LDS_PTR(uint16_t) vd = kd + TILE;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int ci = u * NT + tid;
+      const int row = ci / CPR;
+      const int s = ci % CPR;
+      const int off = row * D + ((s ^ swz<D>(row)) << 3);
+      *(LDS_PTR(u32x4))(kd + off) = kreg[u];
+      *(LDS_PTR(u32x4))(vd + off) = vreg[u];
+    }
+  };
+
+  // ---- one K/V tile: S^T, (mask), online softmax, O^T += V^T P^T
+  auto step = [&](int n, int buf, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    LDS_PTR(const uint16_t) kt = lds + buf * 2 * TILE;
+    LDS_PTR(const uint16_t) vt = kt + TILE;
+
+    // S^T = K Q^T over the BC keys of the tile, fp32 accumulate
+    f32x16 s[KB][QB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int nb = 0; nb < QB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][nb][r] = 0.f;
+      const int row = kb * 32 + sigma(l32);
+      const int sw = swz<D>(row);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int chunk = 2 * kk + hh;
+        const i16x8 kf = *(LDS_PTR(const i16x8))(kt + row * D + ((chunk ^ sw) << 3));
+#pragma unroll
+        for (int nb = 0; nb < QB; ++nb) s[kb][nb] = T::mfma(kf, qf[nb][kk], s[kb][nb]);
+      }
+    }
+
+    // mask the straddling tiles: key index vs the lane's limit
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int nb = 0; nb < QB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int L = lim_row[nb] - n * BC - kb * 32 - 8 * hh;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key_of_reg(r) > L) s[kb][nb][r] = -INFINITY;
+        }
+    }
+
+    // online softmax (log2 domain)
+    float mt[QB];
+    bool any_rescale = false;
+#pragma unroll
+    for (int nb = 0; nb < QB; ++nb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][nb][r]);
+      mx = other_half_max(mx) * p.scale_log2;
+      mt[nb] = mx;
+      any_rescale |= mx > m_run[nb] + RESCALE_TAU;
+    }
+    if (__builtin_amdgcn_ballot_w64(any_rescale) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < QB; ++nb) {
+        const float m_new = fmaxf(m_run[nb], mt[nb]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new);
+        m_run[nb] = m_new;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_l[nb][r] *= alpha;
+        if constexpr (T::LSE_FROM_FP32_SUM) l_fp32[nb] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[cb][nb][r] *= alpha;
+      }
+    }
+    i16x8 pf[QB][BC / 16];
+    i16x8 pf_lo[QB][BC / 16];  // fp16 only: p - hi, rounded
+#pragma unroll
+    for (int nb = 0; nb < QB; ++nb) {
+      const float neg_m = -m_run[nb];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          f32x8 e;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            e[r] = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(s[kb][nb][half * 8 + r], p.scale_log2, neg_m));
+            if constexpr (T::LSE_FROM_FP32_SUM) l_fp32[nb] += e[r];
+          }
+          const i16x8 hi = T::cvt(e);
+          pf[nb][kb * 2 + half] = hi;
+          if constexpr (T::SPLIT_P) pf_lo[nb][kb * 2 + half] = T::cvt(e - T::widen(hi));
+        }
+    }
+
+    // O^T += V^T P^T: V^T fragments by LDS transpose reads
+#pragma unroll
+    for (int t = 0; t < BC / 16; ++t) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int g16 = lane >> 4;
+        const int s16 = lane & 15;
+        const int c = cb * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
+        const int chunk = c >> 3;
+        const int within = c & 7;
+        i16x4 lo, hi;
+        {
+          const int row = 16 * t + 8 * (g16 >> 1) + (s16 >> 2);
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (LDS_PTR(i16x4))(vt + row * D + ((chunk ^ swz<D>(row)) << 3) + within));
+        }
+        {
+          const int row = 16 * t + 8 * (g16 >> 1) + 4 + (s16 >> 2);
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (LDS_PTR(i16x4))(vt + row * D + ((chunk ^ swz<D>(row)) << 3) + within));
+        }
+        const i16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int nb = 0; nb < QB; ++nb) {
+          acc_o[cb][nb] = T::mfma(vf, pf[nb][t], acc_o[cb][nb]);
+          if constexpr (T::SPLIT_P) acc_o[cb][nb] = T::mfma(vf, pf_lo[nb][t], acc_o[cb][nb]);
+        }
+      }
+      // row sums of exactly the 16-bit P that multiplied V
+#pragma unroll
+      for (int nb = 0; nb < QB; ++nb) {
+        acc_l[nb] = T::mfma(ones, pf[nb][t], acc_l[nb]);
+        if constexpr (T::SPLIT_P) acc_l[nb] = T::mfma(ones, pf_lo[nb][t], acc_l[nb]);
+      }
+    }
+  };
+
+  if (n_end > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+  int n = 0;
+  for (; n < n_full; ++n) {
+    const int buf = n & 1;
+    if (n + 1 < n_end) load_tile(n + 1);
+    if (n < w_end) step(n, buf, std::false_type{});
+    if (n + 1 < n_end) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  for (; n < n_end; ++n) {
+    const int buf = n & 1;
+    if (n + 1 < n_end) load_tile(n + 1);
+    if (n < w_end) step(n, buf, std::true_type{});
+    if (n + 1 < n_end) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
+#pragma unroll
+  for (int nb = 0; nb < QB; ++nb) {
+    const int qi = q0w + nb * 32 + l32;
+    const float l_tot = acc_l[nb][0];
+    const bool has = l_tot > 0.f;
+    const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+    float l_lse = l_tot;
+    if constexpr (T::LSE_FROM_FP32_SUM) {
+      // lanes l and l+32 hold the two halves of the row's keys (all lanes
+      // active here)
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_fp32[nb]),
+                                                __float_as_uint(l_fp32[nb]), false, false);
+      l_lse = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if (qi < p.Sq) {
+      uint16_t* orow = p.o + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x8 x;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[r] = acc_o[cb][nb][4 * g + r] * inv;
+            x[r + 4] = 0.f;
+          }
+          const i16x8 y = T::cvt(x);
+          const u32x2 w = {(unsigned)(uint16_t)y[0] | ((unsigned)(uint16_t)y[1] << 16),
+                           (unsigned)(uint16_t)y[2] | ((unsigned)(uint16_t)y[3] << 16)};
+          *(u32x2*)(orow + cb * 32 + 8 * g + 4 * hh) = w;
+        }
+      if (p.lse != nullptr && hh == 0) {
+        const float lse = has ? (m_run[nb] + __builtin_amdgcn_logf(l_lse)) * LN2 : -INFINITY;
+        p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] = lse;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ host side
+struct Plan {
+  int nw, qb, gh, rows_wg, qtiles, ncols, xcd_cols, grid, lds_bytes;
+};
+
+bool sizes_ok(int B, int Sq, int Sk, int Hq, int Hkv) {
+  return B >= 1 && Sq >= 1 && Sk >= 1 && Hq >= 1 && Hkv >= 1;
+}
+
+attn_status validate(const void* q, const void* k, const void* v, void* o,
+                     const float* lse, int B, int Sq, int Sk, int Hq, int Hkv,
+                     int d, float scale, int causal, int dtype) {
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+  if (!sizes_ok(B, Sq, Sk, Hq, Hkv) || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
+    return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)lse) & 3u) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // index-space limits: positions and per-tensor row counts stay in int32
+  // arithmetic inside the kernel; element offsets are 64-bit.
+  if ((int64_t)Sq + Sk >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31))
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
+  (void)Sk;
+  (void)causal;
+  (void)d;
+  Plan pl{};
+  pl.nw = 4;
+  const int group = Hq / Hkv;
+  int gh = 1;
+  while (gh * 2 <= pl.nw && group % (gh * 2) == 0) gh *= 2;
+  pl.gh = gh;
+  const int hsub = group / gh;
+  pl.ncols = B * Hkv * hsub;
+  auto count = [&](int qb) {
+    const int rows = (pl.nw / gh) * 32 * qb;
+    const long long qt = (Sq + rows - 1) / rows;
+    return qt * (long long)pl.ncols;
+  };
+  (void)count;
+  pl.qb = 1;
+  pl.rows_wg = (pl.nw / gh) * 32 * pl.qb;
+  pl.qtiles = (Sq + pl.rows_wg - 1) / pl.rows_wg;
+  pl.xcd_cols = (pl.ncols % 8 == 0) ? pl.ncols / 8 : 0;
+  const long long grid = (long long)pl.qtiles * pl.ncols;
+  pl.grid = grid > 0x7fffffffll ? -1 : (int)grid;
+  pl.lds_bytes = 2 * 2 * BC * d * 2;
+  return pl;
+}
+
+template <int DT, int D, bool CAUSAL>
+hipError_t launch_t(const Plan& pl, const Params& p, hipStream_t st) {
+  dim3 grid(pl.grid), block(pl.nw * 64);
+  hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, 4, 1>), grid, block, pl.lds_bytes, st, p);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_d(int d, bool causal, const Plan& pl, const Params& p, hipStream_t st) {
+  if (d == 128)
+    return causal ? launch_t<DT, 128, true>(pl, p, st) : launch_t<DT, 128, false>(pl, p, st);
+  return causal ? launch_t<DT, 64, true>(pl, p, st) : launch_t<DT, 64, false>(pl, p, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_check(const void* q, const void* k, const void* v, void* o,
+                           float* lse, int B, int Sq, int Sk, int Hq, int Hkv,
+                           int d, float scale, int causal, int dtype) {
+  attn_status st = validate(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
+  if (st != ATTN_OK) return st;
+  const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
+  if (pl.grid <= 0) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
+                          int causal, int dtype, int* out, int n) {
+  // validation with stand-in aligned pointers (sizes only)
+  static const uint64_t dummy[2] = {0, 0};
+  const void* pp = (const void*)(((uintptr_t)dummy + 15) & ~(uintptr_t)15);
+  attn_status st = attn_fwd_check(pp, pp, pp, (void*)pp, nullptr, B, Sq, Sk, Hq,
+                                  Hkv, d, 1.0f, causal, dtype);
+  if (st != ATTN_OK) return st;
+  const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
+  const int vals[8] = {pl.grid, pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
+                       pl.lds_bytes, pl.xcd_cols > 0 ? 1 : 0};
+  for (int i = 0; i < n && i < 8; ++i) out[i] = vals[i];
+  return ATTN_OK;
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int d,
+                     float scale, int causal, int dtype, void* stream) {
+  attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
+  if (st != ATTN_OK) return st;
+  const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
+  Params p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.gh = pl.gh;
+  p.hsub = p.group / pl.gh;
+  p.rows_wg = pl.rows_wg;
+  p.qtiles = pl.qtiles;
+  p.ncols = pl.ncols;
+  p.xcd_cols = pl.xcd_cols;
+  p.off = Sk - Sq;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = dtype == ATTN_DTYPE_BF16
+                     ? launch_d<ATTN_DTYPE_BF16>(d, causal != 0, pl, p, hs)
+                     : launch_d<ATTN_DTYPE_F16>(d, causal != 0, pl, p, hs);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head size or dtype";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"
