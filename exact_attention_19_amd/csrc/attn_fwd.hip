@@ -28,7 +28,8 @@
 //   gfx950 transpose read ds_read_b64_tr_b16.
 // * K and V tiles are double-buffered in LDS with a 16-byte XOR swizzle that
 //   keeps both the row reads of K and the transposed reads of V free of bank
-//   conflicts.
+//   conflicts.  Tiles go global -> LDS with gfx950 direct-to-LDS loads
+//   (global_load_lds_dwordx4), so the prefetch holds no registers.
 // * Online softmax runs in the log2 domain (exp2 with scale*log2(e) folded
 //   into one FMA, as in the cuTile write-up's fast-math step).  The running
 //   max is only moved when a tile's max exceeds it by more than RESCALE_TAU
@@ -69,6 +70,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
+#define GLOBAL_PTR(T) __attribute__((address_space(1))) T*
 
 constexpr int BC = 64;              // keys per K/V tile
 constexpr float RESCALE_TAU = 8.0f; // log2 headroom before the max is moved
@@ -175,7 +177,7 @@ __device__ __forceinline__ float other_half_max(float x) {
 
 // ------------------------------------------------------ the main kernel
 template <int DT, int D, bool CAUSAL, int NW, int QB>
-__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   using T = Ty<DT>;
   constexpr int NT = NW * 64;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -290,35 +292,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(Params p) {
     lim_row[nb] = lim;
   }
 
-  // ---- global -> register -> LDS tile copy
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int n) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int ci = u * NT + tid;
-      const int row = ci / CPR;
-      const int s = ci % CPR;
-      const int j = n * BC + row;
-      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (j < p.Sk) {
-        kx = *(const u32x4*)(kbase + (int64_t)j * kv_row_stride + s * 8);
-        vx = *(const u32x4*)(vbase + (int64_t)j * kv_row_stride + s * 8);
-      }
-      kreg[u] = kx;
-      vreg[u] = vx;
-    }
-  };
-  auto store_tile = [&](int buf) {
+  // ---- global -> LDS tile copy (direct-to-LDS loads, no registers)
+  // Each global_load_lds_dwordx4 of a wave writes 64 consecutive 16-byte
+  // chunks of LDS; lane l picks as its source the logical chunk that the
+  // swizzle places at physical chunk (base + l).  Rows past the end of K/V
+  // re-read the last row: those keys are masked to -inf, so P = 0 there and
+  // the finite values never reach O.
+  auto issue_tile = [&](int n, int buf) {
     LDS_PTR(uint16_t) kd = lds + buf * 2 * TILE;
     LDS_PTR(uint16_t) vd = kd + TILE;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int ci = u * NT + tid;
+      const int cbase = (u * NW + wave) * 64;
+      const int ci = cbase + lane;
       const int row = ci / CPR;
-      const int s = ci % CPR;
-      const int off = row * D + ((s ^ swz<D>(row)) << 3);
-      *(LDS_PTR(u32x4))(kd + off) = kreg[u];
-      *(LDS_PTR(u32x4))(vd + off) = vreg[u];
+      const int slot = ci % CPR;
+      const int sc = slot ^ swz<D>(row);
+      const int j = min(n * BC + row, p.Sk - 1);
+      const int64_t goff = (int64_t)j * kv_row_stride + sc * 8;
+      __builtin_amdgcn_global_load_lds((const GLOBAL_PTR(void))(kbase + goff),
+                                       (LDS_PTR(void))(kd + cbase * 8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const GLOBAL_PTR(void))(vbase + goff),
+                                       (LDS_PTR(void))(vd + cbase * 8), 16, 0, 0);
     }
   };
 
@@ -448,24 +443,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(Params p) {
     }
   };
 
-  if (n_end > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
+  // __syncthreads() waits for all outstanding loads (vmcnt(0)) before the
+  // barrier, which publishes a tile written by the direct loads.
+  if (n_end > 0) issue_tile(0, 0);
+  __syncthreads();
   int n = 0;
   for (; n < n_full; ++n) {
     const int buf = n & 1;
-    if (n + 1 < n_end) load_tile(n + 1);
+    if (n + 1 < n_end) issue_tile(n + 1, buf ^ 1);
     if (n < w_end) step(n, buf, std::false_type{});
-    if (n + 1 < n_end) store_tile(buf ^ 1);
     __syncthreads();
   }
   for (; n < n_end; ++n) {
     const int buf = n & 1;
-    if (n + 1 < n_end) load_tile(n + 1);
+    if (n + 1 < n_end) issue_tile(n + 1, buf ^ 1);
     if (n < w_end) step(n, buf, std::true_type{});
-    if (n + 1 < n_end) store_tile(buf ^ 1);
     __syncthreads();
   }
 
