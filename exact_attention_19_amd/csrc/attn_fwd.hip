@@ -90,6 +90,18 @@ struct Ty<ATTN_DTYPE_BF16> {
   static __device__ __forceinline__ i16x8 cvt(f32x8 x) {
     return __builtin_bit_cast(i16x8, __builtin_convertvector(x, bf16x8));
   }
+  // acc + the sum of the 8 bf16 values of x (v_dot2_f32_bf16 against 1.0:
+  // exact products, fp32 accumulate)
+  static __device__ __forceinline__ float sum8(i16x8 x, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(
+          __builtin_bit_cast(bf16x2, (short __attribute__((ext_vector_type(2)))){x[2 * i], x[2 * i + 1]}),
+          one, acc, false);
+    return acc;
+  }
   static constexpr short ONE = 0x3F80;  // 1.0 in bf16
   static constexpr bool SPLIT_P = false;
   // The sum of the bf16-rounded P normalises O, but one rounded dominant
@@ -110,6 +122,17 @@ struct Ty<ATTN_DTYPE_F16> {
   }
   static __device__ __forceinline__ f32x8 widen(i16x8 x) {
     return __builtin_convertvector(__builtin_bit_cast(f16x8, x), f32x8);
+  }
+  // acc + the sum of the 8 fp16 values of x (v_dot2_f32_f16 against 1.0)
+  static __device__ __forceinline__ float sum8(i16x8 x, float acc) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2(
+          __builtin_bit_cast(f16x2, (short __attribute__((ext_vector_type(2)))){x[2 * i], x[2 * i + 1]}),
+          one, acc, false);
+    return acc;
   }
   static constexpr short ONE = 0x3C00;  // 1.0 in fp16
   // fp16 probabilities are carried as hi + lo halves (P = hi + lo to about
@@ -501,9 +524,421 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   }
 }
 
+// ------------------------------------- the software-pipelined kernel
+//
+// Same tile math as attn_fwd_kernel (one wave = 32 query rows of one head,
+// the waves of a workgroup share every K/V tile), but the work of a tile is
+// skewed across loop iterations so that each iteration hands the vector ALU
+// and the matrix core independent work:
+//
+//   iteration j:  softmax(S(j)) -> P(j)            [VALU: max, exp2, convert]
+//                 O += V(j-1)^T P(j-1)             [MFMA, previous tile]
+//                 S(j+1) = K(j+1) Q^T              [MFMA, next tile]
+//
+// The three streams have no dependencies among them inside the iteration, so
+// the compiler interleaves exp/convert instructions between the MFMAs of the
+// same wave, and two waves per SIMD fill each other's LDS waits.  K runs one
+// tile ahead of V: iteration j reads K(j+1) and V(j-1) while K(j+2) and V(j)
+// stream in, so two K and two V buffers live in LDS.
+//
+// The thresholded max update is decided at the start of an iteration from
+// S(j); the rescale of the accumulators by alpha(j) is applied at the END of
+// the iteration, after O has absorbed V(j-1)^T P(j-1), whose probabilities
+// were taken against the previous max.
+template <typename PT>
+struct PFrag {
+  PT hi[BC / 16];
+  PT lo[BC / 16];  // fp16 only (hi + lo split); unused for bf16
+};
+
+template <int DT, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p) {
+  using T = Ty<DT>;
+  constexpr int NT = NW * 64;
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int CPT = BC * CPR / NT;  // direct loads per lane per tile
+  constexpr int KB = BC / 32;
+  constexpr int CB = D / 32;
+  constexpr int KK = D / 16;
+  constexpr int NP = BC / 16;
+  constexpr int TB = BC * D * 2;      // bytes per K or V tile buffer
+  constexpr int KBUF0 = 0;            // K buffers: 0, TB
+  constexpr int VBUF0 = 2 * TB;       // V buffers: 2TB, 3TB
+  static_assert(CPT * NT == BC * CPR, "tile must split evenly over threads");
+  static_assert(CPT == CB, "one load round per 32-column block");
+
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  LDS_PTR(char) lds = (LDS_PTR(char))smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- work decode: heaviest row blocks first, optionally grouped per XCD
+  int qt, col;
+  {
+    const int L = blockIdx.x;
+    if (p.xcd_cols > 0) {
+      const int xcd = L & 7;
+      const int k = L >> 3;
+      qt = p.qtiles - 1 - k / p.xcd_cols;
+      col = xcd * p.xcd_cols + k % p.xcd_cols;
+    } else {
+      qt = p.qtiles - 1 - L / p.ncols;
+      col = L % p.ncols;
+    }
+  }
+  const int hs = col % p.hsub;
+  const int kvh = (col / p.hsub) % p.Hkv;
+  const int b = col / (p.hsub * p.Hkv);
+  const int head_in_wg = wave % p.gh;
+  const int rowblk = wave / p.gh;
+  const int hq = kvh * p.group + hs * p.gh + head_in_wg;
+  const int q0wg = qt * p.rows_wg;
+  const int q0w = q0wg + rowblk * 32;
+
+  // ---- KV tile range of the workgroup (all waves walk the same tiles)
+  const int q_last_wg = min(q0wg + p.rows_wg, p.Sq) - 1;
+  int kv_end = p.Sk;
+  if (CAUSAL) kv_end = min(p.Sk, q_last_wg + p.off + 1);
+  const int n_end = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  int n_full = p.Sk / BC;
+  if (CAUSAL) {
+    const int lim = q0wg + p.off + 1;
+    n_full = min(n_full, lim > 0 ? lim / BC : 0);
+  }
+  n_full = min(n_full, n_end);
+
+  const int64_t kv_row_stride = (int64_t)p.Hkv * D;
+  const uint16_t* kbase = p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
+  const uint16_t* vbase = p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
+
+  // ---- LDS tile layout of this kernel: column-blocked.  A K or V tile is
+  // stored as D/32 blocks of 32 columns; block cb holds the 64 rows of those
+  // columns, 64 bytes (four 16-byte chunks) per row, and chunk c of row r
+  // sits at slot c ^ ((r >> 2) & 3).  Every fragment address is then a
+  // per-lane base plus compile-time offsets for the column block and the row
+  // group, and both read patterns are free of bank conflicts: the 16 rows of
+  // a K fragment row read land on 16 distinct 16-byte slots of one 256-byte
+  // bank cycle, and the 4 rows x 64 bytes of a V transpose read of 32 lanes
+  // fill one bank cycle exactly.
+  constexpr int BLK = 64 * 64;  // bytes per column block of a tile
+  // K fragment (kb, kk): row 32kb + sigma(l32), logical chunk 2kk + hh, i.e.
+  // block kk/2, in-block chunk 2(kk&1) + hh.
+  uint32_t kbase_lds[2];
+  {
+    const int row = sigma(l32);
+    const int sw = (row >> 2) & 3;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      kbase_lds[par] = (uint32_t)(row * 64 + (((2 * par + hh) ^ sw) << 4));
+  }
+  // V^T fragment (t, cb, half): transpose read of rows 16t + 8(g16>>1) +
+  // 4half + (s16>>2), columns 32cb + 16(g16&1) + 4(s16&3).
+  uint32_t vbase_lds[2];
+  {
+    const int g16 = lane >> 4;
+    const int s16 = lane & 15;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 8 * (g16 >> 1) + 4 * half + (s16 >> 2);
+      const int cc = 16 * (g16 & 1) + 4 * (s16 & 3);  // column inside the block
+      vbase_lds[half] =
+          (uint32_t)(row * 64 + ((((cc >> 3) ^ ((row >> 2) & 3))) << 4) + (cc & 7) * 2);
+    }
+  }
+  auto k_addr = [&](int kbuf, int kb, int kk) {
+    return kbuf + (kk >> 1) * BLK + kb * 32 * 64 + kbase_lds[kk & 1];
+  };
+  auto v_addr = [&](int vbuf, int t, int cb, int half) {
+    return vbuf + cb * BLK + t * 16 * 64 + vbase_lds[half];
+  };
+  // Direct global -> LDS load round u of a wave writes LDS bytes
+  // [(u*NW + wave) * 1024, +1024) of the tile: block (u*NW + wave) / 4, rows
+  // 16 * ((u*NW + wave) % 4) + lane / 4, slot lane % 4.
+  static_assert(NW == 4, "the load mapping assumes four waves");
+  const int ld_row = 16 * wave + (lane >> 2);
+  const int ld_chunk = (lane & 3) ^ ((ld_row >> 2) & 3);
+  const int ld_col = ld_chunk * 8;  // + 32 * u: the column block of round u
+
+  auto issue_rows = [&](const uint16_t* gbase, int n, int lds_byte_base) {
+    int j = n * BC + ld_row;
+    if ((n + 1) * BC > p.Sk) j = min(j, p.Sk - 1);  // masked keys: any finite row
+    const uint16_t* src = gbase + (int64_t)j * kv_row_stride + ld_col;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+      __builtin_amdgcn_global_load_lds((const GLOBAL_PTR(void))(src + 32 * u),
+                                       (LDS_PTR(void))(lds + lds_byte_base + (u * NW + wave) * 1024),
+                                       16, 0, 0);
+  };
+
+  // ---- Q fragments, kept in registers
+  i16x8 qf[KK];
+  {
+    const int qi = q0w + l32;
+    const bool ok = qi < p.Sq;
+    const uint16_t* qrow = p.q + (((int64_t)b * p.Sq + (ok ? qi : 0)) * p.Hq + hq) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (ok) x = *(const u32x4*)(qrow + kk * 16 + hh * 8);
+      qf[kk] = __builtin_bit_cast(i16x8, x);
+    }
+  }
+
+  // ---- state: O^T, running max, and per-lane partial row sums (the lane
+  // holds half of its row's keys; lanes l and l+32 are combined at the end):
+  // l_rnd sums exactly the 16-bit P that multiply V, so O is normalised by a
+  // consistent set of weights; l_fp32 sums the unrounded P for the LSE.
+  f32x16 acc_o[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[cb][r] = 0.f;
+  float m_run = -1e30f;
+  float l_rnd = 0.f;
+  float l_fp32 = 0.f;
+  int lim_row;
+  {
+    const int qi = q0w + l32;
+    lim_row = p.Sk - 1;
+    if (CAUSAL) lim_row = min(lim_row, qi + p.off);
+  }
+  // S^T = K(kbuf) Q^T
+  auto qk = [&](f32x16 (&S)[KB], int kbuf) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const i16x8 kf = *(LDS_PTR(const i16x8))(lds + k_addr(kbuf, kb, kk));
+        S[kb] = T::mfma(kf, qf[kk], S[kb]);
+      }
+    }
+  };
+  // O^T += V(vbuf)^T P^T
+  auto pv = [&](const PFrag<i16x8>& P, int vbuf) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int t = 0; t < NP; ++t) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_PTR(i16x4))(lds + v_addr(vbuf, t, cb, 0)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_PTR(i16x4))(lds + v_addr(vbuf, t, cb, 1)));
+        const i16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc_o[cb] = T::mfma(vf, P.hi[t], acc_o[cb]);
+        if constexpr (T::SPLIT_P) acc_o[cb] = T::mfma(vf, P.lo[t], acc_o[cb]);
+      }
+    }
+  };
+
+  f32x16 SA[KB], SB[KB];
+  PFrag<i16x8> PA, PB;
+#pragma unroll
+  for (int t = 0; t < NP; ++t) {
+    PB.hi[t] = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    PB.lo[t] = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  auto kbuf_of = [](int n) { return KBUF0 + (n & 1) * TB; };
+  auto vbuf_of = [](int n) { return VBUF0 + (n & 1) * TB; };
+
+  // One iteration.  Sc = S(j) on entry, Sn receives S(j+1); Pp = P(j-1),
+  // Pc receives P(j).  PAR = j & 1 fixes every LDS buffer address at compile
+  // time.
+  //
+  // The main block is scheduled by hand as a list of steps (16 for the P V
+  // product, 16 for the next tile's S at d = 128): each step issues the LDS
+  // reads of the step LA places ahead, one MFMA (two for the fp16 hi/lo pair)
+  // and the exp2/convert/row-sum of one score of this tile.  sched_barrier
+  // keeps the steps in order, so LDS reads run ahead of their MFMAs and the
+  // vector ALU works beside the matrix core.
+  constexpr int NPV = CB * NP;   // O^T += V^T P^T steps (cb, t)
+  constexpr int NQK = KB * KK;   // S^T = K Q^T steps (kb, kk)
+  constexpr int NOPS = NPV + NQK;
+  constexpr int NSC = KB * 16;   // scores per lane
+  constexpr int LA = 3;          // read-ahead, in steps
+  constexpr int SPS = (NSC + NOPS - 1) / NOPS;  // scores per step
+
+  auto iter = [&](auto par, int j, f32x16 (&Sc)[KB], f32x16 (&Sn)[KB],
+                  const PFrag<i16x8>& Pp, PFrag<i16x8>& Pc) {
+    constexpr int PAR = decltype(par)::value;
+    constexpr int K_NEXT = KBUF0 + (PAR ^ 1) * TB;  // K(j+1)
+    constexpr int V_PREV = VBUF0 + (PAR ^ 1) * TB;  // V(j-1)
+    constexpr int K_LOAD = KBUF0 + PAR * TB;        // K(j+2)
+    constexpr int V_LOAD = VBUF0 + PAR * TB;        // V(j)
+    if (j + 2 < n_end) issue_rows(kbase, j + 2, K_LOAD);
+    issue_rows(vbase, j, V_LOAD);
+    // mask the straddling tiles, then the row max and the max update
+    if (j >= n_full) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int L = lim_row - j * BC - kb * 32 - 8 * hh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key_of_reg(r) > L) Sc[kb][r] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sc[kb][r]);
+    mx = other_half_max(mx) * p.scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    // move the max only past the threshold: alpha = 1 (no rescale) otherwise
+    const bool resc = __builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_TAU) != 0;
+    float alpha = 1.f;
+    if (resc) {
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+    }
+    const float neg_m = -m_run;
+    float ls = 0.f;   // unrounded P (LSE)
+    float lr = 0.f;   // rounded P (normalisation of O)
+    f32x8 e;
+    i16x8 fr[LA + 1];
+    // LDS reads of step i into fragment slot i % (LA + 1)
+    auto read_step = [&](int i) {
+      if (i < NPV) {
+        const int cb = i / NP, t = i % NP;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_PTR(i16x4))(lds + v_addr(V_PREV, t, cb, 0)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_PTR(i16x4))(lds + v_addr(V_PREV, t, cb, 1)));
+        fr[i % (LA + 1)] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const int q = i - NPV, kb = q / KK, kk = q % KK;
+        fr[i % (LA + 1)] = *(LDS_PTR(const i16x8))(lds + k_addr(K_NEXT, kb, kk));
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < LA; ++i) read_step(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NOPS; ++i) {
+      if (i + LA < NOPS) read_step(i + LA);
+      const i16x8 f = fr[i % (LA + 1)];
+      if (i < NPV) {  // O^T += V(j-1)^T P(j-1)
+        const int cb = i / NP, t = i % NP;
+        acc_o[cb] = T::mfma(f, Pp.hi[t], acc_o[cb]);
+        if constexpr (T::SPLIT_P) acc_o[cb] = T::mfma(f, Pp.lo[t], acc_o[cb]);
+      } else {  // S(j+1)^T = K(j+1) Q^T
+        const int q = i - NPV, kb = q / KK, kk = q % KK;
+        if (kk == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) Sn[kb][r] = 0.f;
+        }
+        Sn[kb] = T::mfma(f, qf[kk], Sn[kb]);
+      }
+#pragma unroll
+      for (int u = 0; u < SPS; ++u) {  // P(j) = exp2(S(j) * c - m)
+        const int sc = i * SPS + u;
+        if (sc < NSC) {
+          const int kb = sc / 16, r = sc % 16;
+          e[sc % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[kb][r], p.scale_log2, neg_m));
+          if constexpr (T::LSE_FROM_FP32_SUM) ls += e[sc % 8];
+          if (sc % 8 == 7) {
+            const i16x8 h = T::cvt(e);
+            Pc.hi[sc / 8] = h;
+            lr = T::sum8(h, lr);
+            // an empty asm use pins the conversion (and the exp2s feeding
+            // it) to this step; the compiler would otherwise sink them to
+            // their use in the next iteration
+            asm volatile("" ::"v"(h));
+            if constexpr (T::SPLIT_P) {
+              const i16x8 lo = T::cvt(e - T::widen(h));
+              Pc.lo[sc / 8] = lo;
+              lr = T::sum8(lo, lr);
+              asm volatile("" ::"v"(lo));
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_rnd = l_rnd * alpha + lr;
+    if constexpr (T::LSE_FROM_FP32_SUM) l_fp32 = l_fp32 * alpha + ls;
+    // rescale after O has absorbed V(j-1)^T P(j-1) (taken against the old max)
+    if (resc) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[cb][r] *= alpha;
+    }
+    __syncthreads();
+  };
+
+  if (n_end > 0) {
+    // prologue: K(0) and K(1) in flight; the V buffer read for "tile -1" in
+    // iteration 0 is cleared so that 0 * V stays 0.
+    issue_rows(kbase, 0, kbuf_of(0));
+    if (n_end > 1) issue_rows(kbase, 1, kbuf_of(1));
+    {
+      LDS_PTR(u32x4) z = (LDS_PTR(u32x4))(lds + vbuf_of(1));
+      for (int i = tid; i < TB / 16; i += NT) z[i] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    qk(SA, kbuf_of(0));
+    __syncthreads();  // every wave has read K(0) before K(2) overwrites it
+    int j = 0;
+    for (; j + 1 < n_end; j += 2) {
+      iter(std::integral_constant<int, 0>{}, j, SA, SB, PB, PA);
+      iter(std::integral_constant<int, 1>{}, j + 1, SB, SA, PA, PB);
+    }
+    if (j < n_end) {
+      iter(std::integral_constant<int, 0>{}, j, SA, SB, PB, PA);
+      pv(PA, vbuf_of(j));  // drain: the last tile's P is in PA
+    } else {
+      pv(PB, vbuf_of(j - 1));  // drain: the last tile's P is in PB
+    }
+  }
+
+  // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
+  {
+    const int qi = q0w + l32;
+    // lanes l and l+32 hold the two halves of the row's keys (all lanes active)
+    auto pair_sum = [](float x) {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                false, false);
+      return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    };
+    const float l_tot = pair_sum(l_rnd);
+    const bool has = l_tot > 0.f;
+    const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+    float l_lse = l_tot;
+    if constexpr (T::LSE_FROM_FP32_SUM) l_lse = pair_sum(l_fp32);
+    if (qi < p.Sq) {
+      uint16_t* orow = p.o + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x8 x;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[r] = acc_o[cb][4 * g + r] * inv;
+            x[r + 4] = 0.f;
+          }
+          const i16x8 y = T::cvt(x);
+          const u32x2 w = {(unsigned)(uint16_t)y[0] | ((unsigned)(uint16_t)y[1] << 16),
+                           (unsigned)(uint16_t)y[2] | ((unsigned)(uint16_t)y[3] << 16)};
+          *(u32x2*)(orow + cb * 32 + 8 * g + 4 * hh) = w;
+        }
+      if (p.lse != nullptr && hh == 0) {
+        const float lse = has ? (m_run + __builtin_amdgcn_logf(l_lse)) * LN2 : -INFINITY;
+        p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] = lse;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ host side
 struct Plan {
-  int nw, qb, gh, rows_wg, qtiles, ncols, xcd_cols, grid, lds_bytes;
+  int nw, qb, gh, rows_wg, qtiles, ncols, xcd_cols, grid, lds_bytes, pipelined;
 };
 
 bool sizes_ok(int B, int Sq, int Sk, int Hq, int Hkv) {
@@ -534,7 +969,6 @@ attn_status validate(const void* q, const void* k, const void* v, void* o,
 Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
   (void)Sk;
   (void)causal;
-  (void)d;
   Plan pl{};
   pl.nw = 4;
   const int group = Hq / Hkv;
@@ -543,26 +977,26 @@ Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
   pl.gh = gh;
   const int hsub = group / gh;
   pl.ncols = B * Hkv * hsub;
-  auto count = [&](int qb) {
-    const int rows = (pl.nw / gh) * 32 * qb;
-    const long long qt = (Sq + rows - 1) / rows;
-    return qt * (long long)pl.ncols;
-  };
-  (void)count;
   pl.qb = 1;
-  pl.rows_wg = (pl.nw / gh) * 32 * pl.qb;
-  pl.qtiles = (Sq + pl.rows_wg - 1) / pl.rows_wg;
+  pl.pipelined = 1;
+  pl.rows_wg = (pl.nw / gh) * 32;
+  const long long qt = (Sq + pl.rows_wg - 1) / pl.rows_wg;
+  pl.qtiles = qt > 0x7fffffffll ? -1 : (int)qt;
   pl.xcd_cols = (pl.ncols % 8 == 0) ? pl.ncols / 8 : 0;
-  const long long grid = (long long)pl.qtiles * pl.ncols;
-  pl.grid = grid > 0x7fffffffll ? -1 : (int)grid;
-  pl.lds_bytes = 2 * 2 * BC * d * 2;
+  const long long grid = qt * pl.ncols;
+  pl.grid = (grid > 0x7fffffffll || pl.qtiles < 0) ? -1 : (int)grid;
+  pl.lds_bytes = 4 * BC * d * 2;
   return pl;
 }
 
 template <int DT, int D, bool CAUSAL>
 hipError_t launch_t(const Plan& pl, const Params& p, hipStream_t st) {
   dim3 grid(pl.grid), block(pl.nw * 64);
-  hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, 4, 1>), grid, block, pl.lds_bytes, st, p);
+  if (pl.pipelined) {
+    hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 4>), grid, block, pl.lds_bytes, st, p);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, 4, 1>), grid, block, pl.lds_bytes, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -596,9 +1030,9 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
                                   Hkv, d, 1.0f, causal, dtype);
   if (st != ATTN_OK) return st;
   const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
-  const int vals[8] = {pl.grid, pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
-                       pl.lds_bytes, pl.xcd_cols > 0 ? 1 : 0};
-  for (int i = 0; i < n && i < 8; ++i) out[i] = vals[i];
+  const int vals[9] = {pl.grid, pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
+                       pl.lds_bytes, pl.xcd_cols > 0 ? 1 : 0, pl.pipelined};
+  for (int i = 0; i < n && i < 9; ++i) out[i] = vals[i];
   return ATTN_OK;
 }
 

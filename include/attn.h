@@ -93,12 +93,14 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
 
 /*
  * attn_fwd_plan -- describe the launch attn_fwd would make for these sizes,
- * without any device call.  Writes up to n ints into `out`:
+ * without any device call.  Writes up to n (at most 9) ints into `out`:
  *   [0] workgroups in the grid   [1] threads per workgroup
  *   [2] query rows per workgroup [3] keys per K/V tile
  *   [4] query heads per workgroup (GQA packing)
  *   [5] query rows per wave      [6] LDS bytes per workgroup
  *   [7] 1 if the grid is ordered per XCD, else 0
+ *   [8] 1 if the software-pipelined kernel (two 32-row blocks per wave,
+ *       softmax of one block overlapping the MFMAs of the other) is used
  * Returns the status attn_fwd_check would return.
  */
 attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,

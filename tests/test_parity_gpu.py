@@ -137,6 +137,36 @@ def test_edge_matrix(Sq, Sk, causal, d, dt, Hq, Hkv, scale):
     _check_full(w, q, k, v, o, lse, strict=False)
 
 
+def _pipelined_cases():
+    cases = []
+    # enough (batch x kv-head) columns that the plan takes the pipelined
+    # kernel even at short lengths; ragged and offset lengths on both sides
+    for Sq, Sk in ((256, 256), (273, 273), (300, 1), (300, 63), (300, 64),
+                   (300, 65), (260, 1000), (1000, 260), (129, 700)):
+        for causal in (False, True):
+            cases.append((Sq, Sk, causal, 128, "bf16", 32, 8))
+    for d in (64, 128):
+        for dt in ("f16", "bf16"):
+            cases.append((333, 517, True, d, dt, 32, 4))
+            cases.append((517, 333, True, d, dt, 16, 16))
+    return cases
+
+
+@pytest.mark.parametrize("Sq,Sk,causal,d,dt,Hq,Hkv", _pipelined_cases())
+def test_pipelined_kernel_edges(Sq, Sk, causal, d, dt, Hq, Hkv):
+    from exact_attention_19_amd import attn_fwd_plan
+    from exact_attention_19_amd.binding import ATTN_DTYPE_BF16, ATTN_DTYPE_F16
+    B = 16
+    code = ATTN_DTYPE_BF16 if dt == "bf16" else ATTN_DTYPE_F16
+    while not attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), code)["pipelined"]:
+        B *= 2
+    w = Workload(f"pp_sq{Sq}_sk{Sk}_c{int(causal)}_d{d}_{dt}_h{Hq}_{Hkv}_b{B}", B, Hq,
+                 Hkv, Sq, Sk, d, dt, causal, 1.0 / math.sqrt(d))
+    q, k, v = make_inputs(w, seed=Sq + 7 * Sk)
+    o, lse = _run(q, k, v, w)
+    _check_full(w, q, k, v, o, lse, strict=False)
+
+
 def test_small_integer_inputs_isolate_softmax():
     """Inputs in {-2..1} make Q K^T exact in fp32 (the CuTe DSL example's
     trick): the remaining error is softmax and P rounding only."""
