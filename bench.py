@@ -54,11 +54,12 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
+def cpu_baseline(w, q, k, v, budget_s: float = 15.0):
     """Time the fp64 oracle on a bounded, seeded sample of query rows of the
     workload (rows drawn uniformly over batch, heads and positions) and scale
     to TFLOP/s with the exact FLOPs of the sampled rows (4*d per visible
-    key)."""
+    key).  The sample is sized from a calibration run of at least a second so
+    that the timed run takes about budget_s."""
     import numpy as np
     from oracle import attn_fwd_oracle
 
@@ -74,12 +75,20 @@ def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
             return np.full(rows.shape, w.Sk, dtype=np.int64)
         return np.clip(i + (w.Sk - w.Sq) + 1, 0, w.Sk)
 
-    # calibrate on a small batch, then size the timed sample to the budget
-    calib = rng.integers(0, total_rows, 4 * cores)
-    t0 = time.perf_counter()
-    attn_fwd_oracle(q, k, v, w.scale, w.causal, rows=calib, nthreads=cores)
-    t_cal = time.perf_counter() - t0
-    n = int(max(cores, min(total_rows, len(calib) * budget_s / max(t_cal, 1e-3))))
+    # calibrate: grow the sample until it takes a second, then size the timed
+    # sample to the budget by visible keys (the oracle's cost per row)
+    n_cal = 4 * cores
+    while True:
+        calib = rng.integers(0, total_rows, n_cal)
+        t0 = time.perf_counter()
+        attn_fwd_oracle(q, k, v, w.scale, w.causal, rows=calib, nthreads=cores)
+        t_cal = time.perf_counter() - t0
+        if t_cal >= 1.0 or n_cal >= total_rows:
+            break
+        n_cal = min(total_rows, n_cal * max(2, int(1.5 / max(t_cal, 1e-3))))
+    per_key = t_cal / max(1, int(visible(calib).sum()))
+    mean_keys = float(visible(rng.integers(0, total_rows, 4096)).mean())
+    n = int(max(cores, min(total_rows, budget_s / (per_key * max(mean_keys, 1.0)))))
     rows = rng.integers(0, total_rows, n)
     t0 = time.perf_counter()
     attn_fwd_oracle(q, k, v, w.scale, w.causal, rows=rows, nthreads=cores)
@@ -92,6 +101,19 @@ def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
             "seconds": round(dt, 2)}
 
 
+def copy_probe(mib: int, steps: int):
+    """Device-to-device copy of a known size, for scaling the HBM byte counters
+    (FETCH_SIZE, WRITE_SIZE) of a profiler run to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,12 +121,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
+                    help="only run a device copy of MIB MiB --steps times "
+                         "(calibration of the profiler's byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the attention forward is built and "
               "timed on a single GPU only (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe, args.steps)
+        return
 
     import torch
     from exact_attention_19_amd import attn_fwd, attn_fwd_plan, load_library

@@ -36,10 +36,10 @@
 //   (2^8): the result is mathematically identical, because numerator and
 //   denominator use the same stale max, and most tiles then skip the
 //   rescaling of the accumulator.
-// * The softmax denominator is accumulated by the matrix cores from the very
-//   16-bit probabilities that multiply V (an extra MFMA against a block of
-//   ones), so the normalisation O = sum P~ V / sum P~ uses one consistent set
-//   of rounded weights; for fp16 inputs P is carried as a hi + lo pair.
+// * The softmax denominator sums the very 16-bit probabilities that multiply
+//   V (v_dot2 against 1.0: exact products, fp32 accumulation), so the
+//   normalisation O = sum P~ V / sum P~ uses one consistent set of rounded
+//   weights; for fp16 inputs P is carried as a hi + lo pair.
 // * Causal masking is applied only on the tiles that straddle the diagonal or
 //   the ragged end of K (the cuTile write-up's K-loop split); tiles above the
 //   diagonal are never visited (its causal loop bound).
@@ -102,7 +102,6 @@ struct Ty<ATTN_DTYPE_BF16> {
           one, acc, false);
     return acc;
   }
-  static constexpr short ONE = 0x3F80;  // 1.0 in bf16
   static constexpr bool SPLIT_P = false;
   // The sum of the bf16-rounded P normalises O, but one rounded dominant
   // weight can move it by 2^-9 relative: the LSE uses an fp32 sum of the
@@ -134,7 +133,6 @@ struct Ty<ATTN_DTYPE_F16> {
           one, acc, false);
     return acc;
   }
-  static constexpr short ONE = 0x3C00;  // 1.0 in fp16
   // fp16 probabilities are carried as hi + lo halves (P = hi + lo to about
   // 22 bits), so the P V product keeps fp32-level accuracy: the fp16
   // tolerance leaves almost no room beside the output rounding of |O| >= 4.
@@ -198,338 +196,11 @@ __device__ __forceinline__ float other_half_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// ------------------------------------------------------ the main kernel
-template <int DT, int D, bool CAUSAL, int NW, int QB>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
-  using T = Ty<DT>;
-  constexpr int NT = NW * 64;
-  constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int CPT = BC * CPR / NT;      // chunks per thread per tile
-  constexpr int KB = BC / 32;             // 32-key blocks per tile
-  constexpr int CB = D / 32;              // 32-wide d blocks
-  constexpr int KK = D / 16;              // k-steps of the S^T product
-  constexpr int TILE = BC * D;            // elements per K (or V) tile
-  static_assert(CPT * NT == BC * CPR, "tile must split evenly over threads");
-
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  // [buf][K|V][BC*D]
-  LDS_PTR(uint16_t) lds = (LDS_PTR(uint16_t))smem;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  // ---- work decode: heaviest row blocks first, optionally grouped per XCD
-  int qt, col;
-  {
-    const int L = blockIdx.x;
-    if (p.xcd_cols > 0) {
-      const int xcd = L & 7;
-      const int k = L >> 3;
-      qt = p.qtiles - 1 - k / p.xcd_cols;
-      col = xcd * p.xcd_cols + k % p.xcd_cols;
-    } else {
-      qt = p.qtiles - 1 - L / p.ncols;
-      col = L % p.ncols;
-    }
-  }
-  const int hs = col % p.hsub;
-  const int kvh = (col / p.hsub) % p.Hkv;
-  const int b = col / (p.hsub * p.Hkv);
-  const int head_in_wg = wave % p.gh;
-  const int rowblk = wave / p.gh;
-  const int hq = kvh * p.group + hs * p.gh + head_in_wg;
-  const int q0wg = qt * p.rows_wg;
-  const int q0w = q0wg + rowblk * (32 * QB);
-
-  // ---- KV tile range of the workgroup and of this wave
-  const int q_last_wg = min(q0wg + p.rows_wg, p.Sq) - 1;
-  int kv_end = p.Sk;
-  if (CAUSAL) kv_end = min(p.Sk, q_last_wg + p.off + 1);
-  const int n_end = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
-  int n_full = p.Sk / BC;
-  if (CAUSAL) {
-    const int lim = q0wg + p.off + 1;
-    n_full = min(n_full, lim > 0 ? lim / BC : 0);
-  }
-  n_full = min(n_full, n_end);
-  int w_end = 0;
-  if (q0w < p.Sq) {
-    const int q_last_w = min(q0w + 32 * QB, p.Sq) - 1;
-    int e = p.Sk;
-    if (CAUSAL) e = min(p.Sk, q_last_w + p.off + 1);
-    w_end = e > 0 ? (e + BC - 1) / BC : 0;
-  }
-
-  const int64_t kv_row_stride = (int64_t)p.Hkv * D;  // elements between keys
-  const uint16_t* kbase = p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
-  const uint16_t* vbase = p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
-
-  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
-  i16x8 qf[QB][KK];
-#pragma unroll
-  for (int nb = 0; nb < QB; ++nb) {
-    const int qi = q0w + nb * 32 + l32;
-    const bool ok = qi < p.Sq;
-    const uint16_t* qrow =
-        p.q + (((int64_t)b * p.Sq + (ok ? qi : 0)) * p.Hq + hq) * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (ok) x = *(const u32x4*)(qrow + kk * 16 + hh * 8);
-      qf[nb][kk] = __builtin_bit_cast(i16x8, x);
-    }
-  }
-
-  // ---- online-softmax state and output accumulator (O^T, one query/lane)
-  f32x16 acc_o[CB][QB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int nb = 0; nb < QB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[cb][nb][r] = 0.f;
-  // The running max starts at a finite, very negative value: any finite score
-  // moves it (exp2 of the difference underflows to 0 for the empty
-  // accumulator), and masked scores (-inf) give exp2(-inf) = 0 against it.
-  float m_run[QB];
-  f32x16 acc_l[QB];  // row sums of the rounded P: every register holds it
-  float l_fp32[QB];  // per-lane partial sums of the unrounded P (for the LSE)
-#pragma unroll
-  for (int nb = 0; nb < QB; ++nb) {
-    m_run[nb] = -1e30f;
-    l_fp32[nb] = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc_l[nb][r] = 0.f;
-  }
-  const i16x8 ones = {T::ONE, T::ONE, T::ONE, T::ONE, T::ONE, T::ONE, T::ONE, T::ONE};
-  // per-lane causal / ragged limit: the last visible key of this lane's rows
-  int lim_row[QB];
-#pragma unroll
-  for (int nb = 0; nb < QB; ++nb) {
-    const int qi = q0w + nb * 32 + l32;
-    int lim = p.Sk - 1;
-    if (CAUSAL) lim = min(lim, qi + p.off);
-    lim_row[nb] = lim;
-  }
-
-  // ---- global -> LDS tile copy (direct-to-LDS loads, no registers)
-  // Each global_load_lds_dwordx4 of a wave writes 64 consecutive 16-byte
-  // chunks of LDS; lane l picks as its source the logical chunk that the
-  // swizzle places at physical chunk (base + l).  Rows past the end of K/V
-  // re-read the last row: those keys are masked to -inf, so P = 0 there and
-  // the finite values never reach O.
-  auto issue_tile = [&](int n, int buf) {
-    LDS_PTR(uint16_t) kd = lds + buf * 2 * TILE;
-    LDS_PTR(uint16_t) vd = kd + TILE;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int cbase = (u * NW + wave) * 64;
-      const int ci = cbase + lane;
-      const int row = ci / CPR;
-      const int slot = ci % CPR;
-      const int sc = slot ^ swz<D>(row);
-      const int j = min(n * BC + row, p.Sk - 1);
-      const int64_t goff = (int64_t)j * kv_row_stride + sc * 8;
-      __builtin_amdgcn_global_load_lds((const GLOBAL_PTR(void))(kbase + goff),
-                                       (LDS_PTR(void))(kd + cbase * 8), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const GLOBAL_PTR(void))(vbase + goff),
-                                       (LDS_PTR(void))(vd + cbase * 8), 16, 0, 0);
-    }
-  };
-
-  // ---- one K/V tile: S^T, (mask), online softmax, O^T += V^T P^T
-  auto step = [&](int n, int buf, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    LDS_PTR(const uint16_t) kt = lds + buf * 2 * TILE;
-    LDS_PTR(const uint16_t) vt = kt + TILE;
-
-    // S^T = K Q^T over the BC keys of the tile, fp32 accumulate
-    f32x16 s[KB][QB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int nb = 0; nb < QB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][nb][r] = 0.f;
-      const int row = kb * 32 + sigma(l32);
-      const int sw = swz<D>(row);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int chunk = 2 * kk + hh;
-        const i16x8 kf = *(LDS_PTR(const i16x8))(kt + row * D + ((chunk ^ sw) << 3));
-#pragma unroll
-        for (int nb = 0; nb < QB; ++nb) s[kb][nb] = T::mfma(kf, qf[nb][kk], s[kb][nb]);
-      }
-    }
-
-    // mask the straddling tiles: key index vs the lane's limit
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int nb = 0; nb < QB; ++nb)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int L = lim_row[nb] - n * BC - kb * 32 - 8 * hh;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key_of_reg(r) > L) s[kb][nb][r] = -INFINITY;
-        }
-    }
-
-    // online softmax (log2 domain)
-    float mt[QB];
-    bool any_rescale = false;
-#pragma unroll
-    for (int nb = 0; nb < QB; ++nb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][nb][r]);
-      mx = other_half_max(mx) * p.scale_log2;
-      mt[nb] = mx;
-      any_rescale |= mx > m_run[nb] + RESCALE_TAU;
-    }
-    if (__builtin_amdgcn_ballot_w64(any_rescale) != 0) {
-#pragma unroll
-      for (int nb = 0; nb < QB; ++nb) {
-        const float m_new = fmaxf(m_run[nb], mt[nb]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new);
-        m_run[nb] = m_new;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_l[nb][r] *= alpha;
-        if constexpr (T::LSE_FROM_FP32_SUM) l_fp32[nb] *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[cb][nb][r] *= alpha;
-      }
-    }
-    i16x8 pf[QB][BC / 16];
-    i16x8 pf_lo[QB][BC / 16];  // fp16 only: p - hi, rounded
-#pragma unroll
-    for (int nb = 0; nb < QB; ++nb) {
-      const float neg_m = -m_run[nb];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          f32x8 e;
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            e[r] = __builtin_amdgcn_exp2f(
-                __builtin_fmaf(s[kb][nb][half * 8 + r], p.scale_log2, neg_m));
-            if constexpr (T::LSE_FROM_FP32_SUM) l_fp32[nb] += e[r];
-          }
-          const i16x8 hi = T::cvt(e);
-          pf[nb][kb * 2 + half] = hi;
-          if constexpr (T::SPLIT_P) pf_lo[nb][kb * 2 + half] = T::cvt(e - T::widen(hi));
-        }
-    }
-
-    // O^T += V^T P^T: V^T fragments by LDS transpose reads
-#pragma unroll
-    for (int t = 0; t < BC / 16; ++t) {
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int g16 = lane >> 4;
-        const int s16 = lane & 15;
-        const int c = cb * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
-        const int chunk = c >> 3;
-        const int within = c & 7;
-        i16x4 lo, hi;
-        {
-          const int row = 16 * t + 8 * (g16 >> 1) + (s16 >> 2);
-          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (LDS_PTR(i16x4))(vt + row * D + ((chunk ^ swz<D>(row)) << 3) + within));
-        }
-        {
-          const int row = 16 * t + 8 * (g16 >> 1) + 4 + (s16 >> 2);
-          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (LDS_PTR(i16x4))(vt + row * D + ((chunk ^ swz<D>(row)) << 3) + within));
-        }
-        const i16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int nb = 0; nb < QB; ++nb) {
-          acc_o[cb][nb] = T::mfma(vf, pf[nb][t], acc_o[cb][nb]);
-          if constexpr (T::SPLIT_P) acc_o[cb][nb] = T::mfma(vf, pf_lo[nb][t], acc_o[cb][nb]);
-        }
-      }
-      // row sums of exactly the 16-bit P that multiplied V
-#pragma unroll
-      for (int nb = 0; nb < QB; ++nb) {
-        acc_l[nb] = T::mfma(ones, pf[nb][t], acc_l[nb]);
-        if constexpr (T::SPLIT_P) acc_l[nb] = T::mfma(ones, pf_lo[nb][t], acc_l[nb]);
-      }
-    }
-  };
-
-  // __syncthreads() waits for all outstanding loads (vmcnt(0)) before the
-  // barrier, which publishes a tile written by the direct loads.
-  if (n_end > 0) issue_tile(0, 0);
-  __syncthreads();
-  int n = 0;
-  for (; n < n_full; ++n) {
-    const int buf = n & 1;
-    if (n + 1 < n_end) issue_tile(n + 1, buf ^ 1);
-    if (n < w_end) step(n, buf, std::false_type{});
-    __syncthreads();
-  }
-  for (; n < n_end; ++n) {
-    const int buf = n & 1;
-    if (n + 1 < n_end) issue_tile(n + 1, buf ^ 1);
-    if (n < w_end) step(n, buf, std::true_type{});
-    __syncthreads();
-  }
-
-  // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
-#pragma unroll
-  for (int nb = 0; nb < QB; ++nb) {
-    const int qi = q0w + nb * 32 + l32;
-    const float l_tot = acc_l[nb][0];
-    const bool has = l_tot > 0.f;
-    const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-    float l_lse = l_tot;
-    if constexpr (T::LSE_FROM_FP32_SUM) {
-      // lanes l and l+32 hold the two halves of the row's keys (all lanes
-      // active here)
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_fp32[nb]),
-                                                __float_as_uint(l_fp32[nb]), false, false);
-      l_lse = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    if (qi < p.Sq) {
-      uint16_t* orow = p.o + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x8 x;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            x[r] = acc_o[cb][nb][4 * g + r] * inv;
-            x[r + 4] = 0.f;
-          }
-          const i16x8 y = T::cvt(x);
-          const u32x2 w = {(unsigned)(uint16_t)y[0] | ((unsigned)(uint16_t)y[1] << 16),
-                           (unsigned)(uint16_t)y[2] | ((unsigned)(uint16_t)y[3] << 16)};
-          *(u32x2*)(orow + cb * 32 + 8 * g + 4 * hh) = w;
-        }
-      if (p.lse != nullptr && hh == 0) {
-        const float lse = has ? (m_run[nb] + __builtin_amdgcn_logf(l_lse)) * LN2 : -INFINITY;
-        p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] = lse;
-      }
-    }
-  }
-}
-
-// ------------------------------------- the software-pipelined kernel
+// ------------------------------------------------------------ the kernel
 //
-// Same tile math as attn_fwd_kernel (one wave = 32 query rows of one head,
-// the waves of a workgroup share every K/V tile), but the work of a tile is
-// skewed across loop iterations so that each iteration hands the vector ALU
-// and the matrix core independent work:
+// One wave = 32 query rows of one head; the waves of a workgroup share every
+// K/V tile.  The work of a tile is skewed across loop iterations so that each
+// iteration hands the vector ALU and the matrix core independent work:
 //
 //   iteration j:  softmax(S(j)) -> P(j)            [VALU: max, exp2, convert]
 //                 O += V(j-1)^T P(j-1)             [MFMA, previous tile]
@@ -562,17 +233,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   constexpr int KK = D / 16;
   constexpr int NP = BC / 16;
   constexpr int TB = BC * D * 2;      // bytes per K or V tile buffer
-  constexpr int KBUF0 = 0;            // K buffers: 0, TB
-  constexpr int VBUF0 = 2 * TB;       // V buffers: 2TB, 3TB
   static_assert(CPT * NT == BC * CPR, "tile must split evenly over threads");
   static_assert(CPT == CB, "one load round per 32-column block");
 
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  LDS_PTR(char) lds = (LDS_PTR(char))smem;
+  // Two K and two V tile buffers, each its own LDS object: the compiler's
+  // alias analysis then separates the direct loads into one buffer from the
+  // reads of another, so no read waits for an unrelated tile load (with one
+  // LDS array every read of a tile waited for all loads in flight).
+  __shared__ __attribute__((aligned(1024))) char lds_k0[TB], lds_k1[TB], lds_v0[TB], lds_v1[TB];
+  auto kbuf_of = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_k1 : (LDS_PTR(char))lds_k0; };
+  auto vbuf_of = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_v1 : (LDS_PTR(char))lds_v0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -611,9 +285,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   }
   n_full = min(n_full, n_end);
 
-  const int64_t kv_row_stride = (int64_t)p.Hkv * D;
-  const uint16_t* kbase = p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
-  const uint16_t* vbase = p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
+  // K and V rows of this (batch, kv head): byte slices with a row stride of
+  // Hkv * D * 2 bytes
+  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
+  const char* kslice = (const char*)(p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
+  const char* vslice = (const char*)(p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
 
   // ---- LDS tile layout of this kernel: column-blocked.  A K or V tile is
   // stored as D/32 blocks of 32 columns; block cb holds the 64 rows of those
@@ -649,11 +325,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
           (uint32_t)(row * 64 + ((((cc >> 3) ^ ((row >> 2) & 3))) << 4) + (cc & 7) * 2);
     }
   }
-  auto k_addr = [&](int kbuf, int kb, int kk) {
-    return kbuf + (kk >> 1) * BLK + kb * 32 * 64 + kbase_lds[kk & 1];
+  auto k_addr = [&](LDS_PTR(char) kbuf, int kb, int kk) {
+    return kbuf + ((kk >> 1) * BLK + kb * 32 * 64 + kbase_lds[kk & 1]);
   };
-  auto v_addr = [&](int vbuf, int t, int cb, int half) {
-    return vbuf + cb * BLK + t * 16 * 64 + vbase_lds[half];
+  auto v_addr = [&](LDS_PTR(char) vbuf, int t, int cb, int half) {
+    return vbuf + (cb * BLK + t * 16 * 64 + vbase_lds[half]);
   };
   // Direct global -> LDS load round u of a wave writes LDS bytes
   // [(u*NW + wave) * 1024, +1024) of the tile: block (u*NW + wave) / 4, rows
@@ -663,15 +339,28 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   const int ld_chunk = (lane & 3) ^ ((ld_row >> 2) & 3);
   const int ld_col = ld_chunk * 8;  // + 32 * u: the column block of round u
 
-  auto issue_rows = [&](const uint16_t* gbase, int n, int lds_byte_base) {
-    int j = n * BC + ld_row;
-    if ((n + 1) * BC > p.Sk) j = min(j, p.Sk - 1);  // masked keys: any finite row
-    const uint16_t* src = gbase + (int64_t)j * kv_row_stride + ld_col;
+  // Tile loads are MUBUF loads to LDS through a buffer descriptor of the
+  // tile: the tile base and record count live in SGPRs, the per-lane offset
+  // is the same for every full tile, and the column round goes in the scalar
+  // offset, so a tile costs no per-lane address arithmetic.  (The FLAT-encoded
+  // global load to LDS would also do, but the compiler then assumes it may
+  // count on the LDS counter and waits for every outstanding LDS read at
+  // each dependency.)  Rows past Sk in the ragged last tile re-read row
+  // Sk - 1 (their keys are masked).  Host validation keeps BC * row_bytes
+  // below 2^31.
+  const uint32_t ld_off = (uint32_t)ld_row * row_bytes + (uint32_t)ld_col * 2;
+  auto issue_rows = [&](const char* slice, int n, LDS_PTR(char) buf) {
+    const char* tile = slice + (int64_t)n * BC * row_bytes;
+    uint32_t off = ld_off;
+    if ((n + 1) * BC > p.Sk)
+      off = (uint32_t)(min(n * BC + ld_row, p.Sk - 1) - n * BC) * row_bytes + (uint32_t)ld_col * 2;
+    // raw buffer, 32-bit data format (word 3 of the descriptor)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)(BC * row_bytes), 0x00020000);
 #pragma unroll
     for (int u = 0; u < CPT; ++u)
-      __builtin_amdgcn_global_load_lds((const GLOBAL_PTR(void))(src + 32 * u),
-                                       (LDS_PTR(void))(lds + lds_byte_base + (u * NW + wave) * 1024),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_PTR(void))(buf + (u * NW + wave) * 1024),
+                                               16, off, 64 * u, 0, 0);
   };
 
   // ---- Q fragments, kept in registers
@@ -707,28 +396,28 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
     if (CAUSAL) lim_row = min(lim_row, qi + p.off);
   }
   // S^T = K(kbuf) Q^T
-  auto qk = [&](f32x16 (&S)[KB], int kbuf) {
+  auto qk = [&](f32x16 (&S)[KB], LDS_PTR(char) kbuf) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const i16x8 kf = *(LDS_PTR(const i16x8))(lds + k_addr(kbuf, kb, kk));
+        const i16x8 kf = *(LDS_PTR(const i16x8))(k_addr(kbuf, kb, kk));
         S[kb] = T::mfma(kf, qf[kk], S[kb]);
       }
     }
   };
   // O^T += V(vbuf)^T P^T
-  auto pv = [&](const PFrag<i16x8>& P, int vbuf) {
+  auto pv = [&](const PFrag<i16x8>& P, LDS_PTR(char) vbuf) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int t = 0; t < NP; ++t) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_PTR(i16x4))(lds + v_addr(vbuf, t, cb, 0)));
+            (LDS_PTR(i16x4))(v_addr(vbuf, t, cb, 0)));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_PTR(i16x4))(lds + v_addr(vbuf, t, cb, 1)));
+            (LDS_PTR(i16x4))(v_addr(vbuf, t, cb, 1)));
         const i16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         acc_o[cb] = T::mfma(vf, P.hi[t], acc_o[cb]);
         if constexpr (T::SPLIT_P) acc_o[cb] = T::mfma(vf, P.lo[t], acc_o[cb]);
@@ -743,8 +432,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
     PB.hi[t] = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
     PB.lo[t] = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
   }
-  auto kbuf_of = [](int n) { return KBUF0 + (n & 1) * TB; };
-  auto vbuf_of = [](int n) { return VBUF0 + (n & 1) * TB; };
 
   // One iteration.  Sc = S(j) on entry, Sn receives S(j+1); Pp = P(j-1),
   // Pc receives P(j).  PAR = j & 1 fixes every LDS buffer address at compile
@@ -756,22 +443,32 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   // and the exp2/convert/row-sum of one score of this tile.  sched_barrier
   // keeps the steps in order, so LDS reads run ahead of their MFMAs and the
   // vector ALU works beside the matrix core.
-  constexpr int NPV = CB * NP;   // O^T += V^T P^T steps (cb, t)
+  constexpr int NPV = CB * NP;   // O^T += V^T P^T steps (t, cb)
   constexpr int NQK = KB * KK;   // S^T = K Q^T steps (kb, kk)
   constexpr int NOPS = NPV + NQK;
   constexpr int NSC = KB * 16;   // scores per lane
   constexpr int LA = 3;          // read-ahead, in steps
-  constexpr int SPS = (NSC + NOPS - 1) / NOPS;  // scores per step
+  // Softmax work per step: the scores of key block 0 of S(j) are spread over
+  // the P V steps and those of key block 1 over the first QK steps (those of
+  // key block 0 of S(j+1)), so each block of S(j) is dead before the MFMAs
+  // of the same block of S(j+1) start and both tiles share one register set.
+  // score_lo(i) is the first score of step i.
+  auto score_lo = [&](int i) {
+    if (i <= NPV) return 16 * i / NPV;
+    if (i <= NPV + KK) return 16 + 16 * (i - NPV) / KK;
+    return NSC;
+  };
+  static_assert(KB == 2, "two 32-key blocks per tile");
 
   auto iter = [&](auto par, int j, f32x16 (&Sc)[KB], f32x16 (&Sn)[KB],
                   const PFrag<i16x8>& Pp, PFrag<i16x8>& Pc) {
     constexpr int PAR = decltype(par)::value;
-    constexpr int K_NEXT = KBUF0 + (PAR ^ 1) * TB;  // K(j+1)
-    constexpr int V_PREV = VBUF0 + (PAR ^ 1) * TB;  // V(j-1)
-    constexpr int K_LOAD = KBUF0 + PAR * TB;        // K(j+2)
-    constexpr int V_LOAD = VBUF0 + PAR * TB;        // V(j)
-    if (j + 2 < n_end) issue_rows(kbase, j + 2, K_LOAD);
-    issue_rows(vbase, j, V_LOAD);
+    LDS_PTR(char) const K_NEXT = kbuf_of(PAR ^ 1);  // K(j+1)
+    LDS_PTR(char) const V_PREV = vbuf_of(PAR ^ 1);  // V(j-1)
+    LDS_PTR(char) const K_LOAD = kbuf_of(PAR);      // K(j+2)
+    LDS_PTR(char) const V_LOAD = vbuf_of(PAR);      // V(j)
+    if (j + 2 < n_end) issue_rows(kslice, j + 2, K_LOAD);
+    issue_rows(vslice, j, V_LOAD);
     // mask the straddling tiles, then the row max and the max update
     if (j >= n_full) {
 #pragma unroll
@@ -804,15 +501,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
     // LDS reads of step i into fragment slot i % (LA + 1)
     auto read_step = [&](int i) {
       if (i < NPV) {
-        const int cb = i / NP, t = i % NP;
+        const int t = i / CB, cb = i % CB;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_PTR(i16x4))(lds + v_addr(V_PREV, t, cb, 0)));
+            (LDS_PTR(i16x4))(v_addr(V_PREV, t, cb, 0)));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_PTR(i16x4))(lds + v_addr(V_PREV, t, cb, 1)));
+            (LDS_PTR(i16x4))(v_addr(V_PREV, t, cb, 1)));
         fr[i % (LA + 1)] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       } else {
         const int q = i - NPV, kb = q / KK, kk = q % KK;
-        fr[i % (LA + 1)] = *(LDS_PTR(const i16x8))(lds + k_addr(K_NEXT, kb, kk));
+        fr[i % (LA + 1)] = *(LDS_PTR(const i16x8))(k_addr(K_NEXT, kb, kk));
       }
     };
 #pragma unroll
@@ -823,7 +520,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
       if (i + LA < NOPS) read_step(i + LA);
       const i16x8 f = fr[i % (LA + 1)];
       if (i < NPV) {  // O^T += V(j-1)^T P(j-1)
-        const int cb = i / NP, t = i % NP;
+        // key block t outer: P(j-1) fragment t dies after step CB*t + CB-1,
+        // before P(j) fragments take registers, and consecutive MFMAs go to
+        // different accumulators
+        const int t = i / CB, cb = i % CB;
         acc_o[cb] = T::mfma(f, Pp.hi[t], acc_o[cb]);
         if constexpr (T::SPLIT_P) acc_o[cb] = T::mfma(f, Pp.lo[t], acc_o[cb]);
       } else {  // S(j+1)^T = K(j+1) Q^T
@@ -834,17 +534,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
         }
         Sn[kb] = T::mfma(f, qf[kk], Sn[kb]);
       }
+      // P(j) = exp2(S(j) * c - m) for the scores of this step
 #pragma unroll
-      for (int u = 0; u < SPS; ++u) {  // P(j) = exp2(S(j) * c - m)
-        const int sc = i * SPS + u;
-        if (sc < NSC) {
+      for (int sc = score_lo(i); sc < score_lo(i + 1); ++sc) {
+        {
           const int kb = sc / 16, r = sc % 16;
           e[sc % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[kb][r], p.scale_log2, neg_m));
-          if constexpr (T::LSE_FROM_FP32_SUM) ls += e[sc % 8];
+          if constexpr (T::LSE_FROM_FP32_SUM) {
+            ls += e[sc % 8];
+            // pinned here: sunk to its use after the block, the sum would
+            // keep every exp2 result of the tile alive
+            asm volatile("" : "+v"(ls));
+          }
           if (sc % 8 == 7) {
             const i16x8 h = T::cvt(e);
             Pc.hi[sc / 8] = h;
             lr = T::sum8(h, lr);
+            asm volatile("" : "+v"(lr));
             // an empty asm use pins the conversion (and the exp2s feeding
             // it) to this step; the compiler would otherwise sink them to
             // their use in the next iteration
@@ -869,18 +575,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[cb][r] *= alpha;
     }
+    // the tile loads of this wave must have landed before the barrier
+    // publishes them to the other waves
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
   if (n_end > 0) {
     // prologue: K(0) and K(1) in flight; the V buffer read for "tile -1" in
     // iteration 0 is cleared so that 0 * V stays 0.
-    issue_rows(kbase, 0, kbuf_of(0));
-    if (n_end > 1) issue_rows(kbase, 1, kbuf_of(1));
+    issue_rows(kslice, 0, kbuf_of(0));
+    if (n_end > 1) issue_rows(kslice, 1, kbuf_of(1));
     {
-      LDS_PTR(u32x4) z = (LDS_PTR(u32x4))(lds + vbuf_of(1));
+      LDS_PTR(u32x4) z = (LDS_PTR(u32x4))vbuf_of(1);
       for (int i = tid; i < TB / 16; i += NT) z[i] = (u32x4){0u, 0u, 0u, 0u};
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(0), K(1) landed
     __syncthreads();
     qk(SA, kbuf_of(0));
     __syncthreads();  // every wave has read K(0) before K(2) overwrites it
@@ -961,6 +671,8 @@ attn_status validate(const void* q, const void* k, const void* v, void* o,
   // index-space limits: positions and per-tensor row counts stay in int32
   // arithmetic inside the kernel; element offsets are 64-bit.
   if ((int64_t)Sq + Sk >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
+  // a K/V tile (64 rows of Hkv * d * 2 bytes) spans less than 2^31 bytes
+  if ((int64_t)Hkv * d * 2 * 64 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31))
     return ATTN_ERR_INVALID_ARG;
   return ATTN_OK;
@@ -992,11 +704,8 @@ Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
 template <int DT, int D, bool CAUSAL>
 hipError_t launch_t(const Plan& pl, const Params& p, hipStream_t st) {
   dim3 grid(pl.grid), block(pl.nw * 64);
-  if (pl.pipelined) {
-    hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 4>), grid, block, pl.lds_bytes, st, p);
-  } else {
-    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, 4, 1>), grid, block, pl.lds_bytes, st, p);
-  }
+  // the tile buffers are static LDS (pl.lds_bytes reports their size)
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 4>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 

@@ -73,10 +73,10 @@ typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
  *   stream hipStream_t to launch on (NULL = the default stream), passed as a
  *          plain pointer
  *
- * Returns ATTN_OK when the kernel was queued.  Every tensor element count
- * must stay below 2^31 / d rows per tensor index space (see
- * attn_fwd_supported for the exact limits); larger problems are rejected with
- * ATTN_ERR_INVALID_ARG rather than risking overflow.
+ * Returns ATTN_OK when the kernel was queued.  Size limits: Sq + Sk < 2^30,
+ * B * Sq * Hq < 2^31 and B * Sk * Hkv < 2^31 (rows of each tensor); larger
+ * problems are rejected with ATTN_ERR_INVALID_ARG rather than risking index
+ * overflow.  attn_fwd_check reports the same status without a device call.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
                      float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int d,
@@ -99,8 +99,9 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
  *   [4] query heads per workgroup (GQA packing)
  *   [5] query rows per wave      [6] LDS bytes per workgroup
  *   [7] 1 if the grid is ordered per XCD, else 0
- *   [8] 1 if the software-pipelined kernel (two 32-row blocks per wave,
- *       softmax of one block overlapping the MFMAs of the other) is used
+ *   [8] 1 if the software-pipelined kernel (the softmax of one K/V tile
+ *       overlapping the matrix products of the previous and next tiles) is
+ *       used
  * Returns the status attn_fwd_check would return.
  */
 attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
