@@ -72,6 +72,8 @@ def test_valid_arguments_pass_validation():
     assert _check() == ATTN_OK
     assert _check(lse=None) == ATTN_OK
     assert _check(d=64, dtype=ATTN_DTYPE_F16, causal=0) == ATTN_OK
+    # the largest head count whose 64-row tile stays below 2^31 bytes
+    assert _check(Hq=(1 << 17) - 8, Hkv=(1 << 17) - 8, B=1, Sq=1, Sk=1) == ATTN_OK
 
 
 @pytest.mark.parametrize("over", [
@@ -82,6 +84,8 @@ def test_valid_arguments_pass_validation():
     dict(scale=float("inf")), dict(causal=2), dict(causal=-1),
     dict(q=A + 8), dict(o=A + 0x3002), dict(lse=A + 0x4002),
     dict(Sq=1 << 29, Sk=1 << 29),
+    # a 64-row K/V tile must span less than 2^31 bytes: Hkv * d * 2 * 64
+    dict(Hq=1 << 17, Hkv=1 << 17, B=1, Sq=1, Sk=1),
 ])
 def test_invalid_arguments(over):
     _lib()
