@@ -7,6 +7,9 @@ package, and this package imports nothing from the product.
 ``attn_fwd_oracle`` runs the plain C implementation in ``attn_oracle.c`` (the
 textbook definition in fp64: scores, two-pass safe softmax over a materialised
 row, then P V; see that file's header for the citations).  ``build_oracle``
-compiles it with gcc.
+compiles it with gcc.  ``attn_fwd_oracle(..., key_range=(k0, k1))`` gives the
+partial state of each row over a key subset, and ``merge_partials_oracle``
+(numpy fp64) combines such partial states with the online-softmax update.
 """
-from .oracle import attn_fwd_oracle, build_oracle, oracle_lib_path  # noqa: F401
+from .oracle import (attn_fwd_oracle, build_oracle, merge_partials_oracle,  # noqa: F401
+                     oracle_lib_path)

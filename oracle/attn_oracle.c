@@ -24,8 +24,17 @@
  *     o[b,i,h,:] = sum_j p_ij * v[b,j,kvh,:]
  *     lse[b,h,i] = m_i + ln sum_{visible j} exp(s_ij - m_i)
  *
- *   A row with no visible key (causal and i < Sq - Sk) gets o = 0 and
- *   lse = -inf.  The pages do not define that case; this follows the CuTe DSL
+ *   Key range: oracle_attn_fwd_range restricts the visible set to keys j in
+ *   [k_begin, k_end) (the causal rule still counts j against the full Sk).
+ *   Its outputs are the partial state of the row over that key subset: the
+ *   normalised output and the log-sum-exp of those keys alone.  These are the
+ *   per-tile states (m, l, O~) of the online softmax ("FlashAttention
+ *   personal implementation notes", section "Online Softmax": the state
+ *   after the tiles of a subset, written as O = O~ / l and lse = m + ln l),
+ *   which a merge combines.  oracle_attn_fwd is the range [0, Sk).
+ *
+ *   A row with no visible key (causal and i < Sq - Sk, or an empty key
+ *   range) gets o = 0 and lse = -inf.  The pages do not define that case; this follows the CuTe DSL
  *   Ampere FlashAttention-2 example, whose normalisation leaves a zero
  *   accumulator unscaled when the row sum is zero.
  *
@@ -50,6 +59,7 @@ typedef struct {
     int64_t B, Sq, Sk, Hq, Hkv, d;
     double scale;
     int causal;
+    int64_t k_begin, k_end; /* key range [k_begin, k_end) */
     const int64_t *rows; /* flat row ids (b*Hq + h)*Sq + i, or NULL = all rows */
     int64_t total;       /* number of rows to compute */
     int64_t first, stride;
@@ -63,14 +73,15 @@ static void one_row(const job_t *J, int64_t b, int64_t h, int64_t i,
     const int64_t kvh = h / (J->Hq / J->Hkv);
     const double *qrow = J->q + ((b * J->Sq + i) * J->Hq + h) * d;
 
-    /* the visible keys are j in [0, nvis) */
-    int64_t nvis = J->Sk;
+    /* the visible keys are j in [j0, nvis) */
+    const int64_t j0 = J->k_begin;
+    int64_t nvis = J->k_end;
     if (J->causal) {
         int64_t lim = i + (J->Sk - J->Sq) + 1;
         if (lim < 0) lim = 0;
         if (lim < nvis) nvis = lim;
     }
-    if (nvis == 0) {
+    if (nvis <= j0) {
         for (int64_t c = 0; c < d; ++c) out_o[c] = 0.0;
         *out_lse = -INFINITY;
         return;
@@ -78,7 +89,7 @@ static void one_row(const job_t *J, int64_t b, int64_t h, int64_t i,
 
     /* first pass: scores and their maximum */
     double m = -INFINITY;
-    for (int64_t j = 0; j < nvis; ++j) {
+    for (int64_t j = j0; j < nvis; ++j) {
         const double *krow = J->k + ((b * J->Sk + j) * J->Hkv + kvh) * d;
         double acc = 0.0;
         for (int64_t c = 0; c < d; ++c) acc += qrow[c] * krow[c];
@@ -87,15 +98,15 @@ static void one_row(const job_t *J, int64_t b, int64_t h, int64_t i,
     }
     /* second pass: exp(s - m), the denominator, the probabilities */
     double sum = 0.0;
-    for (int64_t j = 0; j < nvis; ++j) {
+    for (int64_t j = j0; j < nvis; ++j) {
         p[j] = exp(s[j] - m);
         sum += p[j];
     }
-    for (int64_t j = 0; j < nvis; ++j) p[j] /= sum;
+    for (int64_t j = j0; j < nvis; ++j) p[j] /= sum;
 
     /* o = P V */
     for (int64_t c = 0; c < d; ++c) out_o[c] = 0.0;
-    for (int64_t j = 0; j < nvis; ++j) {
+    for (int64_t j = j0; j < nvis; ++j) {
         const double *vrow = J->v + ((b * J->Sk + j) * J->Hkv + kvh) * d;
         const double pj = p[j];
         for (int64_t c = 0; c < d; ++c) out_o[c] += pj * vrow[c];
@@ -136,16 +147,19 @@ static void *worker(void *arg) {
  * rows == NULL: compute every row; o is (B,Sq,Hq,d), lse is (B,Hq,Sq).
  * rows != NULL: compute only the nrows flat row ids (b*Hq + h)*Sq + i; o is
  *               (nrows, d) and lse is (nrows), in request order.
+ * Keys are restricted to [k_begin, k_end), 0 <= k_begin <= k_end <= Sk.
  * Returns 0 on success, 1 on bad arguments, 2 if a thread could not start or
  * allocate its scratch rows.
  */
-int oracle_attn_fwd(const double *q, const double *k, const double *v,
-                    double *o, double *lse,
-                    int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
-                    int64_t d, double scale, int causal,
-                    const int64_t *rows, int64_t nrows, int nthreads) {
+int oracle_attn_fwd_range(const double *q, const double *k, const double *v,
+                          double *o, double *lse,
+                          int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
+                          int64_t d, double scale, int causal,
+                          int64_t k_begin, int64_t k_end,
+                          const int64_t *rows, int64_t nrows, int nthreads) {
     if (!q || !k || !v || !o || !lse) return 1;
     if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || d < 1) return 1;
+    if (k_begin < 0 || k_begin > k_end || k_end > Sk) return 1;
     if (Hq % Hkv != 0) return 1;
     if (causal != 0 && causal != 1) return 1;
     if (rows && nrows < 0) return 1;
@@ -167,6 +181,7 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v,
         J->q = q; J->k = k; J->v = v; J->o = o; J->lse = lse;
         J->B = B; J->Sq = Sq; J->Sk = Sk; J->Hq = Hq; J->Hkv = Hkv; J->d = d;
         J->scale = scale; J->causal = causal;
+        J->k_begin = k_begin; J->k_end = k_end;
         J->rows = rows; J->total = total;
         J->first = t; J->stride = nthreads;
         started[t] = pthread_create(&tid[t], NULL, worker, J) == 0;
@@ -179,4 +194,14 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v,
         if (ret) rc = 2;
     }
     return rc;
+}
+
+/* Every key: the plain definition of the forward pass. */
+int oracle_attn_fwd(const double *q, const double *k, const double *v,
+                    double *o, double *lse,
+                    int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
+                    int64_t d, double scale, int causal,
+                    const int64_t *rows, int64_t nrows, int nthreads) {
+    return oracle_attn_fwd_range(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale,
+                                 causal, 0, Sk, rows, nrows, nthreads);
 }

@@ -1,7 +1,8 @@
 """ctypes front end of the fp64 C oracle (test infrastructure only).
 
-The arithmetic lives in ``attn_oracle.c``; this module only widens inputs to
-fp64, passes pointers and reshapes the outputs.
+The attention arithmetic lives in ``attn_oracle.c``; this module widens
+inputs to fp64, passes pointers and reshapes the outputs.  The merge of
+partial states (``merge_partials_oracle``) is written here in numpy fp64.
 """
 from __future__ import annotations
 
@@ -39,12 +40,12 @@ def _load():
         if not os.path.exists(_LIB):
             build_oracle(force=True)
         lib = ctypes.CDLL(_LIB)
-        f = lib.oracle_attn_fwd
+        f = lib.oracle_attn_fwd_range
         f.restype = ctypes.c_int
         dp = ctypes.POINTER(ctypes.c_double)
         i64 = ctypes.c_int64
         f.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64,
-                      ctypes.c_double, ctypes.c_int,
+                      ctypes.c_double, ctypes.c_int, i64, i64,
                       ctypes.POINTER(ctypes.c_int64), i64, ctypes.c_int]
         _lib = lib
     return _lib
@@ -61,12 +62,16 @@ def _as_f64(x) -> np.ndarray:
 
 
 def attn_fwd_oracle(q, k, v, scale: float, causal: bool, rows=None,
-                    nthreads: int | None = None):
+                    nthreads: int | None = None, key_range=None):
     """Exact attention forward in fp64.
 
     q: (B, Sq, Hq, d); k, v: (B, Sk, Hkv, d).  Returns (o, lse):
       rows is None -> o (B, Sq, Hq, d), lse (B, Hq, Sq)
       rows given   -> rows are flat ids (b*Hq + h)*Sq + i; o (n, d), lse (n,)
+    key_range=(k0, k1) keeps only keys k0 <= j < k1 (the causal rule still
+    counts j against the full key length): the partial state of each row over
+    that key subset, o normalised over those keys and lse their log-sum-exp
+    (o = 0, lse = -inf where no key of the range is visible).
     """
     qd, kd, vd = _as_f64(q), _as_f64(k), _as_f64(v)
     B, Sq, Hq, d = qd.shape
@@ -86,11 +91,58 @@ def attn_fwd_oracle(q, k, v, scale: float, causal: bool, rows=None,
         o = np.empty((n, d), np.float64)
         lse = np.empty((n,), np.float64)
         rows_p = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
-    rc = _load().oracle_attn_fwd(
+    k0, k1 = (0, Sk) if key_range is None else (int(key_range[0]), int(key_range[1]))
+    rc = _load().oracle_attn_fwd_range(
         qd.ctypes.data_as(dp), kd.ctypes.data_as(dp), vd.ctypes.data_as(dp),
         o.ctypes.data_as(dp), lse.ctypes.data_as(dp),
-        B, Sq, Sk, Hq, Hkv, d, float(scale), int(bool(causal)),
+        B, Sq, Sk, Hq, Hkv, d, float(scale), int(bool(causal)), k0, k1,
         rows_p, n, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_attn_fwd failed with code {rc}")
     return o, lse
+
+
+def merge_partials_oracle(o_parts, lse_parts):
+    """Combine partial attention states over disjoint key subsets, in fp64.
+
+    o_parts: (P, B, Sq, Hq, d) outputs, each normalised over its own keys;
+    lse_parts: (P, B, Hq, Sq) natural-log sums of exp of the scaled scores of
+    those keys (-inf for a row that saw no key).  Returns (o, lse) of the
+    union of the key subsets, o (B, Sq, Hq, d) and lse (B, Hq, Sq).
+
+    This is the online-softmax state update ("FlashAttention personal
+    implementation notes", section "Online Softmax": m_new = max(m_old, m_t),
+    alpha = e^(m_old - m_new), l_new = alpha l_old + (tile sum),
+    O~_new = alpha O~_old + (tile numerator)), applied with whole parts in the
+    place of tiles.  A normalised part (O_p, lse_p) is the state m = lse_p,
+    l = 1, O~ = O_p: it has the same ratio O~/l and the same m + ln l, so
+    each part enters with a tile weight e^(lse_p - m_new).  The result is
+    O = O~ / l and lse = m + ln l; a row that no part saw stays o = 0,
+    lse = -inf.
+    """
+    op = np.asarray(o_parts, dtype=np.float64)
+    lp = np.asarray(lse_parts, dtype=np.float64)
+    P, B, Sq, Hq, d = op.shape
+    if lp.shape != (P, B, Hq, Sq):
+        raise ValueError(f"lse_parts must be {(P, B, Hq, Sq)}, got {lp.shape}")
+    # move to (P, B, Hq, Sq, d) so that a part's row state lines up with its lse
+    op = op.transpose(0, 1, 3, 2, 4)
+    m = np.full((B, Hq, Sq), -np.inf)
+    l = np.zeros((B, Hq, Sq))
+    acc = np.zeros((B, Hq, Sq, d))
+    for t in range(P):
+        m_t = lp[t]
+        m_new = np.maximum(m, m_t)
+        seen = np.isfinite(m_new)
+        # e^(m_old - m_new) and e^(m_t - m_new); rows no part has seen yet
+        # keep alpha = beta = 0 and their zero state
+        with np.errstate(invalid="ignore"):
+            alpha = np.where(seen, np.exp(m - np.where(seen, m_new, 0.0)), 0.0)
+            beta = np.where(seen, np.exp(m_t - np.where(seen, m_new, 0.0)), 0.0)
+        l = alpha * l + beta * 1.0
+        acc = alpha[..., None] * acc + beta[..., None] * op[t]
+        m = m_new
+    seen = l > 0
+    o = np.where(seen[..., None], acc / np.where(seen, l, 1.0)[..., None], 0.0)
+    lse = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)
+    return o.transpose(0, 2, 1, 3).copy(), lse

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attn_fwd_oracle
+from oracle import attn_fwd_oracle, merge_partials_oracle
 from exact_attention_19_amd.workloads import WORKLOADS, make_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_form_cases.json")
@@ -385,3 +385,125 @@ def test_outlier_recipe_rows():
     for h in range(2):
         nrm = k[0, :, h].float().norm(dim=-1)
         assert int((nrm > 40).sum()) == 5
+
+
+# ------------------------------------------ partial states and their merge
+
+def test_merge_golden_cases():
+    data = json.load(open(GOLDEN))["merge_cases"]
+    for case in data["cases"]:
+        op = _arr(case["o_parts"])             # (P, d)
+        lp = np.array([_num(x) for x in case["lse_parts"]])
+        P, d = op.shape
+        o, lse = merge_partials_oracle(op.reshape(P, 1, 1, 1, d), lp.reshape(P, 1, 1, 1))
+        want_o = np.array([_num(x) for x in case["o"]])
+        want_lse = _num(case["lse"])
+        np.testing.assert_allclose(o.reshape(d), want_o, rtol=1e-14, atol=1e-14,
+                                   err_msg=case["name"])
+        if math.isinf(want_lse):
+            assert np.isneginf(lse.item()), case["name"]
+        else:
+            assert abs(lse.item() - want_lse) <= 1e-14 * max(1.0, abs(want_lse)), case["name"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Sk,cuts", [
+    (21, 21, [0, 8, 16, 21]),
+    (13, 30, [0, 1, 2, 17, 30]),      # single-key parts
+    (30, 13, [0, 5, 5, 13]),          # an empty range, rows with no key
+    (9, 40, [0, 40]),                 # one part
+    (17, 64, [0, 16, 32, 48, 64]),
+])
+def test_key_range_partials_merge_to_full_attention(causal, Sq, Sk, cuts):
+    """Partial states over a partition of the keys, merged, give the
+    attention over all keys: the softmax of the union factors through the
+    per-subset maxima and sums."""
+    q, k, v = _rand(40 + Sq, 2, Sq, Sk, 4, 2, 8)
+    o, lse = attn_fwd_oracle(q, k, v, 0.7, causal)
+    parts = [attn_fwd_oracle(q, k, v, 0.7, causal, key_range=(a, b))
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    om, lm = merge_partials_oracle(np.stack([p[0] for p in parts]),
+                                   np.stack([p[1] for p in parts]))
+    np.testing.assert_allclose(om, o, rtol=0, atol=1e-13)
+    fin = np.isfinite(lse)
+    assert np.array_equal(fin, np.isfinite(lm))
+    np.testing.assert_allclose(lm[fin], lse[fin], rtol=0, atol=1e-13)
+
+
+def test_key_range_brute_force_python_loops():
+    """Partial state over keys [2, 5) with pure-Python loops: the softmax of
+    the visible keys of the range alone."""
+    q, k, v = _rand(41, 1, 4, 7, 2, 1, 3)
+    scale, k0, k1 = 0.6, 2, 5
+    o, lse = attn_fwd_oracle(q, k, v, scale, True, key_range=(k0, k1))
+    for h in range(2):
+        for i in range(4):
+            vis = [j for j in range(k0, k1) if j <= i + 3]
+            s = [scale * sum(q[0, i, h, c] * k[0, j, 0, c] for c in range(3)) for j in vis]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            for c in range(3):
+                want = sum(e[t] / z * v[0, j, 0, c] for t, j in enumerate(vis))
+                assert abs(o[0, i, h, c] - want) < 1e-14
+            assert abs(lse[0, h, i] - (mx + math.log(z))) < 1e-14
+
+
+def test_key_range_zero_q_is_mean_of_range():
+    """Q = 0: equal scores, so each row's partial output is the mean of V over
+    the visible keys of the range, and lse is the log of their count."""
+    r = _rng(42)
+    Sq, Sk, d = 6, 10, 4
+    q = np.zeros((1, Sq, 1, d))
+    k = r.standard_normal((1, Sk, 1, d))
+    v = r.standard_normal((1, Sk, 1, d))
+    k0, k1 = 3, 8
+    o, lse = attn_fwd_oracle(q, k, v, 1.0, True, key_range=(k0, k1))
+    for i in range(Sq):
+        vis = [j for j in range(k0, k1) if j <= i + Sk - Sq]
+        if not vis:
+            assert np.all(o[0, i, 0] == 0) and np.isneginf(lse[0, 0, i])
+            continue
+        np.testing.assert_allclose(o[0, i, 0], v[0, vis, 0].mean(axis=0), atol=1e-15)
+        assert abs(lse[0, 0, i] - math.log(len(vis))) < 1e-15
+
+
+def test_key_range_empty_gives_zero_and_minus_inf():
+    q, k, v = _rand(43, 1, 5, 9, 2, 2, 4)
+    o, lse = attn_fwd_oracle(q, k, v, 1.0, False, key_range=(4, 4))
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_merge_identical_parts_adds_log_count():
+    """P copies of one state: the same output, lse + ln P."""
+    r = _rng(44)
+    o1 = r.standard_normal((1, 2, 5, 3, 8))
+    l1 = r.standard_normal((1, 2, 3, 5))
+    for P in (2, 3, 7):
+        o, lse = merge_partials_oracle(np.repeat(o1, P, 0), np.repeat(l1, P, 0))
+        np.testing.assert_allclose(o, o1[0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse, l1[0] + math.log(P), rtol=0, atol=1e-14)
+
+
+def test_merge_is_order_free():
+    r = _rng(45)
+    op = r.standard_normal((5, 1, 4, 2, 8))
+    lp = 3 * r.standard_normal((5, 1, 2, 4))
+    lp[2, 0, 1, :2] = -np.inf
+    o1, l1 = merge_partials_oracle(op, lp)
+    perm = [3, 0, 4, 2, 1]
+    o2, l2 = merge_partials_oracle(op[perm], lp[perm])
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-14)
+
+
+def test_merge_bad_shapes_rejected():
+    with pytest.raises(ValueError):
+        merge_partials_oracle(np.zeros((2, 1, 3, 1, 4)), np.zeros((2, 1, 1, 4)))
+
+
+def test_key_range_bad_arguments_rejected():
+    q, k, v = _rand(46, 1, 3, 5, 1, 1, 4)
+    for kr in ((-1, 3), (3, 2), (0, 6)):
+        with pytest.raises(ValueError):
+            attn_fwd_oracle(q, k, v, 1.0, False, key_range=kr)
