@@ -1,8 +1,12 @@
 """Benchmark of the fused attention forward on one MI355X.
 
-One step is one attn_fwd launch (the whole fused path: Q tile load, K/V
-streaming, both MFMA products, online softmax, masking, epilogue) over one
-batch of seeded synthetic input already resident in HBM.  Prints ONE JSON line:
+One step is one attn_fwd_split call over one batch of seeded synthetic input
+already resident in HBM: the whole fused path (Q tile load, K/V streaming,
+both MFMA products, online softmax, masking, epilogue).  Where the query
+blocks fill the GPU (the 8K and 16K GQA workloads) that is a single attention
+kernel launch, the same as attn_fwd; for short sequences the library's
+automatic key split adds the merge kernel, and the step is both launches.
+Prints ONE JSON line:
 
   value         causal-adjusted TFLOP/s: (4*Sq*Sk*d*Hq*B, halved when causal)
                 divided by the mean wall time per step over the timed steps
@@ -12,6 +16,7 @@ batch of seeded synthetic input already resident in HBM.  Prints ONE JSON line:
                 of rows of the same workload (a baseline, not a target)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--kv-split N]
 """
 from __future__ import annotations
 
@@ -101,6 +106,45 @@ def cpu_baseline(w, q, k, v, budget_s: float = 15.0):
             "seconds": round(dt, 2)}
 
 
+def board_power():
+    """Socket power and core clocks as amd-smi reports them (text), or None."""
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True,
+                             text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    watts = [l.split(":")[1].strip() for l in out.splitlines() if "SOCKET_POWER" in l]
+    clks = [l.split(":")[1].strip() for l in out.splitlines()
+            if l.strip().startswith("CLK:")][:8]
+    return {"socket_power": watts[0] if watts else None, "gfx_clk": clks}
+
+
+def gemm_probe(steps: int):
+    """Sustained rate of a plain bf16 GEMM (8192^3 through torch.matmul) on the
+    same board: the practical matrix-core ceiling under its power limit, as a
+    reference for the attention kernel's rate."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+    for _ in range(20):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        torch.matmul(a, b, out=c)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    print(json.dumps({"gemm_probe": f"bf16 {n}x{n}x{n}", "ms": round(ms, 4),
+                      "tflops": round(2 * n ** 3 / ms / 1e9, 1), "board": board_power()}),
+          flush=True)
+
+
 def copy_probe(mib: int, steps: int):
     """Device-to-device copy of a known size, for scaling the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE) of a profiler run to bytes."""
@@ -123,7 +167,12 @@ def main():
     # timed steps measure the sustained rate
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--kv-split", type=int, default=0,
+                    help="key split of attn_fwd_split: 0 = the library's choice, "
+                         "1 = none, N = at most N pieces per query block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only time a plain bf16 GEMM --steps times (reference)")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a device copy of MIB MiB --steps times "
                          "(calibration of the profiler's byte counters)")
@@ -137,9 +186,13 @@ def main():
     if args.copy_probe > 0:
         copy_probe(args.copy_probe, args.steps)
         return
+    if args.gemm_probe:
+        gemm_probe(args.steps)
+        return
 
     import torch
-    from exact_attention_19_amd import attn_fwd, attn_fwd_plan, load_library
+    from exact_attention_19_amd import (attn_fwd_plan, attn_fwd_split, attn_fwd_split_plan,
+                                        attn_fwd_split_workspace, load_library)
     from exact_attention_19_amd.binding import ATTN_DTYPE_BF16, ATTN_DTYPE_F16
     from exact_attention_19_amd.workloads import WORKLOADS, input_digest, make_inputs
 
@@ -152,9 +205,15 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    dt_code = ATTN_DTYPE_BF16 if w.dtype == "bf16" else ATTN_DTYPE_F16
+    shape = (w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.d, int(w.causal), dt_code)
+    split = attn_fwd_split_plan(*shape, kv_split=args.kv_split)
+    ws_bytes = attn_fwd_split_workspace(*shape, kv_split=args.kv_split)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step():
-        attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+        attn_fwd_split(q, k, v, scale=w.scale, causal=w.causal, kv_split=args.kv_split,
+                       out=o, lse=lse, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -180,8 +239,7 @@ def main():
     flops = w.metric_flops()
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / kern_avg_s / 1e12
-    dt_code = ATTN_DTYPE_BF16 if w.dtype == "bf16" else ATTN_DTYPE_F16
-    plan = attn_fwd_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.d, int(w.causal), dt_code)
+    plan = attn_fwd_plan(*shape)
     props = torch.cuda.get_device_properties(dev)
 
     result = {
@@ -208,6 +266,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
             "traffic": measured_traffic(w.name),
+            # with a key split the step is two launches (attention, merge):
+            # the event pair then times both
+            "launches_per_step": 2 if split["keys_per_piece"] > 0 else 1,
             "kernel_avg_us": round(kern_avg_s * 1e6, 2),
             "kernel_min_us": round(kern_min_s * 1e6, 2),
             "kernel_median_us": round(kern_med_s * 1e6, 2),
@@ -216,7 +277,9 @@ def main():
             "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
         },
         "launch": plan,
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "split": dict(split, kv_split_arg=args.kv_split, workspace_bytes=ws_bytes),
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "board_after_timed_steps": board_power()},
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:

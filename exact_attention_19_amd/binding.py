@@ -15,9 +15,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
-ATTN_DTYPE_F16, ATTN_DTYPE_BF16 = 0, 1
-EXPORTED = ("attn_fwd", "attn_fwd_check", "attn_fwd_plan", "attn_status_str",
-            "attn_abi_version")
+ATTN_DTYPE_F16, ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1, 2
+EXPORTED = ("attn_fwd", "attn_fwd_check", "attn_fwd_plan", "attn_fwd_split",
+            "attn_fwd_split_workspace", "attn_fwd_split_plan", "attn_merge",
+            "attn_merge_check", "attn_status_str", "attn_abi_version")
 
 _lib = None
 
@@ -45,6 +46,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i]
     lib.attn_fwd_plan.restype = i
     lib.attn_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i), i]
+    sz = ctypes.c_size_t
+    lib.attn_fwd_split.restype = i
+    lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.attn_fwd_split_workspace.restype = i
+    lib.attn_fwd_split_workspace.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.attn_fwd_split_plan.restype = i
+    lib.attn_fwd_split_plan.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(i), i]
+    lib.attn_merge.restype = i
+    lib.attn_merge.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i, vp]
+    lib.attn_merge_check.restype = i
+    lib.attn_merge_check.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [i]
     lib.attn_abi_version.restype = i
@@ -61,12 +73,14 @@ def attn_abi_version() -> int:
     return int(load_library().attn_abi_version())
 
 
-def _dtype_code(t) -> int:
+def _dtype_code(t, allow_f32: bool = False) -> int:
     import torch
     if t.dtype == torch.float16:
         return ATTN_DTYPE_F16
     if t.dtype == torch.bfloat16:
         return ATTN_DTYPE_BF16
+    if allow_f32 and t.dtype == torch.float32:
+        return ATTN_DTYPE_F32
     raise TypeError(f"unsupported dtype {t.dtype}: q, k, v must be float16 or bfloat16")
 
 
@@ -89,16 +103,36 @@ def attn_fwd_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Sq, Sk, Hq, Hkv, d,
                                              int(causal), dtype_code))
 
 
-def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
-             out=None, lse=None, return_lse: bool = True, stream=None):
-    """O = softmax(scale * Q K^T + M) V and its LSE, on the GPU.
+def attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype_code, kv_split=0) -> dict:
+    """The launches attn_fwd_split would make (no device call)."""
+    out = (ctypes.c_int * 5)()
+    st = load_library().attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), dtype_code,
+                                            int(kv_split), out, 5)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_split_plan")
+    keys = ("grid", "pieces", "keys_per_piece", "first_split_row", "merge_grid")
+    return dict(zip(keys, list(out)))
 
-    q: (B, Sq, Hq, d); k, v: (B, Sk, Hkv, d); fp16 or bf16 CUDA tensors, dense.
-    Returns (o, lse) with lse fp32 (B, Hq, Sq), or (o, None) if
-    return_lse is False.  The launch goes to ``stream`` (a torch.cuda.Stream)
-    or the current stream.
-    """
-    import torch
+
+def attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, causal, dtype_code, kv_split=0) -> int:
+    """Workspace bytes attn_fwd_split needs (0 when it would not split)."""
+    n = ctypes.c_size_t(0)
+    st = load_library().attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, int(causal),
+                                                 dtype_code, int(kv_split), ctypes.byref(n))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_split_workspace")
+    return int(n.value)
+
+
+def attn_merge_check(o_parts_ptr, lse_parts_ptr, n_parts, parts_dtype, B, Sq, Hq, d,
+                     o_ptr, lse_ptr, dtype_code) -> int:
+    """attn_merge's validation on raw integer addresses; returns the status."""
+    return int(load_library().attn_merge_check(o_parts_ptr, lse_parts_ptr, n_parts,
+                                               parts_dtype, B, Sq, Hq, d, o_ptr, lse_ptr,
+                                               dtype_code))
+
+
+def _check_qkv(q, k, v):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (batch, seq, heads, d_head)")
     B, Sq, Hq, d = q.shape
@@ -114,8 +148,12 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous (batch, seq, heads, d_head)")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
+    return B, Sq, Sk, Hq, Hkv, d, code
+
+
+def _outputs(q, out, lse, return_lse):
+    import torch
+    B, Sq, Hq, _ = q.shape
     if out is None:
         out = torch.empty_like(q)
     if return_lse and lse is None:
@@ -123,6 +161,23 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (B, Hq, Sq)):
         raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+    return out, lse
+
+
+def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
+             out=None, lse=None, return_lse: bool = True, stream=None):
+    """O = softmax(scale * Q K^T + M) V and its LSE, on the GPU.
+
+    q: (B, Sq, Hq, d); k, v: (B, Sk, Hkv, d); fp16 or bf16 CUDA tensors, dense.
+    Returns (o, lse) with lse fp32 (B, Hq, Sq), or (o, None) if
+    return_lse is False.  The launch goes to ``stream`` (a torch.cuda.Stream)
+    or the current stream.
+    """
+    import torch
+    B, Sq, Sk, Hq, Hkv, d, code = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse, return_lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = load_library().attn_fwd(
@@ -132,4 +187,74 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
         ctypes.c_void_p(stream.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_split(q, k, v, scale: float | None = None, causal: bool = False,
+                   kv_split: int = 0, out=None, lse=None, return_lse: bool = True,
+                   workspace=None, stream=None):
+    """attn_fwd with the keys of long query blocks split over workgroups and
+    merged (for grids too small to fill the GPU).  kv_split: 0 = the
+    library's choice, 1 = no split, k > 1 = at most k pieces per block.
+    ``workspace`` is a uint8 CUDA tensor of at least attn_fwd_split_workspace
+    bytes (allocated here when None).  Returns (o, lse) as attn_fwd does."""
+    import torch
+    B, Sq, Sk, Hq, Hkv, d, code = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse, return_lse)
+    if workspace is None:  # (a given workspace is size-checked by the library)
+        need = attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, causal, code, kv_split)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().attn_fwd_split(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None,
+        B, Sq, Sk, Hq, Hkv, d, float(scale), int(bool(causal)), code, int(kv_split),
+        ws_ptr, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_split")
+    return out, lse
+
+
+def attn_merge(o_parts, lse_parts, dtype=None, out=None, lse=None,
+               return_lse: bool = True, stream=None):
+    """Merge partial attention states over disjoint key subsets.
+
+    o_parts: (P, B, Sq, Hq, d) CUDA tensor, float32, float16 or bfloat16, each
+    part normalised over its own keys; lse_parts: (P, B, Hq, Sq) float32
+    (-inf = the part saw no key).  dtype: the output dtype (torch.float16 or
+    torch.bfloat16; default: that of o_parts, or bfloat16 for float32 parts).
+    Returns (o, lse) of the union: o (B, Sq, Hq, d), lse (B, Hq, Sq)."""
+    import torch
+    if o_parts.dim() != 5 or lse_parts.dim() != 4:
+        raise ValueError("o_parts must be (P, B, Sq, Hq, d) and lse_parts (P, B, Hq, Sq)")
+    P, B, Sq, Hq, d = o_parts.shape
+    if tuple(lse_parts.shape) != (P, B, Hq, Sq) or lse_parts.dtype != torch.float32:
+        raise ValueError("lse_parts must be a float32 (P, B, Hq, Sq) tensor")
+    for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    pcode = _dtype_code(o_parts, allow_f32=True)
+    if dtype is None:
+        dtype = torch.bfloat16 if o_parts.dtype == torch.float32 else o_parts.dtype
+    if out is None:
+        out = torch.empty((B, Sq, Hq, d), dtype=dtype, device=o_parts.device)
+    ocode = _dtype_code(out)
+    if tuple(out.shape) != (B, Sq, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B, Sq, Hq, d) tensor")
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=o_parts.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(o_parts.device)
+    st = load_library().attn_merge(
+        o_parts.data_ptr(), lse_parts.data_ptr(), P, pcode, B, Sq, Hq, d, out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, ocode,
+        ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_merge")
     return out, lse

@@ -49,6 +49,12 @@
 // * Work items are ordered heaviest-first (causal row blocks near the end of
 //   the sequence first) and, when the counts allow, grouped per XCD so that
 //   the workgroups sharing a kv head land on the same L2.
+// * Key split (attn_fwd_split): when the row blocks are too few to fill the
+//   chip, the K/V tiles of a row block are cut into pieces of a fixed number
+//   of tiles, one workgroup per piece.  A piece writes its row states in fp32
+//   (output normalised over its own keys, and the log-sum-exp of those keys)
+//   and a second kernel merges the pieces with the online-softmax rescale
+//   (personal-notes page, section "Online Softmax", applied to whole pieces).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -62,6 +68,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -157,7 +164,32 @@ struct Params {
   int xcd_cols;  // columns per XCD when the grid is XCD-ordered, else 0
   int off;       // Sk - Sq
   float scale_log2;  // scale * log2(e)
+  // key split: K/V tiles per piece (even; 0 = no split).  A row block with
+  // more tiles than that is cut into pieces; the pieces write fp32 partial
+  // states for rows q_split.. Sq-1 (sq_split = Sq - q_split rows):
+  //   part_o  [piece][b][i - q_split][hq][D], normalised over the piece's keys
+  //   part_lse[piece][b][hq][i - q_split], natural log (-inf: no key seen)
+  int chunk;
+  int q_split, sq_split;
+  float* part_o;
+  float* part_lse;
 };
+
+// K/V tiles visited by the query rows [q0, q0 + rows) (clipped to Sq): the
+// causal limit of the last row, or all of K.
+__host__ __device__ inline int block_tiles(int q0, int rows, int Sq, int Sk, int off,
+                                           bool causal) {
+  const int q_last = (q0 + rows < Sq ? q0 + rows : Sq) - 1;
+  int kv_end = Sk;
+  if (causal && q_last + off + 1 < kv_end) kv_end = q_last + off + 1;
+  return kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+}
+
+// Pieces of a row block of `tiles` tiles under a split of `chunk` tiles per
+// piece (a block that fits one piece is not split).
+__host__ __device__ inline int block_pieces(int tiles, int chunk) {
+  return (chunk > 0 && tiles > chunk) ? (tiles + chunk - 1) / chunk : 1;
+}
 
 // 16-byte-chunk XOR swizzle of a K/V tile row in LDS.  Row r of the tile
 // stores its logical chunk s at physical chunk s ^ swz(r).  For d = 128 (16
@@ -250,19 +282,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- work decode: heaviest row blocks first, optionally grouped per XCD
-  int qt, col;
+  // ---- work decode: heaviest row blocks first, optionally grouped per XCD;
+  // with a key split, all first pieces, then all second pieces, ...
+  int qt, col, piece;
   {
     const int L = blockIdx.x;
+    int u;
     if (p.xcd_cols > 0) {
       const int xcd = L & 7;
       const int k = L >> 3;
-      qt = p.qtiles - 1 - k / p.xcd_cols;
+      u = k / p.xcd_cols;
       col = xcd * p.xcd_cols + k % p.xcd_cols;
     } else {
-      qt = p.qtiles - 1 - L / p.ncols;
+      u = L / p.ncols;
       col = L % p.ncols;
     }
+    piece = u / p.qtiles;
+    qt = p.qtiles - 1 - (u - piece * p.qtiles);
   }
   const int hs = col % p.hsub;
   const int kvh = (col / p.hsub) % p.Hkv;
@@ -273,11 +309,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   const int q0wg = qt * p.rows_wg;
   const int q0w = q0wg + rowblk * 32;
 
-  // ---- KV tile range of the workgroup (all waves walk the same tiles)
-  const int q_last_wg = min(q0wg + p.rows_wg, p.Sq) - 1;
-  int kv_end = p.Sk;
-  if (CAUSAL) kv_end = min(p.Sk, q_last_wg + p.off + 1);
-  const int n_end = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  // ---- KV tile range of the workgroup (all waves walk the same tiles):
+  // tiles [j_lo, j_hi) of the row block's n_end.  j_lo is even (the chunk is
+  // even), so tile j always sits in buffer j & 1.
+  const int n_end = block_tiles(q0wg, p.rows_wg, p.Sq, p.Sk, p.off, CAUSAL);
+  const int pieces = block_pieces(n_end, p.chunk);
+  if (piece >= pieces) return;  // an empty piece: uniform over the workgroup
+  const bool split = pieces > 1;
+  const int j_lo = piece * p.chunk;
+  const int j_hi = split ? min(n_end, j_lo + p.chunk) : n_end;
   int n_full = p.Sk / BC;
   if (CAUSAL) {
     const int lim = q0wg + p.off + 1;
@@ -467,7 +507,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
     LDS_PTR(char) const V_PREV = vbuf_of(PAR ^ 1);  // V(j-1)
     LDS_PTR(char) const K_LOAD = kbuf_of(PAR);      // K(j+2)
     LDS_PTR(char) const V_LOAD = vbuf_of(PAR);      // V(j)
-    if (j + 2 < n_end) issue_rows(kslice, j + 2, K_LOAD);
+    if (j + 2 < j_hi) issue_rows(kslice, j + 2, K_LOAD);
     issue_rows(vslice, j, V_LOAD);
     // mask the straddling tiles, then the row max and the max update
     if (j >= n_full) {
@@ -581,11 +621,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
     __syncthreads();
   };
 
-  if (n_end > 0) {
-    // prologue: K(0) and K(1) in flight; the V buffer read for "tile -1" in
-    // iteration 0 is cleared so that 0 * V stays 0.
-    issue_rows(kslice, 0, kbuf_of(0));
-    if (n_end > 1) issue_rows(kslice, 1, kbuf_of(1));
+  if (j_hi > j_lo) {
+    // prologue: K(j_lo) and K(j_lo+1) in flight; the V buffer read for the
+    // tile before j_lo in the first iteration is cleared so that 0 * V stays 0.
+    issue_rows(kslice, j_lo, kbuf_of(0));
+    if (j_lo + 1 < j_hi) issue_rows(kslice, j_lo + 1, kbuf_of(1));
     {
       LDS_PTR(u32x4) z = (LDS_PTR(u32x4))vbuf_of(1);
       for (int i = tid; i < TB / 16; i += NT) z[i] = (u32x4){0u, 0u, 0u, 0u};
@@ -594,12 +634,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
     __syncthreads();
     qk(SA, kbuf_of(0));
     __syncthreads();  // every wave has read K(0) before K(2) overwrites it
-    int j = 0;
-    for (; j + 1 < n_end; j += 2) {
+    int j = j_lo;
+    for (; j + 1 < j_hi; j += 2) {
       iter(std::integral_constant<int, 0>{}, j, SA, SB, PB, PA);
       iter(std::integral_constant<int, 1>{}, j + 1, SB, SA, PA, PB);
     }
-    if (j < n_end) {
+    if (j < j_hi) {
       iter(std::integral_constant<int, 0>{}, j, SA, SB, PB, PA);
       pv(PA, vbuf_of(j));  // drain: the last tile's P is in PA
     } else {
@@ -621,7 +661,25 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
     const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
     float l_lse = l_tot;
     if constexpr (T::LSE_FROM_FP32_SUM) l_lse = pair_sum(l_fp32);
-    if (qi < p.Sq) {
+    if (split && qi < p.Sq) {
+      // fp32 partial state of this piece (rows of a split block are >= q_split)
+      const int ii = qi - p.q_split;
+      float* prow = p.part_o +
+                    ((((int64_t)piece * p.B + b) * p.sq_split + ii) * p.Hq + hq) * D;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = acc_o[cb][4 * g + r] * inv;
+          *(f32x4*)(prow + cb * 32 + 8 * g + 4 * hh) = x;
+        }
+      if (hh == 0) {
+        const float lse = has ? (m_run + __builtin_amdgcn_logf(l_lse)) * LN2 : -INFINITY;
+        p.part_lse[(((int64_t)piece * p.B + b) * p.Hq + hq) * p.sq_split + ii] = lse;
+      }
+    } else if (qi < p.Sq) {
       uint16_t* orow = p.o + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
@@ -644,6 +702,109 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
       }
     }
   }
+}
+
+// ------------------------------------------------------------ merge kernel
+//
+// Combines partial row states over disjoint key subsets into the state of
+// their union: with M = max_p lse_p and w_p = e^(lse_p - M),
+//   O = sum_p w_p O_p / sum_p w_p,   LSE = M + ln sum_p w_p.
+// This is the online-softmax update of the personal-notes page (section
+// "Online Softmax": new max, the factor e^(m_old - m_new) on the old
+// denominator and output) with a whole normalised part (O_p, lse_p), i.e. the
+// state m = lse_p, l = 1, in the place of a tile.  A part with lse = -inf saw
+// no key and gets weight 0; a row that no part saw gets O = 0, LSE = -inf.
+//
+// Memory-bound: each thread owns 4 consecutive elements of one row (D / 4
+// threads per row), so the reads of a part row and the write of O are
+// contiguous across the row's threads.
+struct MergeParams {
+  const void* parts;      // part p, row r: parts + (p * rows + r) * D elements
+  const float* parts_lse; // part p, (b, h, i): + p * rows + (b * Hq + h) * sq_rows + i - q_first
+  uint16_t* o;            // (B, Sq, Hq, D)
+  float* lse;             // (B, Hq, Sq) or null
+  int B, Sq, Hq;
+  int n_parts;  // parts per row; 0 = the piece count of a key split (below)
+  int q_first;  // first merged query row; rows are (b, q_first.. Sq-1, h)
+  int sq_rows;  // Sq - q_first
+  int64_t rows; // B * sq_rows * Hq
+  // key split (n_parts == 0): row i has block_pieces(block_tiles(...)) parts
+  int rows_wg, chunk, Sk, off, causal;
+};
+
+template <int PDT>
+__device__ __forceinline__ f32x4 load_part4(const void* base, int64_t elem) {
+  if constexpr (PDT == ATTN_DTYPE_F32) {
+    return *(const f32x4*)((const float*)base + elem);
+  } else {
+    const u32x2 w = *(const u32x2*)((const uint16_t*)base + elem);
+    f32x4 x;
+    if constexpr (PDT == ATTN_DTYPE_BF16) {
+      x[0] = __uint_as_float(w[0] << 16);
+      x[1] = __uint_as_float(w[0] & 0xffff0000u);
+      x[2] = __uint_as_float(w[1] << 16);
+      x[3] = __uint_as_float(w[1] & 0xffff0000u);
+    } else {
+      // one half at a time: reading both halves of w[1] through a bit cast of
+      // the vector element to a two-half vector was compiled to a reuse of
+      // w[0] (one dword loaded instead of two)
+      x[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xffffu));
+      x[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] >> 16));
+      x[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] & 0xffffu));
+      x[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] >> 16));
+    }
+    return x;
+  }
+}
+
+template <int PDT, int ODT, int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
+  constexpr int TPR = D / 4;        // threads per row
+  constexpr int RPB = 256 / TPR;    // rows per workgroup
+  constexpr float LOG2E = 1.44269504088896340736f;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (r >= p.rows) return;
+  const int c = (threadIdx.x % TPR) * 4;
+  const int hq = (int)(r % p.Hq);
+  const int64_t t = r / p.Hq;
+  const int ii = (int)(t % p.sq_rows);
+  const int b = (int)(t / p.sq_rows);
+  const int qi = p.q_first + ii;
+  int n = p.n_parts;
+  if (n == 0) {
+    const int q0 = (qi / p.rows_wg) * p.rows_wg;
+    n = block_pieces(block_tiles(q0, p.rows_wg, p.Sq, p.Sk, p.off, p.causal != 0), p.chunk);
+    if (n == 1) return;  // a block that was not split wrote O itself
+  }
+  const int64_t lrow = ((int64_t)b * p.Hq + hq) * p.sq_rows + ii;
+  float M = -INFINITY;
+  for (int q = 0; q < n; ++q) M = fmaxf(M, p.parts_lse[(int64_t)q * p.rows + lrow]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float W = 0.f;
+  if (M > -INFINITY) {
+    for (int q = 0; q < n; ++q) {
+      const float w =
+          __builtin_amdgcn_exp2f((p.parts_lse[(int64_t)q * p.rows + lrow] - M) * LOG2E);
+      const f32x4 x = load_part4<PDT>(p.parts, ((int64_t)q * p.rows + r) * D + c);
+      W += w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, x[e], acc[e]);
+    }
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  f32x8 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[e] = acc[e] * inv;
+    y[e + 4] = 0.f;
+  }
+  const i16x8 h = Ty<ODT>::cvt(y);
+  const u32x2 w2 = {(unsigned)(uint16_t)h[0] | ((unsigned)(uint16_t)h[1] << 16),
+                    (unsigned)(uint16_t)h[2] | ((unsigned)(uint16_t)h[3] << 16)};
+  *(u32x2*)(p.o + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D + c) = w2;
+  if (p.lse != nullptr && c == 0)
+    p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] =
+        W > 0.f ? M + __builtin_amdgcn_logf(W) * LN2 : -INFINITY;
 }
 
 // ------------------------------------------------------------ host side
@@ -701,19 +862,146 @@ Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
   return pl;
 }
 
+// Key split.  Workgroup slots of the chip: 256 CUs x 2 resident workgroups of
+// the attention kernel.  When the row blocks alone leave slots idle, the
+// automatic choice cuts every block into pieces of about (total tiles /
+// slots) tiles, but never below kMinChunk tiles: a piece pays its own Q load,
+// pipeline fill and fp32 partial write, and the merge reads every partial.
+constexpr int kSlots = 512;
+constexpr int kMinChunk = 4;
+
+struct SplitPlan {
+  Plan base;
+  int chunk;           // tiles per piece, even; 0 = no split
+  int npieces;         // pieces of the longest row block
+  int q_first;         // first query row of a split block (Sq if none)
+  long long grid;      // attention workgroups
+  long long merge_rows;
+  long long merge_grid;
+  size_t lse_offset;   // byte offset of part_lse in the workspace
+  size_t ws_bytes;     // workspace bytes (0 = none)
+};
+
+SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
+                          int kv_split) {
+  SplitPlan sp{};
+  sp.base = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
+  const Plan& pl = sp.base;
+  sp.chunk = 0;
+  sp.npieces = 1;
+  sp.q_first = Sq;
+  sp.grid = pl.grid;
+  if (pl.grid <= 0 || kv_split == 1) return sp;
+  const int off = Sk - Sq;
+  const int nmax = block_tiles((pl.qtiles - 1) * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0);
+  int chunk;
+  if (kv_split == 0) {
+    if ((long long)pl.qtiles * pl.ncols >= kSlots) return sp;
+    long long total = 0;
+    for (int qt = 0; qt < pl.qtiles; ++qt)
+      total += block_tiles(qt * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0);
+    total *= pl.ncols;
+    long long c = (total + kSlots - 1) / kSlots;
+    if (c < kMinChunk) c = kMinChunk;
+    chunk = (int)(c > nmax ? nmax : c);
+  } else {
+    chunk = (nmax + kv_split - 1) / kv_split;
+  }
+  chunk += chunk & 1;  // even: a piece starts on buffer 0 of the tile ring
+  if (chunk < 2) chunk = 2;
+  if (chunk >= nmax) return sp;
+  sp.chunk = chunk;
+  sp.npieces = block_pieces(nmax, chunk);
+  int qt0 = 0;
+  while (block_pieces(block_tiles(qt0 * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0),
+                      chunk) == 1)
+    ++qt0;  // ends: the last block has npieces > 1 pieces
+  sp.q_first = qt0 * pl.rows_wg;
+  sp.grid = (long long)sp.npieces * pl.qtiles * pl.ncols;
+  sp.merge_rows = (long long)B * (Sq - sp.q_first) * Hq;
+  const int rpb = 256 / (d / 4);
+  sp.merge_grid = (sp.merge_rows + rpb - 1) / rpb;
+  const size_t parts = (size_t)sp.npieces * (size_t)sp.merge_rows;
+  sp.lse_offset = ((parts * (size_t)d * 4) + 255) & ~(size_t)255;
+  sp.ws_bytes = sp.lse_offset + parts * 4;
+  if (sp.grid > 0x7fffffffll || sp.merge_grid > 0x7fffffffll) sp.grid = -1;
+  return sp;
+}
+
+template <int PDT, int ODT>
+hipError_t launch_merge(int d, long long grid, const MergeParams& mp, hipStream_t st) {
+  if (d == 128)
+    hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 128>), dim3((unsigned)grid), dim3(256), 0,
+                       st, mp);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 64>), dim3((unsigned)grid), dim3(256), 0,
+                       st, mp);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_any(int parts_dtype, int dtype, int d, long long grid,
+                            const MergeParams& mp, hipStream_t st) {
+  if (dtype == ATTN_DTYPE_BF16) {
+    if (parts_dtype == ATTN_DTYPE_F32) return launch_merge<ATTN_DTYPE_F32, ATTN_DTYPE_BF16>(d, grid, mp, st);
+    if (parts_dtype == ATTN_DTYPE_BF16) return launch_merge<ATTN_DTYPE_BF16, ATTN_DTYPE_BF16>(d, grid, mp, st);
+    return launch_merge<ATTN_DTYPE_F16, ATTN_DTYPE_BF16>(d, grid, mp, st);
+  }
+  if (parts_dtype == ATTN_DTYPE_F32) return launch_merge<ATTN_DTYPE_F32, ATTN_DTYPE_F16>(d, grid, mp, st);
+  if (parts_dtype == ATTN_DTYPE_BF16) return launch_merge<ATTN_DTYPE_BF16, ATTN_DTYPE_F16>(d, grid, mp, st);
+  return launch_merge<ATTN_DTYPE_F16, ATTN_DTYPE_F16>(d, grid, mp, st);
+}
+
 template <int DT, int D, bool CAUSAL>
-hipError_t launch_t(const Plan& pl, const Params& p, hipStream_t st) {
-  dim3 grid(pl.grid), block(pl.nw * 64);
+hipError_t launch_t(const Plan& pl, long long nwg, const Params& p, hipStream_t st) {
+  dim3 grid((unsigned)nwg), block(pl.nw * 64);
   // the tile buffers are static LDS (pl.lds_bytes reports their size)
   hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 4>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_d(int d, bool causal, const Plan& pl, const Params& p, hipStream_t st) {
+hipError_t launch_d(int d, bool causal, const Plan& pl, long long nwg, const Params& p,
+                    hipStream_t st) {
   if (d == 128)
-    return causal ? launch_t<DT, 128, true>(pl, p, st) : launch_t<DT, 128, false>(pl, p, st);
-  return causal ? launch_t<DT, 64, true>(pl, p, st) : launch_t<DT, 64, false>(pl, p, st);
+    return causal ? launch_t<DT, 128, true>(pl, nwg, p, st)
+                  : launch_t<DT, 128, false>(pl, nwg, p, st);
+  return causal ? launch_t<DT, 64, true>(pl, nwg, p, st) : launch_t<DT, 64, false>(pl, nwg, p, st);
+}
+
+Params fill_params(const Plan& pl, const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int Sq, int Sk, int Hq, int Hkv, float scale) {
+  Params p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.gh = pl.gh;
+  p.hsub = p.group / pl.gh;
+  p.rows_wg = pl.rows_wg;
+  p.qtiles = pl.qtiles;
+  p.ncols = pl.ncols;
+  p.xcd_cols = pl.xcd_cols;
+  p.off = Sk - Sq;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  p.chunk = 0;
+  p.q_split = Sq;
+  p.sq_split = 0;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
+  return p;
+}
+
+hipError_t launch_attn(int dtype, int d, int causal, const Plan& pl, long long nwg,
+                       const Params& p, hipStream_t st) {
+  return dtype == ATTN_DTYPE_BF16 ? launch_d<ATTN_DTYPE_BF16>(d, causal != 0, pl, nwg, p, st)
+                                  : launch_d<ATTN_DTYPE_F16>(d, causal != 0, pl, nwg, p, st);
 }
 
 }  // namespace
@@ -751,30 +1039,121 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
   attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
   if (st != ATTN_OK) return st;
   const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
-  Params p{};
-  p.q = (const uint16_t*)q;
-  p.k = (const uint16_t*)k;
-  p.v = (const uint16_t*)v;
-  p.o = (uint16_t*)o;
-  p.lse = lse;
-  p.B = B;
-  p.Sq = Sq;
-  p.Sk = Sk;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.group = Hq / Hkv;
-  p.gh = pl.gh;
-  p.hsub = p.group / pl.gh;
-  p.rows_wg = pl.rows_wg;
-  p.qtiles = pl.qtiles;
-  p.ncols = pl.ncols;
-  p.xcd_cols = pl.xcd_cols;
-  p.off = Sk - Sq;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  const Params p = fill_params(pl, q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, scale);
+  hipError_t e = launch_attn(dtype, d, causal, pl, pl.grid, p, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
+                                int dtype, int kv_split, int* out, int n) {
+  if (kv_split < 0) return ATTN_ERR_INVALID_ARG;
+  int base[9];
+  attn_status st = attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype, base, 9);
+  if (st != ATTN_OK) return st;
+  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split);
+  if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
+  const int vals[5] = {(int)sp.grid, sp.npieces, sp.chunk * BC, sp.q_first,
+                       (int)sp.merge_grid};
+  for (int i = 0; i < n && i < 5; ++i) out[i] = vals[i];
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_split_workspace(int B, int Sq, int Sk, int Hq, int Hkv, int d,
+                                     int causal, int dtype, int kv_split, size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  int out[5];
+  attn_status st = attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype, kv_split, out, 5);
+  if (st != ATTN_OK) return st;
+  *bytes = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split).ws_bytes;
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Sq, int Sk, int Hq, int Hkv, int d, float scale,
+                           int causal, int dtype, int kv_split, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
+  if (st != ATTN_OK) return st;
+  if (kv_split < 0) return ATTN_ERR_INVALID_ARG;
+  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split);
+  if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
+  if (sp.chunk > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
+                       workspace_bytes < sp.ws_bytes))
+    return ATTN_ERR_INVALID_ARG;
+  Params p = fill_params(sp.base, q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, scale);
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = dtype == ATTN_DTYPE_BF16
-                     ? launch_d<ATTN_DTYPE_BF16>(d, causal != 0, pl, p, hs)
-                     : launch_d<ATTN_DTYPE_F16>(d, causal != 0, pl, p, hs);
+  if (sp.chunk == 0) {
+    hipError_t e = launch_attn(dtype, d, causal, sp.base, sp.grid, p, hs);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  }
+  p.chunk = sp.chunk;
+  p.q_split = sp.q_first;
+  p.sq_split = Sq - sp.q_first;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + sp.lse_offset);
+  hipError_t e = launch_attn(dtype, d, causal, sp.base, sp.grid, p, hs);
+  if (e != hipSuccess) return ATTN_ERR_LAUNCH;
+  MergeParams mp{};
+  mp.parts = p.part_o;
+  mp.parts_lse = p.part_lse;
+  mp.o = (uint16_t*)o;
+  mp.lse = lse;
+  mp.B = B;
+  mp.Sq = Sq;
+  mp.Hq = Hq;
+  mp.n_parts = 0;
+  mp.q_first = sp.q_first;
+  mp.sq_rows = Sq - sp.q_first;
+  mp.rows = sp.merge_rows;
+  mp.rows_wg = sp.base.rows_wg;
+  mp.chunk = sp.chunk;
+  mp.Sk = Sk;
+  mp.off = Sk - Sq;
+  mp.causal = causal;
+  e = launch_merge_any(ATTN_DTYPE_F32, dtype, d, sp.merge_grid, mp, hs);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status attn_merge_check(const void* o_parts, const float* lse_parts, int n_parts,
+                             int parts_dtype, int B, int Sq, int Hq, int d, void* o,
+                             float* lse, int dtype) {
+  if (!o_parts || !lse_parts || !o) return ATTN_ERR_INVALID_ARG;
+  if (n_parts < 1 || B < 1 || Sq < 1 || Hq < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (parts_dtype != ATTN_DTYPE_F32 && parts_dtype != ATTN_DTYPE_F16 &&
+      parts_dtype != ATTN_DTYPE_BF16)
+    return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const uintptr_t need = parts_dtype == ATTN_DTYPE_F32 ? 15u : 7u;
+  if (((uintptr_t)o_parts & need) || ((uintptr_t)o & 7u) || ((uintptr_t)lse_parts & 3u) ||
+      ((uintptr_t)lse & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  const long long rows = (long long)B * Sq * Hq;
+  if (rows >= (1ll << 31) || rows * n_parts >= (1ll << 40)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+attn_status attn_merge(const void* o_parts, const float* lse_parts, int n_parts,
+                       int parts_dtype, int B, int Sq, int Hq, int d, void* o, float* lse,
+                       int dtype, void* stream) {
+  attn_status st = attn_merge_check(o_parts, lse_parts, n_parts, parts_dtype, B, Sq, Hq, d, o,
+                                    lse, dtype);
+  if (st != ATTN_OK) return st;
+  MergeParams mp{};
+  mp.parts = o_parts;
+  mp.parts_lse = lse_parts;
+  mp.o = (uint16_t*)o;
+  mp.lse = lse;
+  mp.B = B;
+  mp.Sq = Sq;
+  mp.Hq = Hq;
+  mp.n_parts = n_parts;
+  mp.q_first = 0;
+  mp.sq_rows = Sq;
+  mp.rows = (long long)B * Sq * Hq;
+  const int rpb = 256 / (d / 4);
+  const long long grid = (mp.rows + rpb - 1) / rpb;
+  hipError_t e = launch_merge_any(parts_dtype, dtype, d, grid, mp, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

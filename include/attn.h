@@ -2,7 +2,7 @@
  * attn.h -- C ABI of the fused exact-attention forward for AMD Instinct
  * MI355X (gfx950).
  *
- * The library computes, in one kernel launch,
+ * The library computes (attn_fwd: in one kernel launch)
  *
  *     O   = softmax(scale * Q K^T + M) V
  *     LSE = log of the softmax denominator (natural log, scaled scores)
@@ -28,10 +28,11 @@
  *             P V product, as on every page; O is rounded to nearest even.
  *
  * Ownership and synchronisation
- *   The caller owns every buffer.  The library allocates nothing, keeps no
- *   state between calls and never synchronises: the work is queued on
- *   `stream` and the call returns.  It does not read o or lse; on success
- *   every element of o (and of lse if given) is written.
+ *   The caller owns every buffer (attn_fwd_split's workspace included).  The
+ *   library allocates nothing, keeps no state between calls and never
+ *   synchronises: the work is queued on `stream` and the call returns.  It
+ *   does not read o or lse; on success every element of o (and of lse if
+ *   given) is written.
  *
  * Errors
  *   A nonzero status means nothing was launched and nothing was written,
@@ -40,6 +41,8 @@
  */
 #ifndef EXACT_ATTENTION_19_AMD_ATTN_H
 #define EXACT_ATTENTION_19_AMD_ATTN_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -54,9 +57,10 @@ typedef enum {
   ATTN_ERR_LAUNCH = 3       /* HIP reported an error for the launch */
 } attn_status;
 
-typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+/* F32 is accepted only for the partial outputs passed to attn_merge. */
+typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1, ATTN_DTYPE_F32 = 2 } attn_dtype;
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /*
  * attn_fwd -- fused attention forward.
@@ -106,6 +110,103 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
  */
 attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
                           int causal, int dtype, int* out, int n);
+
+/*
+ * attn_fwd_split -- attn_fwd for problems whose query blocks are too few to
+ * fill the GPU (short sequences, few heads): the keys of each long query
+ * block are cut into ranges ("pieces") that separate workgroups process, and
+ * the pieces are merged.
+ *
+ * Each piece produces, per query row, the state of the online softmax over
+ * its keys alone ("FlashAttention personal implementation notes", section
+ * "Online Softmax": running max, denominator and unnormalised output), kept
+ * as an fp32 output normalised over those keys plus their log-sum-exp.  A
+ * second kernel combines the pieces of a row with that section's rescale
+ * (factor e^(m_i - m_new) on each state), as attn_merge does.  The result is
+ * the same attention as attn_fwd's, to within rounding.
+ *
+ *   q ... dtype  as for attn_fwd (same validation, same status codes)
+ *   kv_split     0 = the library's choice (split only when the query blocks
+ *                leave workgroup slots of a 256-CU device idle);
+ *                1 = never split (exactly attn_fwd);
+ *                k > 1 = cut the longest query block into at most k pieces
+ *                (pieces hold a whole, even number of 64-key tiles)
+ *   workspace    device pointer, 256-byte aligned, of at least the size
+ *                attn_fwd_split_workspace reports for the same arguments; may
+ *                be NULL when that size is 0 (no split).  Owned by the
+ *                caller; its contents on entry do not matter and on return
+ *                are scratch.  Two calls in flight must not share one.
+ *   workspace_bytes  its size in bytes
+ *   stream       as for attn_fwd; up to two kernels are queued on it
+ *
+ * Returns ATTN_ERR_INVALID_ARG for kv_split < 0 or a missing, misaligned or
+ * too small workspace, else as attn_fwd.
+ */
+attn_status attn_fwd_split(const void* q, const void* k, const void* v, void* o,
+                           float* lse, int B, int Sq, int Sk, int Hq, int Hkv,
+                           int d, float scale, int causal, int dtype,
+                           int kv_split, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_split_workspace -- bytes of workspace attn_fwd_split needs for
+ * these arguments (0 when it would not split), without any device call.
+ * Returns the status attn_fwd_split's validation of the sizes would return.
+ */
+attn_status attn_fwd_split_workspace(int B, int Sq, int Sk, int Hq, int Hkv,
+                                     int d, int causal, int dtype,
+                                     int kv_split, size_t* bytes);
+
+/*
+ * attn_fwd_split_plan -- the launches attn_fwd_split would make, without any
+ * device call.  Writes up to n (at most 5) ints into `out`:
+ *   [0] attention workgroups     [1] pieces of the longest query block
+ *   [2] keys per piece (0 = no split)
+ *   [3] first query row of a split block (Sq when nothing is split)
+ *   [4] merge workgroups (0 when nothing is split)
+ */
+attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
+                                int causal, int dtype, int kv_split, int* out,
+                                int n);
+
+/*
+ * attn_merge -- combine partial attention states over disjoint key subsets
+ * into the state of their union (e.g. the key shards of one sequence computed
+ * by separate attention calls or on separate devices):
+ *
+ *     M = max_p lse_p,  w_p = e^(lse_p - M),
+ *     O = sum_p w_p O_p / sum_p w_p,   LSE = M + ln sum_p w_p
+ *
+ * the online-softmax update of the personal-notes page (section "Online
+ * Softmax") applied to whole parts.  A part with lse = -inf saw no key and
+ * has weight 0; a row that no part saw gets O = 0 and LSE = -inf.
+ *
+ *   o_parts     device pointer, n_parts blocks of (B, Sq, Hq, d) elements of
+ *               parts_dtype (ATTN_DTYPE_F32, F16 or BF16), part p at element
+ *               offset p * B * Sq * Hq * d; each normalised over its own
+ *               keys (as attn_fwd's O is); 16-byte aligned for F32, 8-byte
+ *               aligned otherwise
+ *   lse_parts   device pointer, n_parts blocks of (B, Hq, Sq) floats: the
+ *               natural-log LSE of each part, as attn_fwd returns it; 4-byte
+ *               aligned
+ *   n_parts     >= 1
+ *   B, Sq, Hq, d  sizes (d = 64 or 128)
+ *   o           device pointer, (B, Sq, Hq, d) of dtype (F16 or BF16),
+ *               8-byte aligned; written (must not overlap the inputs)
+ *   lse         B * Hq * Sq floats, or NULL to skip
+ *   stream      as for attn_fwd
+ *
+ * Size limit: B * Sq * Hq < 2^31.  attn_merge_check reports the status
+ * without a device call.
+ */
+attn_status attn_merge(const void* o_parts, const float* lse_parts,
+                       int n_parts, int parts_dtype, int B, int Sq, int Hq,
+                       int d, void* o, float* lse, int dtype, void* stream);
+
+/* attn_merge's validation without any device call (safe without a GPU). */
+attn_status attn_merge_check(const void* o_parts, const float* lse_parts,
+                             int n_parts, int parts_dtype, int B, int Sq,
+                             int Hq, int d, void* o, float* lse, int dtype);
 
 /* Human-readable name of a status code (static string). */
 const char* attn_status_str(int status);

@@ -133,3 +133,113 @@ def test_plan_rejects_bad_sizes():
     _lib()
     with pytest.raises(binding.AttnError):
         binding.attn_fwd_plan(1, 0, 8, 4, 4, 64, 0, ATTN_DTYPE_F16)
+
+
+# ------------------------------------------------------------- key split
+
+def _tiles(q0, rows, Sq, Sk, causal):
+    """K/V tiles (64 keys) visited by query rows [q0, q0 + rows)."""
+    last = min(q0 + rows, Sq) - 1
+    end = min(Sk, last + Sk - Sq + 1) if causal else Sk
+    return -(-end // 64) if end > 0 else 0
+
+
+@pytest.mark.parametrize("cfg", [
+    (2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16),
+    (1, 1280, 1536, 16, 16, 128, 1, ATTN_DTYPE_F16),
+    (1, 1237, 1531, 16, 16, 128, 1, ATTN_DTYPE_F16),
+    (2, 700, 200, 8, 2, 128, 1, ATTN_DTYPE_BF16),
+    (1, 300, 2000, 4, 1, 64, 0, ATTN_DTYPE_BF16),
+])
+@pytest.mark.parametrize("kv_split", [0, 2, 3, 7, 1000])
+def test_split_plan_follows_the_piece_rule(cfg, kv_split):
+    """The split plan against a re-derivation of its rule: pieces of an even
+    number of tiles, a block split only when longer than one piece, the
+    first split row the start of the first split block, and the workspace
+    holding one fp32 row state per piece and split row."""
+    _lib()
+    B, Sq, Sk, Hq, Hkv, d, causal, dt = cfg
+    base = binding.attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, causal, dt)
+    sp = binding.attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, dt, kv_split)
+    ws = binding.attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, causal, dt, kv_split)
+    rows = base["rows_per_wg"]
+    qtiles = -(-Sq // rows)
+    ncols = base["grid"] // qtiles
+    tiles = [_tiles(t * rows, rows, Sq, Sk, causal) for t in range(qtiles)]
+    if sp["keys_per_piece"] == 0:
+        assert sp["pieces"] == 1 and sp["grid"] == base["grid"] and ws == 0
+        assert sp["first_split_row"] == Sq and sp["merge_grid"] == 0
+        if kv_split > 1:  # a requested split is dropped only when it cannot cut
+            assert -(-max(tiles) // kv_split) + (-(-max(tiles) // kv_split)) % 2 >= max(tiles)
+        return
+    chunk = sp["keys_per_piece"] // 64
+    assert chunk % 2 == 0 and chunk < max(tiles)
+    if kv_split > 1:
+        c = -(-max(tiles) // kv_split)
+        assert chunk == max(2, c + c % 2)
+    pieces = [-(-t // chunk) if t > chunk else 1 for t in tiles]
+    assert sp["pieces"] == max(pieces)
+    assert sp["grid"] == max(pieces) * qtiles * ncols
+    first = next(t for t in range(qtiles) if pieces[t] > 1) * rows
+    assert sp["first_split_row"] == first
+    assert all(p > 1 for p in pieces[first // rows:])
+    merge_rows = B * (Sq - first) * Hq
+    assert sp["merge_grid"] == -(-merge_rows // (256 // (d // 4)))
+    part_bytes = max(pieces) * merge_rows * d * 4
+    assert ws == -(-part_bytes // 256) * 256 + max(pieces) * merge_rows * 4
+
+
+def test_split_automatic_choice():
+    _lib()
+    # grids that fill the chip are not split
+    sp = binding.attn_fwd_split_plan(1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16, 0)
+    assert sp["keys_per_piece"] == 0
+    # the short workloads are, in pieces of at least 4 tiles
+    for cfg in ((2, 1024, 1024, 16, 16, 128, 1), (1, 1280, 1536, 16, 16, 128, 1)):
+        sp = binding.attn_fwd_split_plan(*cfg, ATTN_DTYPE_F16, 0)
+        assert sp["pieces"] > 1 and sp["keys_per_piece"] >= 256
+    assert binding.attn_fwd_split_plan(1, 128, 128, 2, 2, 64, 0, ATTN_DTYPE_F16, 1)["pieces"] == 1
+
+
+def test_split_rejects_before_any_device_call():
+    lib = _lib()
+    f = ctypes.c_float(0.1)
+    args = (A, A, A, A, None, 2, 1024, 1024, 16, 16, 128, f, 1, ATTN_DTYPE_F16)
+    need = binding.attn_fwd_split_workspace(2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16, 4)
+    assert need > 0
+    W = 0x100000
+    assert lib.attn_fwd_split(*args, -1, W, need, None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_split(*args, 4, None, need, None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_split(*args, 4, W + 16, need, None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_split(*args, 4, W, need - 1, None) == ATTN_ERR_INVALID_ARG
+    bad = (A, A, A, A, None, 2, 1024, 1024, 16, 6, 128, f, 1, ATTN_DTYPE_F16)
+    assert lib.attn_fwd_split(*bad, 4, W, need, None) == ATTN_ERR_INVALID_ARG
+    with pytest.raises(binding.AttnError):
+        binding.attn_fwd_split_plan(2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16, -2)
+    st = lib.attn_fwd_split_workspace(2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16, 0, None)
+    assert st == ATTN_ERR_INVALID_ARG
+
+
+MGOOD = dict(o_parts=A, lse_parts=A + 0x1000, n_parts=3, parts_dtype=binding.ATTN_DTYPE_F32,
+             B=2, Sq=100, Hq=8, d=128, o=A + 0x2000, lse=A + 0x3000, dtype=ATTN_DTYPE_BF16)
+
+
+def _mcheck(**over):
+    a = dict(MGOOD, **over)
+    return binding.attn_merge_check(a["o_parts"], a["lse_parts"], a["n_parts"],
+                                    a["parts_dtype"], a["B"], a["Sq"], a["Hq"], a["d"],
+                                    a["o"], a["lse"], a["dtype"])
+
+
+def test_merge_validation():
+    _lib()
+    assert _mcheck() == ATTN_OK
+    assert _mcheck(lse=None, d=64, parts_dtype=ATTN_DTYPE_F16, o_parts=A + 8) == ATTN_OK
+    for over in (dict(o_parts=None), dict(lse_parts=None), dict(o=None), dict(n_parts=0),
+                 dict(B=0), dict(Sq=0), dict(Hq=0), dict(o_parts=A + 8), dict(o=A + 4),
+                 dict(lse=A + 2), dict(lse_parts=A + 2), dict(B=1 << 20, Sq=1 << 12)):
+        assert _mcheck(**over) == ATTN_ERR_INVALID_ARG, over
+    for over in (dict(d=96), dict(parts_dtype=7), dict(dtype=binding.ATTN_DTYPE_F32)):
+        assert _mcheck(**over) == ATTN_ERR_UNSUPPORTED, over
+    lib = _lib()
+    assert lib.attn_merge(A, A, 0, 2, 1, 8, 2, 64, A, None, 0, None) == ATTN_ERR_INVALID_ARG
