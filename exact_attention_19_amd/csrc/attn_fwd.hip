@@ -862,13 +862,13 @@ Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
   return pl;
 }
 
-// Key split.  Workgroup slots of the chip: 256 CUs x 2 resident workgroups of
-// the attention kernel.  When the row blocks alone leave slots idle, the
-// automatic choice cuts every block into pieces of about (total tiles /
-// slots) tiles, but never below kMinChunk tiles: a piece pays its own Q load,
-// pipeline fill and fp32 partial write, and the merge reads every partial.
-constexpr int kSlots = 512;
-constexpr int kMinChunk = 4;
+// Key split.  One workgroup of the attention kernel already draws most of a
+// CU's matrix throughput (a second one on the same CU mostly shares it), so
+// the automatic choice splits only when the query blocks leave CUs idle
+// (fewer blocks than kCUs), and then takes the smallest even piece length
+// whose pieces still number at most kCUs: the longest piece sets the time,
+// and every piece beyond one per CU would share a CU with another.
+constexpr int kCUs = 256;
 
 struct SplitPlan {
   Plan base;
@@ -896,14 +896,22 @@ SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int cau
   const int nmax = block_tiles((pl.qtiles - 1) * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0);
   int chunk;
   if (kv_split == 0) {
-    if ((long long)pl.qtiles * pl.ncols >= kSlots) return sp;
-    long long total = 0;
-    for (int qt = 0; qt < pl.qtiles; ++qt)
-      total += block_tiles(qt * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0);
-    total *= pl.ncols;
-    long long c = (total + kSlots - 1) / kSlots;
-    if (c < kMinChunk) c = kMinChunk;
-    chunk = (int)(c > nmax ? nmax : c);
+    if ((long long)pl.qtiles * pl.ncols >= kCUs) return sp;
+    // the piece count falls as the piece length grows: bisect over even
+    // lengths c = 2h for the smallest one with at most kCUs pieces
+    auto fits = [&](int c) {
+      long long pieces = 0;
+      for (int qt = 0; qt < pl.qtiles; ++qt)
+        pieces += block_pieces(block_tiles(qt * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0), c);
+      return pieces * pl.ncols <= kCUs;
+    };
+    int lo = 1, hi = (nmax + 1) / 2;  // fits(2 * hi) holds: one piece per block
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (fits(2 * mid)) hi = mid;
+      else lo = mid + 1;
+    }
+    chunk = 2 * lo;
   } else {
     chunk = (nmax + kv_split - 1) / kv_split;
   }

@@ -126,8 +126,9 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
  * the same attention as attn_fwd's, to within rounding.
  *
  *   q ... dtype  as for attn_fwd (same validation, same status codes)
- *   kv_split     0 = the library's choice (split only when the query blocks
- *                leave workgroup slots of a 256-CU device idle);
+ *   kv_split     0 = the library's choice: split only when there are fewer
+ *                query blocks than the 256 CUs of the device, into the
+ *                shortest pieces that still number at most 256;
  *                1 = never split (exactly attn_fwd);
  *                k > 1 = cut the longest query block into at most k pieces
  *                (pieces hold a whole, even number of 64-key tiles)

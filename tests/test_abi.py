@@ -190,15 +190,33 @@ def test_split_plan_follows_the_piece_rule(cfg, kv_split):
 
 
 def test_split_automatic_choice():
+    """kv_split = 0: no split when the query blocks number at least the 256
+    CUs; otherwise the shortest even piece length (in 64-key tiles) whose
+    pieces number at most 256."""
     _lib()
-    # grids that fill the chip are not split
-    sp = binding.attn_fwd_split_plan(1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16, 0)
-    assert sp["keys_per_piece"] == 0
-    # the short workloads are, in pieces of at least 4 tiles
-    for cfg in ((2, 1024, 1024, 16, 16, 128, 1), (1, 1280, 1536, 16, 16, 128, 1)):
-        sp = binding.attn_fwd_split_plan(*cfg, ATTN_DTYPE_F16, 0)
-        assert sp["pieces"] > 1 and sp["keys_per_piece"] >= 256
-    assert binding.attn_fwd_split_plan(1, 128, 128, 2, 2, 64, 0, ATTN_DTYPE_F16, 1)["pieces"] == 1
+    for cfg in ((1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16),
+                (2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16),
+                (1, 1280, 1536, 16, 16, 128, 1, ATTN_DTYPE_F16),
+                (1, 1237, 1531, 16, 16, 128, 1, ATTN_DTYPE_F16),
+                (1, 64, 4096, 1, 1, 128, 0, ATTN_DTYPE_F16),
+                (16, 1, 8192, 32, 8, 128, 0, ATTN_DTYPE_BF16),
+                (1, 300, 300, 4, 2, 64, 1, ATTN_DTYPE_F16),
+                (1, 128, 128, 2, 2, 64, 0, ATTN_DTYPE_F16)):
+        B, Sq, Sk, Hq, Hkv, d, causal, dt = cfg
+        base = binding.attn_fwd_plan(*cfg)
+        sp = binding.attn_fwd_split_plan(*cfg, 0)
+        rows = base["rows_per_wg"]
+        qtiles = -(-Sq // rows)
+        ncols = base["grid"] // qtiles
+        tiles = [_tiles(t * rows, rows, Sq, Sk, causal) for t in range(qtiles)]
+        want = 0
+        if qtiles * ncols < 256:
+            for c in range(2, max(tiles), 2):
+                n = sum(-(-t // c) if t > c else 1 for t in tiles) * ncols
+                if n <= 256:
+                    want = c
+                    break
+        assert sp["keys_per_piece"] == 64 * want, cfg
 
 
 def test_split_rejects_before_any_device_call():
