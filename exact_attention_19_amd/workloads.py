@@ -18,8 +18,11 @@ nearest even).  Distributions:
 The shapes follow the pages' workloads: a tiny MHA case, the p1/p3-style
 1K-2K causal MHA shapes (the CuTe DSL Ampere example's Sq=1280, Sk=1536,
 H=16, d=128, scale 1.0 case), and Qwen3-like GQA prefill layouts at 8K and
-16K (the MiniPaged-Qwen page's GQA head grouping).  Layout is
-(batch, seq, heads, d_head).
+16K (the MiniPaged-Qwen page's GQA head grouping), and decode: one (or a
+few) new query tokens per sequence over a long cached K/V, the phase the
+MiniPaged-Qwen page (section 19) sets apart from prefill because the query
+side then has almost no parallelism and the work becomes reading the K/V
+cache.  Layout is (batch, seq, heads, d_head).
 """
 from __future__ import annotations
 
@@ -102,6 +105,15 @@ WORKLOADS = {
         Workload("gqa8_causal_outlier_bf16_b1_hq32_hkv4_s16384_d128", 1, 32, 4,
                  16384, 16384, 128, "bf16", True, 1.0 / math.sqrt(128),
                  "outlier"),
+        # decode: the 8K GQA heads, one new token for each of 32 sequences
+        Workload("decode_gqa4_bf16_b32_hq32_hkv8_sq1_sk8192_d128", 32, 32, 8, 1,
+                 8192, 128, "bf16", True, 1.0 / math.sqrt(128)),
+        # decode of one long sequence: only the key split fills the GPU
+        Workload("decode_gqa4_bf16_b1_hq32_hkv8_sq1_sk32768_d128", 1, 32, 8, 1,
+                 32768, 128, "bf16", True, 1.0 / math.sqrt(128)),
+        # four new tokens per sequence (bottom-right causal among themselves)
+        Workload("decode_gqa4_bf16_b32_hq32_hkv8_sq4_sk8192_d128", 32, 32, 8, 4,
+                 8192, 128, "bf16", True, 1.0 / math.sqrt(128)),
     ]
 }
 
@@ -109,6 +121,8 @@ WORKLOADS = {
 HEADLINE = "gqa4_causal_bf16_b1_hq32_hkv8_s8192_d128"
 # The largest single-GPU workload.
 LARGEST = "gqa8_causal_outlier_bf16_b1_hq32_hkv4_s16384_d128"
+# Decode workloads (bound by reading K and V from HBM).
+DECODE = [n for n in WORKLOADS if n.startswith("decode_")]
 
 
 def make_inputs(w: Workload, seed: int = 0, device="cpu"):

@@ -267,3 +267,19 @@ def test_key_shards_merged_equal_full_attention(dt):
     bound = TOL_O[dt] + half_ulp(o_ref, dt)
     assert np.all(diff <= bound), f"max|dO| = {diff.max()}"
     assert np.abs(lse.double().cpu().numpy() - lse_ref).max() <= TOL_LSE
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("kv_split", [0, 1, 8])
+@pytest.mark.parametrize("name", ["decode_gqa4_bf16_b32_hq32_hkv8_sq1_sk8192_d128",
+                                  "decode_gqa4_bf16_b1_hq32_hkv8_sq1_sk32768_d128",
+                                  "decode_gqa4_bf16_b32_hq32_hkv8_sq4_sk8192_d128"])
+def test_decode_workloads_full_parity(name, kv_split):
+    """Decode (one or four new tokens per sequence over a long K/V cache) at
+    full size, every output row against the oracle, whole and split."""
+    w = WORKLOADS[name]
+    q, k, v, ref = _oracle_of(name)
+    o, lse, plan = _run_split(q, k, v, w, kv_split)
+    err = _check_full(w, q, k, v, o, lse, ref=ref)
+    _say(f"{name} split {kv_split} ({plan['pieces']} pieces): max|dO| = {err:.3e}")
