@@ -134,17 +134,23 @@ def gemm_probe(steps: int):
     for _ in range(20):
         torch.matmul(a, b, out=c)
     torch.cuda.synchronize()
+    # the board's power and clocks, sampled while the GEMMs run
+    import threading
+    board = {}
+    sampler = threading.Thread(target=lambda: board.update(board_power() or {}))
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(steps):
         torch.matmul(a, b, out=c)
     e.record()
+    sampler.start()
     torch.cuda.synchronize()
+    sampler.join()
     ms = s.elapsed_time(e) / steps
     print(json.dumps({"gemm_probe": f"bf16 {n}x{n}x{n}", "ms": round(ms, 4),
-                      "tflops": round(2 * n ** 3 / ms / 1e9, 1), "board": board_power()}),
-          flush=True)
+                      "tflops": round(2 * n ** 3 / ms / 1e9, 1),
+                      "board_during_gemms": board}), flush=True)
 
 
 def copy_probe(mib: int, steps: int):
@@ -286,8 +292,7 @@ def main():
         }),
         "launch": plan,
         "split": dict(split, kv_split_arg=args.kv_split, workspace_bytes=ws_bytes),
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "board_after_timed_steps": board_power()},
+        "device": {"name": props.name, "cus": props.multi_processor_count},
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:

@@ -2,11 +2,13 @@
 
 ``attn_fwd`` runs the HIP kernel of ``libattn.so`` through its C ABI
 (``include/attn.h``); ``attn_fwd_split`` splits the keys of long query blocks
-over workgroups and merges them (small grids); ``attn_merge`` combines
+over workgroups and merges them (small grids); ``attn_fwd_strided`` takes
+strided views (e.g. the (B, H, S, d) layout); ``attn_merge`` combines
 partial states over disjoint key subsets.  The library is loaded on first use; if it has not been
 built, that call raises ImportError (there is no fallback path).
 """
 from .binding import (  # noqa: F401
     AttnError, attn_abi_version, attn_fwd, attn_fwd_check, attn_fwd_plan,
-    attn_fwd_split, attn_fwd_split_plan, attn_fwd_split_workspace, attn_merge,
+    attn_fwd_split, attn_fwd_split_plan, attn_fwd_split_workspace, attn_fwd_strided,
+    attn_fwd_strided_check, attn_merge,
     attn_merge_check, attn_status_str, load_library)

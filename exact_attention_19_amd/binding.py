@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(PKG, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
 ATTN_DTYPE_F16, ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1, 2
 EXPORTED = ("attn_fwd", "attn_fwd_check", "attn_fwd_plan", "attn_fwd_split",
-            "attn_fwd_split_workspace", "attn_fwd_split_plan", "attn_merge",
-            "attn_merge_check", "attn_status_str", "attn_abi_version")
+            "attn_fwd_split_workspace", "attn_fwd_split_plan", "attn_fwd_strided",
+            "attn_fwd_strided_check", "attn_merge", "attn_merge_check",
+            "attn_status_str", "attn_abi_version")
 
 _lib = None
 
@@ -53,6 +54,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_split_workspace.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.attn_fwd_split_plan.restype = i
     lib.attn_fwd_split_plan.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(i), i]
+    ll12 = ctypes.POINTER(ctypes.c_longlong)
+    lib.attn_fwd_strided.restype = i
+    lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, ll12, i,
+                                     vp, sz, vp]
+    lib.attn_fwd_strided_check.restype = i
+    lib.attn_fwd_strided_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, ll12]
     lib.attn_merge.restype = i
     lib.attn_merge.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i, vp]
     lib.attn_merge_check.restype = i
@@ -218,6 +225,80 @@ def attn_fwd_split(q, k, v, scale: float | None = None, causal: bool = False,
         ws_ptr, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_split")
+    return out, lse
+
+
+def _strides_arg(vals):
+    arr = (ctypes.c_longlong * 12)(*[int(x) for x in vals])
+    return arr
+
+
+def attn_fwd_strided_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Sq, Sk, Hq, Hkv, d,
+                           scale, causal, dtype_code, strides) -> int:
+    """attn_fwd_strided's validation on raw addresses and 12 element strides."""
+    return int(load_library().attn_fwd_strided_check(
+        q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Sq, Sk, Hq, Hkv, d, float(scale),
+        int(causal), dtype_code, _strides_arg(strides)))
+
+
+def attn_fwd_strided(q, k, v, scale: float | None = None, causal: bool = False,
+                     layout: str = "bshd", kv_split: int = 0, out=None, lse=None,
+                     return_lse: bool = True, workspace=None, stream=None):
+    """attn_fwd on strided views: q, k, v (and ``out``) may be any views whose
+    last dimension is contiguous, e.g. slices of a packed QKV projection.
+
+    layout "bshd": q is (B, Sq, Hq, d) and k, v are (B, Sk, Hkv, d);
+    layout "bhsd": q is (B, Hq, Sq, d) and k, v are (B, Hkv, Sk, d).
+    ``out`` (allocated here, dense, when None) has the layout of q.  lse is
+    (B, Hq, Sq) fp32.  kv_split and workspace as for attn_fwd_split."""
+    import torch
+    if layout not in ("bshd", "bhsd"):
+        raise ValueError("layout must be 'bshd' or 'bhsd'")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D")
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    # logical (b, s, h, c) views
+    view = (lambda t: t) if layout == "bshd" else (lambda t: t.transpose(1, 2))
+    qv, kv_, vv, ov = view(q), view(k), view(v), view(out)
+    B, Sq, Hq, d = qv.shape
+    Bk, Sk, Hkv, dk = kv_.shape
+    if tuple(vv.shape) != (Bk, Sk, Hkv, dk) or Bk != B or dk != d or tuple(ov.shape) != (B, Sq, Hq, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}, out {tuple(out.shape)} ({layout})")
+    code = _dtype_code(q)
+    for name, t in (("q", qv), ("k", kv_), ("v", vv), ("out", ov)):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v and out must share one dtype")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq, Sq)):
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+    strides = []
+    for t in (qv, kv_, vv, ov):
+        strides += [t.stride(0), t.stride(1), t.stride(2)]
+    if workspace is None:
+        need = attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, causal, code, kv_split)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().attn_fwd_strided(
+        qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), ov.data_ptr(),
+        lse.data_ptr() if lse is not None else None,
+        B, Sq, Sk, Hq, Hkv, d, float(scale), int(bool(causal)), code, _strides_arg(strides),
+        int(kv_split), ws_ptr, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_strided")
     return out, lse
 
 

@@ -154,6 +154,12 @@ struct Params {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
+  // element strides of (batch, seq, head); d is contiguous.  Every row
+  // starts 16-byte aligned (host-checked).
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
   int B, Sq, Sk, Hq, Hkv;
   int group;     // Hq / Hkv
   int gh;        // query heads per workgroup (divides group and the wave count)
@@ -189,20 +195,6 @@ __host__ __device__ inline int block_tiles(int q0, int rows, int Sq, int Sk, int
 // piece (a block that fits one piece is not split).
 __host__ __device__ inline int block_pieces(int tiles, int chunk) {
   return (chunk > 0 && tiles > chunk) ? (tiles + chunk - 1) / chunk : 1;
-}
-
-// 16-byte-chunk XOR swizzle of a K/V tile row in LDS.  Row r of the tile
-// stores its logical chunk s at physical chunk s ^ swz(r).  For d = 128 (16
-// chunks per 256-byte row) swz permutes the 16 rows of a K fragment onto 16
-// distinct bank groups, and puts the 4 consecutive rows of a V transpose read
-// on 4 disjoint bank-group quads; the d = 64 form does the same with 8 chunks
-// per row (two rows per 256-byte bank cycle).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128)
-    return ((r & 3) << 2) | ((r >> 2) & 3);
-  else
-    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Position of accumulator row m (of a 32x32 MFMA block) in the key order.
@@ -255,7 +247,7 @@ struct PFrag {
 };
 
 template <int DT, int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_kernel(Params p) {
   using T = Ty<DT>;
   constexpr int NT = NW * 64;
   constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -325,11 +317,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   }
   n_full = min(n_full, n_end);
 
-  // K and V rows of this (batch, kv head): byte slices with a row stride of
-  // Hkv * D * 2 bytes
-  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
-  const char* kslice = (const char*)(p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
-  const char* vslice = (const char*)(p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
+  // K and V rows of this (batch, kv head): byte slices whose rows (keys) are
+  // k_ss * 2 and v_ss * 2 bytes apart
+  const uint32_t rbk = (uint32_t)(p.k_ss * 2);
+  const uint32_t rbv = (uint32_t)(p.v_ss * 2);
+  const char* kslice = (const char*)(p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh);
+  const char* vslice = (const char*)(p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh);
 
   // ---- LDS tile layout of this kernel: column-blocked.  A K or V tile is
   // stored as D/32 blocks of 32 columns; block cb holds the 64 rows of those
@@ -386,10 +379,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   // global load to LDS would also do, but the compiler then assumes it may
   // count on the LDS counter and waits for every outstanding LDS read at
   // each dependency.)  Rows past Sk in the ragged last tile re-read row
-  // Sk - 1 (their keys are masked).  Host validation keeps BC * row_bytes
+  // Sk - 1 (their keys are masked).  Host validation keeps BC * (row stride)
   // below 2^31.
-  const uint32_t ld_off = (uint32_t)ld_row * row_bytes + (uint32_t)ld_col * 2;
-  auto issue_rows = [&](const char* slice, int n, LDS_PTR(char) buf) {
+  const uint32_t ld_off_k = (uint32_t)ld_row * rbk + (uint32_t)ld_col * 2;
+  const uint32_t ld_off_v = (uint32_t)ld_row * rbv + (uint32_t)ld_col * 2;
+  auto issue_rows = [&](const char* slice, uint32_t row_bytes, uint32_t ld_off, int n,
+                        LDS_PTR(char) buf) {
     const char* tile = slice + (int64_t)n * BC * row_bytes;
     uint32_t off = ld_off;
     if ((n + 1) * BC > p.Sk)
@@ -408,7 +403,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   {
     const int qi = q0w + l32;
     const bool ok = qi < p.Sq;
-    const uint16_t* qrow = p.q + (((int64_t)b * p.Sq + (ok ? qi : 0)) * p.Hq + hq) * D;
+    const uint16_t* qrow =
+        p.q + (int64_t)b * p.q_sb + (int64_t)(ok ? qi : 0) * p.q_ss + (int64_t)hq * p.q_sh;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
@@ -507,8 +503,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
     LDS_PTR(char) const V_PREV = vbuf_of(PAR ^ 1);  // V(j-1)
     LDS_PTR(char) const K_LOAD = kbuf_of(PAR);      // K(j+2)
     LDS_PTR(char) const V_LOAD = vbuf_of(PAR);      // V(j)
-    if (j + 2 < j_hi) issue_rows(kslice, j + 2, K_LOAD);
-    issue_rows(vslice, j, V_LOAD);
+    if (j + 2 < j_hi) issue_rows(kslice, rbk, ld_off_k, j + 2, K_LOAD);
+    issue_rows(vslice, rbv, ld_off_v, j, V_LOAD);
     // mask the straddling tiles, then the row max and the max update
     if (j >= n_full) {
 #pragma unroll
@@ -624,8 +620,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
   if (j_hi > j_lo) {
     // prologue: K(j_lo) and K(j_lo+1) in flight; the V buffer read for the
     // tile before j_lo in the first iteration is cleared so that 0 * V stays 0.
-    issue_rows(kslice, j_lo, kbuf_of(0));
-    if (j_lo + 1 < j_hi) issue_rows(kslice, j_lo + 1, kbuf_of(1));
+    issue_rows(kslice, rbk, ld_off_k, j_lo, kbuf_of(0));
+    if (j_lo + 1 < j_hi) issue_rows(kslice, rbk, ld_off_k, j_lo + 1, kbuf_of(1));
     {
       LDS_PTR(u32x4) z = (LDS_PTR(u32x4))vbuf_of(1);
       for (int i = tid; i < TB / 16; i += NT) z[i] = (u32x4){0u, 0u, 0u, 0u};
@@ -680,7 +676,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
         p.part_lse[(((int64_t)piece * p.B + b) * p.Hq + hq) * p.sq_split + ii] = lse;
       }
     } else if (qi < p.Sq) {
-      uint16_t* orow = p.o + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D;
+      uint16_t* orow = p.o + (int64_t)b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)hq * p.o_sh;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -721,7 +717,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_pipe_kernel(Params p
 struct MergeParams {
   const void* parts;      // part p, row r: parts + (p * rows + r) * D elements
   const float* parts_lse; // part p, (b, h, i): + p * rows + (b * Hq + h) * sq_rows + i - q_first
-  uint16_t* o;            // (B, Sq, Hq, D)
+  uint16_t* o;            // (B, Sq, Hq, D) through the strides below
+  int64_t o_sb, o_ss, o_sh;
   float* lse;             // (B, Hq, Sq) or null
   int B, Sq, Hq;
   int n_parts;  // parts per row; 0 = the piece count of a key split (below)
@@ -762,6 +759,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
   constexpr int TPR = D / 4;        // threads per row
   constexpr int RPB = 256 / TPR;    // rows per workgroup
   constexpr float LOG2E = 1.44269504088896340736f;
+  if ((int)threadIdx.x >= RPB * TPR) return;  // d = 96: 240 of 256 threads
   const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   if (r >= p.rows) return;
   const int c = (threadIdx.x % TPR) * 4;
@@ -801,7 +799,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
   const i16x8 h = Ty<ODT>::cvt(y);
   const u32x2 w2 = {(unsigned)(uint16_t)h[0] | ((unsigned)(uint16_t)h[1] << 16),
                     (unsigned)(uint16_t)h[2] | ((unsigned)(uint16_t)h[3] << 16)};
-  *(u32x2*)(p.o + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D + c) = w2;
+  *(u32x2*)(p.o + (int64_t)b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)hq * p.o_sh + c) = w2;
   if (p.lse != nullptr && c == 0)
     p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] =
         W > 0.f ? M + __builtin_amdgcn_logf(W) * LN2 : -INFINITY;
@@ -828,7 +826,7 @@ attn_status validate(const void* q, const void* k, const void* v, void* o,
     return ATTN_ERR_INVALID_ARG;
   if (((uintptr_t)lse) & 3u) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   // index-space limits: positions and per-tensor row counts stay in int32
   // arithmetic inside the kernel; element offsets are 64-bit.
   if ((int64_t)Sq + Sk >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
@@ -836,6 +834,27 @@ attn_status validate(const void* q, const void* k, const void* v, void* o,
   if ((int64_t)Hkv * d * 2 * 64 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31))
     return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+// Element strides (batch, seq, head) of q, k, v, o, in that order.
+struct Strides {
+  int64_t s[12];
+};
+
+Strides dense_strides(int Sq, int Sk, int Hq, int Hkv, int d) {
+  const int64_t q[3] = {(int64_t)Sq * Hq * d, (int64_t)Hq * d, d};
+  const int64_t k[3] = {(int64_t)Sk * Hkv * d, (int64_t)Hkv * d, d};
+  return Strides{{q[0], q[1], q[2], k[0], k[1], k[2], k[0], k[1], k[2], q[0], q[1], q[2]}};
+}
+
+// Strides: non-negative multiples of 8 elements (16-byte aligned rows), and a
+// K or V tile (64 key rows) within 2^31 bytes of its first row.
+attn_status validate_strides(const int64_t* st) {
+  if (st == nullptr) return ATTN_ERR_INVALID_ARG;
+  for (int i = 0; i < 12; ++i)
+    if (st[i] < 0 || (st[i] & 7) != 0) return ATTN_ERR_INVALID_ARG;
+  if (st[4] * 2 * 64 >= (1ll << 31) || st[7] * 2 * 64 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   return ATTN_OK;
 }
 
@@ -938,12 +957,14 @@ SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int cau
 
 template <int PDT, int ODT>
 hipError_t launch_merge(int d, long long grid, const MergeParams& mp, hipStream_t st) {
-  if (d == 128)
-    hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 128>), dim3((unsigned)grid), dim3(256), 0,
-                       st, mp);
-  else
-    hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 64>), dim3((unsigned)grid), dim3(256), 0,
-                       st, mp);
+  const dim3 g((unsigned)grid), b(256);
+  switch (d) {
+    case 32: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 32>), g, b, 0, st, mp); break;
+    case 64: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 64>), g, b, 0, st, mp); break;
+    case 96: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 96>), g, b, 0, st, mp); break;
+    case 128: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 128>), g, b, 0, st, mp); break;
+    default: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 256>), g, b, 0, st, mp); break;
+  }
   return hipGetLastError();
 }
 
@@ -967,18 +988,32 @@ hipError_t launch_t(const Plan& pl, long long nwg, const Params& p, hipStream_t 
   return hipGetLastError();
 }
 
+template <int DT, int D>
+hipError_t launch_c(bool causal, const Plan& pl, long long nwg, const Params& p,
+                    hipStream_t st) {
+  return causal ? launch_t<DT, D, true>(pl, nwg, p, st) : launch_t<DT, D, false>(pl, nwg, p, st);
+}
+
 template <int DT>
 hipError_t launch_d(int d, bool causal, const Plan& pl, long long nwg, const Params& p,
                     hipStream_t st) {
-  if (d == 128)
-    return causal ? launch_t<DT, 128, true>(pl, nwg, p, st)
-                  : launch_t<DT, 128, false>(pl, nwg, p, st);
-  return causal ? launch_t<DT, 64, true>(pl, nwg, p, st) : launch_t<DT, 64, false>(pl, nwg, p, st);
+  switch (d) {
+    case 32: return launch_c<DT, 32>(causal, pl, nwg, p, st);
+    case 64: return launch_c<DT, 64>(causal, pl, nwg, p, st);
+    case 96: return launch_c<DT, 96>(causal, pl, nwg, p, st);
+    case 128: return launch_c<DT, 128>(causal, pl, nwg, p, st);
+    default: return launch_c<DT, 256>(causal, pl, nwg, p, st);
+  }
 }
 
 Params fill_params(const Plan& pl, const void* q, const void* k, const void* v, void* o,
-                   float* lse, int B, int Sq, int Sk, int Hq, int Hkv, float scale) {
+                   float* lse, int B, int Sq, int Sk, int Hq, int Hkv, float scale,
+                   const Strides& st) {
   Params p{};
+  p.q_sb = st.s[0], p.q_ss = st.s[1], p.q_sh = st.s[2];
+  p.k_sb = st.s[3], p.k_ss = st.s[4], p.k_sh = st.s[5];
+  p.v_sb = st.s[6], p.v_ss = st.s[7], p.v_sh = st.s[8];
+  p.o_sb = st.s[9], p.o_ss = st.s[10], p.o_sh = st.s[11];
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
@@ -1010,6 +1045,51 @@ hipError_t launch_attn(int dtype, int d, int causal, const Plan& pl, long long n
                        const Params& p, hipStream_t st) {
   return dtype == ATTN_DTYPE_BF16 ? launch_d<ATTN_DTYPE_BF16>(d, causal != 0, pl, nwg, p, st)
                                   : launch_d<ATTN_DTYPE_F16>(d, causal != 0, pl, nwg, p, st);
+}
+
+// The forward pass with strides and an optional key split.  Arguments are
+// validated by the callers.
+attn_status run_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal,
+                        int dtype, const Strides& st, int kv_split, void* workspace,
+                        size_t workspace_bytes, hipStream_t hs) {
+  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split);
+  if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
+  if (sp.chunk > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
+                       workspace_bytes < sp.ws_bytes))
+    return ATTN_ERR_INVALID_ARG;
+  Params p = fill_params(sp.base, q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, scale, st);
+  if (sp.chunk == 0) {
+    hipError_t e = launch_attn(dtype, d, causal, sp.base, sp.grid, p, hs);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  }
+  p.chunk = sp.chunk;
+  p.q_split = sp.q_first;
+  p.sq_split = Sq - sp.q_first;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + sp.lse_offset);
+  hipError_t e = launch_attn(dtype, d, causal, sp.base, sp.grid, p, hs);
+  if (e != hipSuccess) return ATTN_ERR_LAUNCH;
+  MergeParams mp{};
+  mp.parts = p.part_o;
+  mp.parts_lse = p.part_lse;
+  mp.o = (uint16_t*)o;
+  mp.o_sb = p.o_sb, mp.o_ss = p.o_ss, mp.o_sh = p.o_sh;
+  mp.lse = lse;
+  mp.B = B;
+  mp.Sq = Sq;
+  mp.Hq = Hq;
+  mp.n_parts = 0;
+  mp.q_first = sp.q_first;
+  mp.sq_rows = Sq - sp.q_first;
+  mp.rows = sp.merge_rows;
+  mp.rows_wg = sp.base.rows_wg;
+  mp.chunk = sp.chunk;
+  mp.Sk = Sk;
+  mp.off = Sk - Sq;
+  mp.causal = causal;
+  e = launch_merge_any(ATTN_DTYPE_F32, dtype, d, sp.merge_grid, mp, hs);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -1046,10 +1126,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
                      float scale, int causal, int dtype, void* stream) {
   attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
   if (st != ATTN_OK) return st;
-  const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
-  const Params p = fill_params(pl, q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, scale);
-  hipError_t e = launch_attn(dtype, d, causal, pl, pl.grid, p, (hipStream_t)stream);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  return run_forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype,
+                     dense_strides(Sq, Sk, Hq, Hkv, d), 1, nullptr, 0, (hipStream_t)stream);
 }
 
 attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
@@ -1083,43 +1161,32 @@ attn_status attn_fwd_split(const void* q, const void* k, const void* v, void* o,
   attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
   if (st != ATTN_OK) return st;
   if (kv_split < 0) return ATTN_ERR_INVALID_ARG;
-  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split);
-  if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
-  if (sp.chunk > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
-                       workspace_bytes < sp.ws_bytes))
-    return ATTN_ERR_INVALID_ARG;
-  Params p = fill_params(sp.base, q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, scale);
-  hipStream_t hs = (hipStream_t)stream;
-  if (sp.chunk == 0) {
-    hipError_t e = launch_attn(dtype, d, causal, sp.base, sp.grid, p, hs);
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
-  }
-  p.chunk = sp.chunk;
-  p.q_split = sp.q_first;
-  p.sq_split = Sq - sp.q_first;
-  p.part_o = (float*)workspace;
-  p.part_lse = (float*)((char*)workspace + sp.lse_offset);
-  hipError_t e = launch_attn(dtype, d, causal, sp.base, sp.grid, p, hs);
-  if (e != hipSuccess) return ATTN_ERR_LAUNCH;
-  MergeParams mp{};
-  mp.parts = p.part_o;
-  mp.parts_lse = p.part_lse;
-  mp.o = (uint16_t*)o;
-  mp.lse = lse;
-  mp.B = B;
-  mp.Sq = Sq;
-  mp.Hq = Hq;
-  mp.n_parts = 0;
-  mp.q_first = sp.q_first;
-  mp.sq_rows = Sq - sp.q_first;
-  mp.rows = sp.merge_rows;
-  mp.rows_wg = sp.base.rows_wg;
-  mp.chunk = sp.chunk;
-  mp.Sk = Sk;
-  mp.off = Sk - Sq;
-  mp.causal = causal;
-  e = launch_merge_any(ATTN_DTYPE_F32, dtype, d, sp.merge_grid, mp, hs);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  return run_forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype,
+                     dense_strides(Sq, Sk, Hq, Hkv, d), kv_split, workspace, workspace_bytes,
+                     (hipStream_t)stream);
+}
+
+attn_status attn_fwd_strided_check(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int d,
+                                   float scale, int causal, int dtype,
+                                   const long long* strides) {
+  attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
+  if (st != ATTN_OK) return st;
+  return validate_strides((const int64_t*)strides);
+}
+
+attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int Sq, int Sk, int Hq, int Hkv, int d, float scale,
+                             int causal, int dtype, const long long* strides, int kv_split,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = attn_fwd_strided_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal,
+                                          dtype, strides);
+  if (st != ATTN_OK) return st;
+  if (kv_split < 0) return ATTN_ERR_INVALID_ARG;
+  Strides sv;
+  for (int i = 0; i < 12; ++i) sv.s[i] = strides[i];
+  return run_forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype, sv, kv_split,
+                     workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 attn_status attn_merge_check(const void* o_parts, const float* lse_parts, int n_parts,
@@ -1131,7 +1198,7 @@ attn_status attn_merge_check(const void* o_parts, const float* lse_parts, int n_
       parts_dtype != ATTN_DTYPE_BF16)
     return ATTN_ERR_UNSUPPORTED;
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   const uintptr_t need = parts_dtype == ATTN_DTYPE_F32 ? 15u : 7u;
   if (((uintptr_t)o_parts & need) || ((uintptr_t)o & 7u) || ((uintptr_t)lse_parts & 3u) ||
       ((uintptr_t)lse & 3u))
@@ -1151,6 +1218,7 @@ attn_status attn_merge(const void* o_parts, const float* lse_parts, int n_parts,
   mp.parts = o_parts;
   mp.parts_lse = lse_parts;
   mp.o = (uint16_t*)o;
+  mp.o_sb = (int64_t)Sq * Hq * d, mp.o_ss = (int64_t)Hq * d, mp.o_sh = d;
   mp.lse = lse;
   mp.B = B;
   mp.Sq = Sq;

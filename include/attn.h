@@ -70,7 +70,7 @@ typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1, ATTN_DTYPE_F32 = 2 } att
  *   o      device pointer, (B, Sq, Hq, d), 16-byte aligned; written
  *   lse    device pointer to B*Hq*Sq floats, 4-byte aligned, or NULL to skip
  *   B, Sq, Sk, Hq, Hkv, d   sizes, all >= 1; Hq must be a multiple of Hkv;
- *          d must be 64 or 128
+ *          d must be 32, 64, 96, 128 or 256
  *   scale  multiplier of the scores, finite and > 0 (1/sqrt(d) is usual)
  *   causal 0 = no mask, 1 = bottom-right causal mask
  *   dtype  an attn_dtype value
@@ -150,6 +150,39 @@ attn_status attn_fwd_split(const void* q, const void* k, const void* v, void* o,
                            size_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_strided -- attn_fwd_split on tensors with arbitrary row strides:
+ * any (batch, seq, head) layout with d contiguous, e.g. the (B, H, S, d)
+ * layout of the personal-notes and cuTile pages, or q, k, v sliced out of
+ * one packed projection output.
+ *
+ *   strides  12 element strides (not bytes), in the order
+ *            q: batch, seq, head;  k: batch, seq, head;
+ *            v: batch, seq, head;  o: batch, seq, head.
+ *            Element (b, s, h, c) of q is at q + b*qs_b + s*qs_s + h*qs_h + c.
+ *            Each stride must be >= 0 and a multiple of 8 (16-byte aligned
+ *            rows), and 64 * (k and v seq stride) * 2 < 2^31.  The rows of o
+ *            must not overlap each other or the inputs (not checked).
+ *   lse      as for attn_fwd: contiguous fp32 (B, Hq, Sq) or NULL
+ *   kv_split, workspace, workspace_bytes  as for attn_fwd_split (the
+ *            workspace size does not depend on the strides)
+ *
+ * Dense (B, S, H, d) strides give exactly attn_fwd_split's launches.
+ */
+attn_status attn_fwd_strided(const void* q, const void* k, const void* v,
+                             void* o, float* lse, int B, int Sq, int Sk,
+                             int Hq, int Hkv, int d, float scale, int causal,
+                             int dtype, const long long* strides,
+                             int kv_split, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* attn_fwd_strided's validation without any device call. */
+attn_status attn_fwd_strided_check(const void* q, const void* k, const void* v,
+                                   void* o, float* lse, int B, int Sq, int Sk,
+                                   int Hq, int Hkv, int d, float scale,
+                                   int causal, int dtype,
+                                   const long long* strides);
+
+/*
  * attn_fwd_split_workspace -- bytes of workspace attn_fwd_split needs for
  * these arguments (0 when it would not split), without any device call.
  * Returns the status attn_fwd_split's validation of the sizes would return.
@@ -191,7 +224,7 @@ attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
  *               natural-log LSE of each part, as attn_fwd returns it; 4-byte
  *               aligned
  *   n_parts     >= 1
- *   B, Sq, Hq, d  sizes (d = 64 or 128)
+ *   B, Sq, Hq, d  sizes (d = 32, 64, 96, 128 or 256)
  *   o           device pointer, (B, Sq, Hq, d) of dtype (F16 or BF16),
  *               8-byte aligned; written (must not overlap the inputs)
  *   lse         B * Hq * Sq floats, or NULL to skip

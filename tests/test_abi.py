@@ -72,6 +72,8 @@ def test_valid_arguments_pass_validation():
     assert _check() == ATTN_OK
     assert _check(lse=None) == ATTN_OK
     assert _check(d=64, dtype=ATTN_DTYPE_F16, causal=0) == ATTN_OK
+    for d in (32, 96, 256):
+        assert _check(d=d) == ATTN_OK
     # the largest head count whose 64-row tile stays below 2^31 bytes
     assert _check(Hq=(1 << 17) - 8, Hkv=(1 << 17) - 8, B=1, Sq=1, Sk=1) == ATTN_OK
 
@@ -92,7 +94,7 @@ def test_invalid_arguments(over):
     assert _check(**over) == ATTN_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("over", [dict(d=96), dict(d=256), dict(d=32),
+@pytest.mark.parametrize("over", [dict(d=80), dict(d=512), dict(d=16), dict(d=48),
                                   dict(dtype=2), dict(dtype=-1)])
 def test_unsupported(over):
     _lib()
@@ -257,7 +259,57 @@ def test_merge_validation():
                  dict(B=0), dict(Sq=0), dict(Hq=0), dict(o_parts=A + 8), dict(o=A + 4),
                  dict(lse=A + 2), dict(lse_parts=A + 2), dict(B=1 << 20, Sq=1 << 12)):
         assert _mcheck(**over) == ATTN_ERR_INVALID_ARG, over
-    for over in (dict(d=96), dict(parts_dtype=7), dict(dtype=binding.ATTN_DTYPE_F32)):
+    for over in (dict(d=80), dict(parts_dtype=7), dict(dtype=binding.ATTN_DTYPE_F32)):
         assert _mcheck(**over) == ATTN_ERR_UNSUPPORTED, over
     lib = _lib()
     assert lib.attn_merge(A, A, 0, 2, 1, 8, 2, 64, A, None, 0, None) == ATTN_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------ strided input
+
+def _dense(B, Sq, Sk, Hq, Hkv, d):
+    q = [Sq * Hq * d, Hq * d, d]
+    k = [Sk * Hkv * d, Hkv * d, d]
+    return q + k + k + q
+
+
+def test_strided_validation():
+    _lib()
+    B, Sq, Sk, Hq, Hkv, d = 2, 100, 120, 8, 2, 128
+    args = (A, A + 0x1000, A + 0x2000, A + 0x3000, A + 0x4000, B, Sq, Sk, Hq, Hkv, d,
+            0.125, 1, ATTN_DTYPE_BF16)
+    good = _dense(B, Sq, Sk, Hq, Hkv, d)
+    assert binding.attn_fwd_strided_check(*args, good) == ATTN_OK
+    # (B, H, S, d) strides and a packed (B, S, Hq + 2 Hkv, d) projection
+    bhsd = [Hq * Sq * d, d, Sq * d, Hkv * Sk * d, d, Sk * d, Hkv * Sk * d, d, Sk * d,
+            Hq * Sq * d, d, Sq * d]
+    assert binding.attn_fwd_strided_check(*args, bhsd) == ATTN_OK
+    W = (Hq + 2 * Hkv) * d
+    packed = [Sq * W, W, d, Sq * W, W, d, Sq * W, W, d] + good[9:]
+    assert binding.attn_fwd_strided_check(*args, packed) == ATTN_OK
+    assert binding.attn_fwd_strided_check(*args, [0] * 12) == ATTN_OK  # broadcast reads
+    for i in range(12):
+        for bad in (-8, 4, 1):
+            st = list(good)
+            st[i] = bad
+            assert binding.attn_fwd_strided_check(*args, st) == ATTN_ERR_INVALID_ARG, (i, bad)
+    for i in (4, 7):  # a 64-key tile must span less than 2^31 bytes
+        st = list(good)
+        st[i] = 1 << 24
+        assert binding.attn_fwd_strided_check(*args, st) == ATTN_ERR_INVALID_ARG
+    lib = _lib()
+    assert lib.attn_fwd_strided_check(*args[:11], ctypes.c_float(0.125), 1, ATTN_DTYPE_BF16,
+                                      None) == ATTN_ERR_INVALID_ARG
+    # the usual argument checks come first
+    bad_args = args[:9] + (6,) + args[10:]
+    assert binding.attn_fwd_strided_check(*bad_args, good) == ATTN_ERR_INVALID_ARG
+
+
+def test_strided_rejects_before_any_device_call():
+    lib = _lib()
+    st = binding._strides_arg([8] * 11 + [3])
+    assert lib.attn_fwd_strided(A, A, A, A, None, 1, 8, 8, 4, 4, 64, ctypes.c_float(1.0), 0,
+                                ATTN_DTYPE_F16, st, 0, None, 0, None) == ATTN_ERR_INVALID_ARG
+    st = binding._strides_arg(_dense(1, 8, 8, 4, 4, 64))
+    assert lib.attn_fwd_strided(A, A, A, A, None, 1, 8, 8, 4, 4, 64, ctypes.c_float(1.0), 0,
+                                ATTN_DTYPE_F16, st, -1, None, 0, None) == ATTN_ERR_INVALID_ARG

@@ -1,0 +1,142 @@
+"""GPU parity of the layout and head-size breadth, through the C ABI, against
+the fp64 oracle: strided inputs (the (B, H, S, d) layout, q/k/v sliced from a
+packed projection, an output written into a wider buffer), and head sizes
+32, 96 and 256 next to 64 and 128.  The oracle always sees the logical
+(B, S, H, d) tensors, made dense on the CPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_19_amd.workloads import Workload, make_inputs
+from parity_common import _check_full, _say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_attention_19_amd import load_library
+    load_library()  # fail loudly if the HIP library is missing
+
+
+def _w(name, B, Hq, Hkv, Sq, Sk, d, dt, causal):
+    return Workload(name, B, Hq, Hkv, Sq, Sk, d, dt, causal, 1.0 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("kv_split", [1, 0, 3])
+@pytest.mark.parametrize("Sq,Sk,causal,dt,Hq,Hkv", [
+    (300, 300, True, "bf16", 8, 2), (129, 700, True, "f16", 4, 4),
+    (700, 129, True, "bf16", 8, 1), (257, 333, False, "f16", 6, 3)])
+def test_bhsd_layout(Sq, Sk, causal, dt, Hq, Hkv, kv_split):
+    from exact_attention_19_amd import attn_fwd_strided
+    w = _w(f"bhsd_{Sq}_{Sk}", 2, Hq, Hkv, Sq, Sk, 128, dt, causal)
+    q, k, v = make_inputs(w, seed=Sq + Sk)
+    # (B, H, S, d) copies on the device
+    qh, kh, vh = (t.transpose(1, 2).contiguous().cuda() for t in (q, k, v))
+    _say(f"[gpu] attn_fwd_strided bhsd {w.name} {dt} causal={causal} kv_split={kv_split}")
+    o, lse = attn_fwd_strided(qh, kh, vh, scale=w.scale, causal=causal, layout="bhsd",
+                              kv_split=kv_split)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (2, Hq, Sq, 128)
+    _check_full(w, q, k, v, o.transpose(1, 2).cpu(), lse.cpu(), strict=False)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_qkv_projection(causal):
+    """q, k, v as head slices of one (B, S, Hq + 2 Hkv, d) tensor (Sq = Sk)."""
+    from exact_attention_19_amd import attn_fwd_strided
+    B, S, Hq, Hkv, d = 2, 333, 8, 2, 128
+    w = _w("packed", B, Hq, Hkv, S, S, d, "bf16", causal)
+    q, k, v = make_inputs(w, seed=7)
+    packed = torch.cat([q, k, v], dim=2).cuda()  # (B, S, Hq + 2 Hkv, d)
+    qs, ks, vs = packed[:, :, :Hq], packed[:, :, Hq:Hq + Hkv], packed[:, :, Hq + Hkv:]
+    assert not qs.is_contiguous()
+    _say(f"[gpu] attn_fwd_strided packed causal={causal}")
+    o, lse = attn_fwd_strided(qs, ks, vs, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+
+
+def test_k_and_v_with_different_strides_and_strided_output():
+    """k in (B, S, H, d), v in (B, H, S, d) (as logical views), and o written
+    into the first half of a wider buffer whose second half must stay."""
+    from exact_attention_19_amd import attn_fwd_strided
+    B, Sq, Sk, Hq, Hkv, d = 2, 200, 450, 8, 4, 64
+    w = _w("mixed", B, Hq, Hkv, Sq, Sk, d, "f16", True)
+    q, k, v = make_inputs(w, seed=8)
+    vg = v.transpose(1, 2).contiguous().cuda().transpose(1, 2)  # logical (B, Sk, Hkv, d)
+    wide = torch.full((B, Sq, Hq, 2 * d), 5.0, dtype=torch.float16, device="cuda")
+    out = wide[..., :d]
+    for kv_split in (1, 4):
+        _say(f"[gpu] attn_fwd_strided mixed strides kv_split={kv_split}")
+        o, lse = attn_fwd_strided(q.cuda(), k.cuda(), vg, scale=w.scale, causal=True, out=out,
+                                  kv_split=kv_split)
+        torch.cuda.synchronize()
+        assert o.data_ptr() == out.data_ptr()
+        assert torch.all(wide[..., d:] == 5.0)
+        _check_full(w, q, k, v, out.cpu(), lse.cpu(), strict=False)
+
+
+def test_strided_dense_equals_attn_fwd_bit_for_bit():
+    from exact_attention_19_amd import attn_fwd, attn_fwd_strided
+    w = _w("dense_eq", 1, 16, 4, 513, 1000, 128, "bf16", True)
+    q, k, v = (t.cuda() for t in make_inputs(w, seed=9))
+    o1, l1 = attn_fwd(q, k, v, scale=w.scale, causal=True)
+    o2, l2 = attn_fwd_strided(q, k, v, scale=w.scale, causal=True, kv_split=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _head_size_cases():
+    cases = []
+    for d in (32, 96, 256):
+        for dt in ("f16", "bf16"):
+            cases.append((d, dt, 1, 128, 128, False, 2, 2))
+            cases.append((d, dt, 2, 333, 517, True, 8, 2))
+            cases.append((d, dt, 1, 517, 300, True, 4, 4))
+            cases.append((d, dt, 1, 1, 700, True, 8, 1))
+    return cases
+
+
+@pytest.mark.parametrize("d,dt,B,Sq,Sk,causal,Hq,Hkv", _head_size_cases())
+def test_head_sizes(d, dt, B, Sq, Sk, causal, Hq, Hkv):
+    from exact_attention_19_amd import attn_fwd
+    w = _w(f"hd{d}_{dt}_{Sq}_{Sk}", B, Hq, Hkv, Sq, Sk, d, dt, causal)
+    q, k, v = make_inputs(w, seed=d + Sq)
+    _say(f"[gpu] attn_fwd head size {d} {w.name} causal={causal}")
+    o, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_head_sizes_with_key_split(d):
+    from exact_attention_19_amd import attn_fwd_split
+    w = _w(f"hd{d}_split", 1, 8, 2, 300, 2000, d, "bf16", True)
+    q, k, v = make_inputs(w, seed=d)
+    _say(f"[gpu] attn_fwd_split head size {d}")
+    o, lse = attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=True,
+                            kv_split=5)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+
+
+def test_merge_head_sizes():
+    """attn_merge at d = 96 (a row of 24 threads) against numpy in fp64."""
+    from exact_attention_19_amd import attn_merge
+    from oracle import merge_partials_oracle
+    r = np.random.default_rng(12)
+    P, B, Sq, Hq, d = 3, 2, 37, 3, 96
+    op = r.standard_normal((P, B, Sq, Hq, d)).astype(np.float32)
+    lp = (2 * r.standard_normal((P, B, Hq, Sq))).astype(np.float32)
+    o_ref, lse_ref = merge_partials_oracle(op.astype(np.float64), lp.astype(np.float64))
+    o, lse = attn_merge(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda(),
+                        dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert np.abs(o.double().cpu().numpy() - o_ref).max() <= 2e-3
+    assert np.abs(lse.double().cpu().numpy() - lse_ref).max() <= 1e-4
