@@ -116,10 +116,51 @@ def board_power():
                              text=True, timeout=20).stdout
     except (OSError, subprocess.SubprocessError):
         return None
-    watts = [l.split(":")[1].strip() for l in out.splitlines() if "SOCKET_POWER" in l]
+    power = {}
+    for line in out.splitlines():
+        key, _, val = line.strip().partition(":")
+        if "POWER" in key and val.strip():
+            power.setdefault(key.strip().lower(), val.strip())
     clks = [l.split(":")[1].strip() for l in out.splitlines()
             if l.strip().startswith("CLK:")][:8]
-    return {"socket_power": watts[0] if watts else None, "gfx_clk": clks}
+    return {"power": power, "gfx_clk": clks}
+
+
+class BoardSampler:
+    """Reads the board with amd-smi over and over in a thread until stopped;
+    keeps the reading with the highest socket power (the loaded one)."""
+
+    def __init__(self):
+        import threading
+        self.stop = threading.Event()
+        self.samples = []
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self.stop.is_set():
+            b = board_power()
+            if b is None:
+                return
+            self.samples.append(b)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join(timeout=30)
+
+    def loaded(self):
+        def watts(b):
+            try:
+                return float(b["power"].get("socket_power", "0").split()[0])
+            except (ValueError, AttributeError):
+                return 0.0
+        if not self.samples:
+            return {}
+        best = max(self.samples, key=watts)
+        return dict(best, samples=len(self.samples))
 
 
 def gemm_probe(steps: int):
@@ -134,23 +175,18 @@ def gemm_probe(steps: int):
     for _ in range(20):
         torch.matmul(a, b, out=c)
     torch.cuda.synchronize()
-    # the board's power and clocks, sampled while the GEMMs run
-    import threading
-    board = {}
-    sampler = threading.Thread(target=lambda: board.update(board_power() or {}))
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
-        torch.matmul(a, b, out=c)
-    e.record()
-    sampler.start()
-    torch.cuda.synchronize()
-    sampler.join()
+    with BoardSampler() as board:  # the board's power and clocks during the GEMMs
+        s.record()
+        for _ in range(steps):
+            torch.matmul(a, b, out=c)
+        e.record()
+        torch.cuda.synchronize()
     ms = s.elapsed_time(e) / steps
     print(json.dumps({"gemm_probe": f"bf16 {n}x{n}x{n}", "ms": round(ms, 4),
                       "tflops": round(2 * n ** 3 / ms / 1e9, 1),
-                      "board_during_gemms": board}), flush=True)
+                      "board_during_gemms": board.loaded()}), flush=True)
 
 
 def copy_probe(mib: int, steps: int):
@@ -179,6 +215,9 @@ def main():
                     help="key split of attn_fwd_split: 0 = the library's choice, "
                          "1 = none, N = at most N pieces per query block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--board-sample", action="store_true",
+                    help="after the timed steps, keep stepping for about 3 s while "
+                         "amd-smi reads the socket power and clocks")
     ap.add_argument("--gemm-probe", action="store_true",
                     help="only time a plain bf16 GEMM --steps times (reference)")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
@@ -295,6 +334,13 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count},
         "kernel_source_digest": kernel_source_digest(),
     }
+    if args.board_sample:
+        # about 8 s of back-to-back steps while amd-smi reads the board
+        with BoardSampler() as board:
+            for _ in range(max(4, int(8.0 / max(kern_avg_s, 1e-6)))):
+                step()
+            torch.cuda.synchronize()
+        result["device"]["board_under_load"] = board.loaded()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu)
     print(json.dumps(result), flush=True)
