@@ -10,6 +10,8 @@ row, then P V; see that file's header for the citations).  ``build_oracle``
 compiles it with gcc.  ``attn_fwd_oracle(..., key_range=(k0, k1))`` gives the
 partial state of each row over a key subset, and ``merge_partials_oracle``
 (numpy fp64) combines such partial states with the online-softmax update.
+``attn_bwd_oracle`` gives the gradients of sum(dO * O) through the same
+definition (chain rule, softmax Jacobian).
 """
-from .oracle import (attn_fwd_oracle, build_oracle, merge_partials_oracle,  # noqa: F401
-                     oracle_lib_path)
+from .oracle import (attn_bwd_oracle, attn_fwd_oracle, build_oracle,  # noqa: F401
+                     merge_partials_oracle, oracle_lib_path)

@@ -205,3 +205,147 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v,
     return oracle_attn_fwd_range(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale,
                                  causal, 0, Sk, rows, nrows, nthreads);
 }
+
+/*
+ * Backward pass: the gradients of L = sum(dO * O) with respect to q, k and
+ * v, from the plain definition, in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY (see the top of this file).
+ *
+ * The pages return the LSE for training (the CuTe DSL example's docstring)
+ * and name FlashAttention 1 and 2 as the algorithms; they print no backward
+ * formula, so this is the chain rule through the forward definition above:
+ *
+ *   p_ij   = softmax_j(s_ij) over the visible keys   (forward definition)
+ *   dv_j  += sum_i p_ij * do_i                       (O = P V)
+ *   dp_ij  = do_i . v_j
+ *   ds_ij  = p_ij * (dp_ij - sum_j' p_ij' dp_ij')    (Jacobian of softmax:
+ *            d p_ij / d s_ij' = p_ij (delta_jj' - p_ij'))
+ *   dq_i   = scale * sum_j ds_ij k_j                 (s = scale * q . k)
+ *   dk_j  += scale * sum_i ds_ij q_i
+ *
+ * GQA: dk and dv of kv head kvh sum the contributions of every query head
+ * that reads it.  Rows with no visible key contribute nothing and get dq = 0.
+ * P is materialised per row (two passes, as in the forward); nothing is
+ * tiled.  Work is dealt per (batch, kv head) so that each thread owns its
+ * dk and dv rows; results do not depend on the thread count.
+ */
+typedef struct {
+    const double *q, *k, *v, *dout;
+    double *dq, *dk, *dv;
+    int64_t B, Sq, Sk, Hq, Hkv, d;
+    double scale;
+    int causal;
+    int64_t first, stride; /* (b, kvh) pairs first, first + stride, ... */
+} bjob_t;
+
+static void *bwd_worker(void *arg) {
+    const bjob_t *J = (const bjob_t *)arg;
+    const int64_t d = J->d, g = J->Hq / J->Hkv;
+    double *s = (double *)malloc(sizeof(double) * (size_t)J->Sk);
+    double *p = (double *)malloc(sizeof(double) * (size_t)J->Sk);
+    double *dp = (double *)malloc(sizeof(double) * (size_t)J->Sk);
+    if (!s || !p || !dp) {
+        free(s); free(p); free(dp);
+        return (void *)1;
+    }
+    for (int64_t pair = J->first; pair < J->B * J->Hkv; pair += J->stride) {
+        const int64_t b = pair / J->Hkv, kvh = pair % J->Hkv;
+        for (int64_t j = 0; j < J->Sk; ++j)
+            for (int64_t c = 0; c < d; ++c) {
+                J->dk[((b * J->Sk + j) * J->Hkv + kvh) * d + c] = 0.0;
+                J->dv[((b * J->Sk + j) * J->Hkv + kvh) * d + c] = 0.0;
+            }
+        for (int64_t h = kvh * g; h < (kvh + 1) * g; ++h) {
+            for (int64_t i = 0; i < J->Sq; ++i) {
+                const double *qrow = J->q + ((b * J->Sq + i) * J->Hq + h) * d;
+                const double *dorow = J->dout + ((b * J->Sq + i) * J->Hq + h) * d;
+                double *dqrow = J->dq + ((b * J->Sq + i) * J->Hq + h) * d;
+                for (int64_t c = 0; c < d; ++c) dqrow[c] = 0.0;
+                int64_t nvis = J->Sk;
+                if (J->causal) {
+                    int64_t lim = i + (J->Sk - J->Sq) + 1;
+                    if (lim < 0) lim = 0;
+                    if (lim < nvis) nvis = lim;
+                }
+                if (nvis == 0) continue;
+                /* forward: scores, max, probabilities */
+                double m = -INFINITY;
+                for (int64_t j = 0; j < nvis; ++j) {
+                    const double *krow = J->k + ((b * J->Sk + j) * J->Hkv + kvh) * d;
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < d; ++c) acc += qrow[c] * krow[c];
+                    s[j] = J->scale * acc;
+                    if (s[j] > m) m = s[j];
+                }
+                double sum = 0.0;
+                for (int64_t j = 0; j < nvis; ++j) {
+                    p[j] = exp(s[j] - m);
+                    sum += p[j];
+                }
+                for (int64_t j = 0; j < nvis; ++j) p[j] /= sum;
+                /* dp and the softmax Jacobian-vector product */
+                double pdp = 0.0;
+                for (int64_t j = 0; j < nvis; ++j) {
+                    const double *vrow = J->v + ((b * J->Sk + j) * J->Hkv + kvh) * d;
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < d; ++c) acc += dorow[c] * vrow[c];
+                    dp[j] = acc;
+                    pdp += p[j] * acc;
+                }
+                for (int64_t j = 0; j < nvis; ++j) {
+                    const double ds = p[j] * (dp[j] - pdp);
+                    const double *krow = J->k + ((b * J->Sk + j) * J->Hkv + kvh) * d;
+                    double *dkrow = J->dk + ((b * J->Sk + j) * J->Hkv + kvh) * d;
+                    double *dvrow = J->dv + ((b * J->Sk + j) * J->Hkv + kvh) * d;
+                    for (int64_t c = 0; c < d; ++c) {
+                        dqrow[c] += J->scale * ds * krow[c];
+                        dkrow[c] += J->scale * ds * qrow[c];
+                        dvrow[c] += p[j] * dorow[c];
+                    }
+                }
+            }
+        }
+    }
+    free(s); free(p); free(dp);
+    return NULL;
+}
+
+/*
+ * q, dout, dq: (B, Sq, Hq, d); k, v, dk, dv: (B, Sk, Hkv, d), all fp64.
+ * Returns 0 on success, 1 on bad arguments, 2 if a thread failed.
+ */
+int oracle_attn_bwd(const double *q, const double *k, const double *v,
+                    const double *dout, double *dq, double *dk, double *dv,
+                    int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
+                    int64_t d, double scale, int causal, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+    if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || d < 1) return 1;
+    if (Hq % Hkv != 0) return 1;
+    if (causal != 0 && causal != 1) return 1;
+    const int64_t pairs = B * Hkv;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > pairs) nthreads = (int)pairs;
+    bjob_t jobs[256];
+    pthread_t tid[256];
+    int started[256];
+    int rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        bjob_t *J = &jobs[t];
+        J->q = q; J->k = k; J->v = v; J->dout = dout;
+        J->dq = dq; J->dk = dk; J->dv = dv;
+        J->B = B; J->Sq = Sq; J->Sk = Sk; J->Hq = Hq; J->Hkv = Hkv; J->d = d;
+        J->scale = scale; J->causal = causal;
+        J->first = t; J->stride = nthreads;
+        started[t] = pthread_create(&tid[t], NULL, bwd_worker, J) == 0;
+        if (!started[t]) rc = 2;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        if (!started[t]) continue;
+        void *ret = NULL;
+        pthread_join(tid[t], &ret);
+        if (ret) rc = 2;
+    }
+    return rc;
+}

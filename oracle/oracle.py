@@ -47,6 +47,10 @@ def _load():
         f.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64,
                       ctypes.c_double, ctypes.c_int, i64, i64,
                       ctypes.POINTER(ctypes.c_int64), i64, ctypes.c_int]
+        g = lib.oracle_attn_bwd
+        g.restype = ctypes.c_int
+        g.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64,
+                      ctypes.c_double, ctypes.c_int, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -146,3 +150,29 @@ def merge_partials_oracle(o_parts, lse_parts):
     o = np.where(seen[..., None], acc / np.where(seen, l, 1.0)[..., None], 0.0)
     lse = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)
     return o.transpose(0, 2, 1, 3).copy(), lse
+
+
+def attn_bwd_oracle(q, k, v, dout, scale: float, causal: bool, nthreads: int | None = None):
+    """Gradients (dq, dk, dv) of sum(dout * O) in fp64, O the attention
+    forward of (q, k, v); shapes as for attn_fwd_oracle, dout like q.  The
+    arithmetic is attn_oracle.c's oracle_attn_bwd (chain rule through the
+    two-pass softmax definition)."""
+    qd, kd, vd, dod = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    B, Sq, Hq, d = qd.shape
+    Bk, Sk, Hkv, dk_ = kd.shape
+    if vd.shape != kd.shape or Bk != B or dk_ != d or dod.shape != qd.shape:
+        raise ValueError("shape mismatch between q, k, v, dout")
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    dq = np.empty_like(qd)
+    dk = np.empty_like(kd)
+    dv = np.empty_like(vd)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = _load().oracle_attn_bwd(
+        qd.ctypes.data_as(dp), kd.ctypes.data_as(dp), vd.ctypes.data_as(dp),
+        dod.ctypes.data_as(dp), dq.ctypes.data_as(dp), dk.ctypes.data_as(dp),
+        dv.ctypes.data_as(dp), B, Sq, Sk, Hq, Hkv, d, float(scale), int(bool(causal)),
+        int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd failed with code {rc}")
+    return dq, dk, dv

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attn_fwd_oracle, merge_partials_oracle
+from oracle import attn_bwd_oracle, attn_fwd_oracle, merge_partials_oracle
 from exact_attention_19_amd.workloads import WORKLOADS, make_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_form_cases.json")
@@ -507,3 +507,102 @@ def test_key_range_bad_arguments_rejected():
     for kr in ((-1, 3), (3, 2), (0, 6)):
         with pytest.raises(ValueError):
             attn_fwd_oracle(q, k, v, 1.0, False, key_range=kr)
+
+
+# ----------------------------------------------------------- backward pass
+
+def test_backward_golden_cases():
+    data = json.load(open(GOLDEN))["backward_cases"]
+    for case in data["cases"]:
+        q = _arr(case["q"])[None, :, None, :]
+        k = _arr(case["k"])[None, :, None, :]
+        v = _arr(case["v"])[None, :, None, :]
+        do = _arr(case["dout"])[None, :, None, :]
+        dq, dk, dv = attn_bwd_oracle(q, k, v, do, case["scale"], case["causal"])
+        for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+            np.testing.assert_allclose(got[0, :, 0, :], _arr(case[name]), rtol=1e-14,
+                                       atol=1e-14, err_msg=f"{case['name']} {name}")
+
+
+def _loss(q, k, v, do, scale, causal):
+    o, _ = attn_fwd_oracle(q, k, v, scale, causal)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_central_differences(causal):
+    """Each gradient entry against (L(x + h) - L(x - h)) / 2h of the forward
+    oracle, on a tiny GQA case with an offset."""
+    q, k, v = _rand(50, 1, 5, 7, 4, 2, 3)
+    do = _rng(51).standard_normal(q.shape)
+    scale, h = 0.7, 1e-5
+    dq, dk, dv = attn_bwd_oracle(q, k, v, do, scale, causal)
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(*x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = _loss(q, k, v, do, scale, causal)
+            x[idx] = keep - h
+            lm = _loss(q, k, v, do, scale, causal)
+            x[idx] = keep
+            assert abs((lp - lm) / (2 * h) - g[idx]) < 1e-8, (idx, g[idx])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_torch_autograd_fp64(causal):
+    """torch CPU autograd in fp64 through softmax(QK^T * scale + mask) V
+    (an independent library path) with GQA and a bottom-right offset."""
+    B, Sq, Sk, Hq, Hkv, d = 2, 19, 31, 8, 2, 16
+    q, k, v = _rand(52, B, Sq, Sk, Hq, Hkv, d)
+    do = _rng(53).standard_normal(q.shape)
+    dq, dk, dv = attn_bwd_oracle(q, k, v, do, 0.3, causal)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    kk = tk.repeat_interleave(Hq // Hkv, dim=2).permute(0, 2, 3, 1)   # (B, H, d, Sk)
+    vv = tv.repeat_interleave(Hq // Hkv, dim=2).permute(0, 2, 1, 3)   # (B, H, Sk, d)
+    s = torch.matmul(tq.permute(0, 2, 1, 3), kk) * 0.3
+    s = s.masked_fill(~torch.from_numpy(_mask(Sq, Sk, causal)), float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), vv).permute(0, 2, 1, 3)
+    (o * torch.from_numpy(do)).sum().backward()
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    """sum_j dK_j = 0 (rows of dS sum to zero); sum_j dV_j = sum of dO over
+    the rows that see a key (rows of P sum to one), per (batch, kv head)."""
+    B, Sq, Sk, Hq, Hkv, d = 2, 23, 17, 6, 2, 8
+    q, k, v = _rand(54, B, Sq, Sk, Hq, Hkv, d)
+    do = _rng(55).standard_normal(q.shape)
+    dq, dk, dv = attn_bwd_oracle(q, k, v, do, 0.9, causal)
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    seen = np.array([min(Sk, max(0, i + Sk - Sq + 1)) > 0 if causal else True
+                     for i in range(Sq)])
+    g = Hq // Hkv
+    for kvh in range(Hkv):
+        want = do[:, seen, kvh * g:(kvh + 1) * g].sum(axis=(1, 2))
+        np.testing.assert_allclose(dv[:, :, kvh].sum(axis=1), want, atol=1e-12)
+    # rows that see no key get dq = 0
+    assert np.all(dq[:, ~seen] == 0)
+
+
+def test_backward_constant_v_and_key_shift():
+    """Equal V rows make O independent of Q and K: dQ = dK = 0.  Shifting every
+    key by one vector leaves P, hence dQ, dV (and dK) unchanged."""
+    B, Sq, Sk, Hq, Hkv, d = 1, 9, 12, 4, 2, 8
+    q, k, v = _rand(56, B, Sq, Sk, Hq, Hkv, d)
+    do = _rng(57).standard_normal(q.shape)
+    vc = np.broadcast_to(v[:, :1], v.shape).copy()
+    dq, dk, dv = attn_bwd_oracle(q, k, vc, do, 0.5, True)
+    assert np.abs(dq).max() < 1e-13 and np.abs(dk).max() < 1e-13
+    dq1, dk1, dv1 = attn_bwd_oracle(q, k, v, do, 0.5, True)
+    shift = _rng(58).standard_normal((1, 1, Hkv, d))
+    dq2, dk2, dv2 = attn_bwd_oracle(q, k + shift, v, do, 0.5, True)
+    for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
+        np.testing.assert_allclose(a, b, atol=1e-11)
+
+
+def test_backward_bad_arguments_rejected():
+    q, k, v = _rand(59, 1, 3, 5, 2, 2, 4)
+    with pytest.raises(ValueError):
+        attn_bwd_oracle(q, k, v, q[:, :2], 1.0, False)
