@@ -18,8 +18,8 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 
 ATTN_DTYPE_F16, ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1, 2
 EXPORTED = ("attn_fwd", "attn_fwd_check", "attn_fwd_plan", "attn_fwd_split",
             "attn_fwd_split_workspace", "attn_fwd_split_plan", "attn_fwd_strided",
-            "attn_fwd_strided_check", "attn_merge", "attn_merge_check",
-            "attn_status_str", "attn_abi_version")
+            "attn_fwd_strided_check", "attn_merge", "attn_merge_check", "attn_bwd",
+            "attn_bwd_check", "attn_bwd_workspace", "attn_status_str", "attn_abi_version")
 
 _lib = None
 
@@ -60,6 +60,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      vp, sz, vp]
     lib.attn_fwd_strided_check.restype = i
     lib.attn_fwd_strided_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, ll12]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_bwd_check.restype = i
+    lib.attn_bwd_check.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i]
+    lib.attn_bwd_workspace.restype = i
+    lib.attn_bwd_workspace.argtypes = [i, i, i, ctypes.POINTER(sz)]
     lib.attn_merge.restype = i
     lib.attn_merge.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i, vp]
     lib.attn_merge_check.restype = i
@@ -339,3 +345,58 @@ def attn_merge(o_parts, lse_parts, dtype=None, out=None, lse=None,
     if st != ATTN_OK:
         raise AttnError(st, "attn_merge")
     return out, lse
+
+
+def attn_bwd_workspace(B, Sq, Hq) -> int:
+    """Workspace bytes attn_bwd needs (two fp32 values per query row)."""
+    n = ctypes.c_size_t(0)
+    st = load_library().attn_bwd_workspace(B, Sq, Hq, ctypes.byref(n))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_workspace")
+    return int(n.value)
+
+
+def attn_bwd_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr,
+                   B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype_code) -> int:
+    """attn_bwd's validation on raw addresses; returns the status code."""
+    return int(load_library().attn_bwd_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr,
+                                             dq_ptr, dk_ptr, dv_ptr, B, Sq, Sk, Hq, Hkv, d,
+                                             float(scale), int(causal), dtype_code))
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * o) for o, lse = attn_fwd(q, k, v).
+
+    q, o, dout: (B, Sq, Hq, d); k, v: (B, Sk, Hkv, d); one dtype (fp16/bf16),
+    dense; lse: (B, Hq, Sq) fp32 from attn_fwd.  Outputs are allocated when
+    not given; ``workspace`` (uint8, attn_bwd_workspace bytes) likewise."""
+    import torch
+    B, Sq, Sk, Hq, Hkv, d, code = _check_qkv(q, k, v)
+    for name, t in (("o", o), ("dout", dout)):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_cuda \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped like its input")
+    if workspace is None:
+        workspace = torch.empty(attn_bwd_workspace(B, Sq, Hq), dtype=torch.uint8,
+                                device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Sq, Sk, Hq, Hkv, d, float(scale),
+        int(bool(causal)), code, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

@@ -1,0 +1,575 @@
+// Backward pass of the fused exact attention for AMD Instinct MI355X (gfx950).
+//
+// Given Q, K, V, the forward output O and its LSE, and the output gradient
+// dO, computes dQ, dK, dV of L = sum(dO * O).  The LSE is what the forward
+// returns it for (the CuTe DSL example's docstring: the log-sum-exp is kept
+// for training); the algorithm is the FlashAttention-2 backward the pages
+// cite: P is recomputed tile by tile from the scores and the LSE, never
+// stored, with
+//
+//   D_i   = dO_i . O_i                       (= sum_j P_ij dP_ij)
+//   dP_ij = dO_i . V_j
+//   dS_ij = P_ij (dP_ij - D_i)
+//   dV_j  = sum_i P_ij dO_i
+//   dQ_i  = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i
+//
+// Three launches on one stream:
+//   prep   D_i and lse_i * log2(e) per query row (memory-bound),
+//   dq     query-row outer, like the forward: one wave owns 32 query rows,
+//          K and V tiles stream through LDS, dQ^T = K^T dS^T accumulates in
+//          registers,
+//   dkdv   key outer: one wave owns 32 keys of one kv head, the Q and dO
+//          tiles of every query row (and every query head of the GQA group)
+//          that sees them stream through LDS, dK^T = Q^T dS and dV^T = dO^T P
+//          accumulate in registers.
+// Each gradient element is written once by one lane: no atomics, and the
+// results do not depend on scheduling.
+//
+// The MFMA layouts follow the forward kernel: a 32x32x16 accumulator of a
+// product whose rows were fed in the sigma order is, converted to 16 bit,
+// directly the B operand of the next product over those rows; operands with
+// the tile's rows as the contraction come from ds_read_b64_tr_b16.
+
+#include "attn_common.h"
+
+namespace {
+
+constexpr float LOG2E = 1.44269504088896340736f;
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dvec;  // D_i, [B][Hq][Sq]
+  float* l2;    // lse_i * log2(e), +inf for rows that see no key, [B][Hq][Sq]
+  int B, Sq, Sk, Hq, Hkv;
+  int group, gh, hsub, rows_wg, qtiles, ncols, xcd_cols;  // dq launch (forward plan)
+  int off;      // Sk - Sq
+  float scale, scale_log2;
+};
+
+// ------------------------------------------------------------ prep
+// Eight threads per query row, each over 16-byte chunks t, t + 8, ... of the
+// row, then a reduction over the eight lanes.  Rows are taken in memory
+// order (b, i, h), so consecutive rows are contiguous.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  const int t = threadIdx.x & 7;
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
+  const bool valid = row < rows;
+  float acc = 0.f;
+  if (valid) {
+    const uint16_t* orow = p.o + row * D;
+    const uint16_t* drow = p.dout + row * D;
+    for (int c = t; c < CH; c += 8) {
+      const u32x4 a = *(const u32x4*)(orow + 8 * c);
+      const u32x4 g = *(const u32x4*)(drow + 8 * c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float a0, a1, g0, g1;
+        if constexpr (DT == ATTN_DTYPE_BF16) {
+          a0 = __uint_as_float(a[w] << 16);
+          a1 = __uint_as_float(a[w] & 0xffff0000u);
+          g0 = __uint_as_float(g[w] << 16);
+          g1 = __uint_as_float(g[w] & 0xffff0000u);
+        } else {
+          a0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(a[w] & 0xffffu));
+          a1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(a[w] >> 16));
+          g0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(g[w] & 0xffffu));
+          g1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(g[w] >> 16));
+        }
+        acc = __builtin_fmaf(a0, g0, acc);
+        acc = __builtin_fmaf(a1, g1, acc);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 1, 8);
+  acc += __shfl_xor(acc, 2, 8);
+  acc += __shfl_xor(acc, 4, 8);
+  if (valid && t == 0) {
+    const int h = (int)(row % p.Hq);
+    const int64_t bi = row / p.Hq;
+    const int i = (int)(bi % p.Sq);
+    const int b = (int)(bi / p.Sq);
+    const int64_t at = ((int64_t)b * p.Hq + h) * p.Sq + i;
+    const float l = p.lse[at];
+    p.dvec[at] = acc;
+    p.l2[at] = l > -INFINITY ? l * LOG2E : INFINITY;
+  }
+}
+
+// ------------------------------------------------------------ dQ
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdParams p) {
+  using T = Ty<DT>;
+  constexpr int CB = D / 32;
+  constexpr int KK = D / 16;
+  constexpr int TB = 64 * D * 2;
+  __shared__ __attribute__((aligned(1024))) char lds_k0[TB], lds_k1[TB], lds_v0[TB], lds_v1[TB];
+  auto kbuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_k1 : (LDS_PTR(char))lds_k0; };
+  auto vbuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_v1 : (LDS_PTR(char))lds_v0; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // work decode: the forward's (heaviest row blocks first, XCD-grouped)
+  int qt, col;
+  {
+    const int L = blockIdx.x;
+    if (p.xcd_cols > 0) {
+      const int xcd = L & 7;
+      const int k = L >> 3;
+      qt = p.qtiles - 1 - k / p.xcd_cols;
+      col = xcd * p.xcd_cols + k % p.xcd_cols;
+    } else {
+      qt = p.qtiles - 1 - L / p.ncols;
+      col = L % p.ncols;
+    }
+  }
+  const int hs = col % p.hsub;
+  const int kvh = (col / p.hsub) % p.Hkv;
+  const int b = col / (p.hsub * p.Hkv);
+  const int hq = kvh * p.group + hs * p.gh + wave % p.gh;
+  const int q0wg = qt * p.rows_wg;
+  const int q0w = q0wg + (wave / p.gh) * 32;
+
+  const int n_end = block_tiles(q0wg, p.rows_wg, p.Sq, p.Sk, p.off, CAUSAL);
+  int n_full = p.Sk / 64;
+  if (CAUSAL) {
+    const int lim = q0wg + p.off + 1;
+    n_full = min(n_full, lim > 0 ? lim / 64 : 0);
+  }
+
+  const uint32_t rbkv = (uint32_t)p.Hkv * D * 2;
+  const char* kslice = (const char*)(p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
+  const char* vslice = (const char*)(p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
+
+  // this lane's query row: Q and dO fragments (B operands, d as k)
+  const int qi = q0w + l32;
+  const bool ok = qi < p.Sq;
+  i16x8 qf[KK], dof[KK];
+  {
+    const int64_t r = ((int64_t)b * p.Sq + (ok ? qi : 0)) * p.Hq + hq;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (ok) {
+        x = *(const u32x4*)(p.q + r * D + kk * 16 + hh * 8);
+        y = *(const u32x4*)(p.dout + r * D + kk * 16 + hh * 8);
+      }
+      qf[kk] = __builtin_bit_cast(i16x8, x);
+      dof[kk] = __builtin_bit_cast(i16x8, y);
+    }
+  }
+  float lse2 = INFINITY, drow = 0.f;
+  if (ok) {
+    const int64_t at = ((int64_t)b * p.Hq + hq) * p.Sq + qi;
+    lse2 = p.l2[at];
+    drow = p.dvec[at];
+  }
+  int lim_row = p.Sk - 1;
+  if (CAUSAL) lim_row = min(lim_row, qi + p.off);
+
+  uint32_t rbase[2], tbase[2];
+  row_frag_bases(lane, rbase);
+  tr_frag_bases(lane, tbase);
+
+  f32x16 acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  if (n_end > 0) {
+    load_tile<D>(kslice, rbkv, 0, p.Sk, kbuf(0), wave, lane);
+    load_tile<D>(vslice, rbkv, 0, p.Sk, vbuf(0), wave, lane);
+    for (int j = 0; j < n_end; ++j) {
+      // tile j has landed (this wave's loads) and every wave is done with
+      // tile j - 1, whose buffers now take tile j + 1
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 1 < n_end) {
+        load_tile<D>(kslice, rbkv, j + 1, p.Sk, kbuf(j + 1), wave, lane);
+        load_tile<D>(vslice, rbkv, j + 1, p.Sk, vbuf(j + 1), wave, lane);
+      }
+      LDS_PTR(char) const kt = kbuf(j);
+      LDS_PTR(char) const vt = vbuf(j);
+      // S^T = K Q^T and dP^T = V dO^T for the 64 keys of the tile
+      f32x16 S[2], dP[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          S[kb][r] = 0.f;
+          dP[kb][r] = 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          S[kb] = T::mfma(read_row_frag(kt, rbase, kb, kk), qf[kk], S[kb]);
+          dP[kb] = T::mfma(read_row_frag(vt, rbase, kb, kk), dof[kk], dP[kb]);
+        }
+      }
+      if (j >= n_full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int L = lim_row - j * 64 - kb * 32 - 8 * hh;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key_of_reg(r) > L) S[kb][r] = -INFINITY;
+        }
+      }
+      // dS^T = P^T (dP^T - D), rounded to 16 bit: registers 8t'..8t'+7 are
+      // keys 16t' + 8hh + 0..7, the B operand of the next product
+      i16x8 dsf[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        f32x8 e;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float s = S[f >> 1][8 * (f & 1) + r];
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s, p.scale_log2, -lse2));
+          e[r] = pr * (dP[f >> 1][8 * (f & 1) + r] - drow);
+        }
+        dsf[f] = T::cvt(e);
+      }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[cb] = T::mfma(read_tr_frag(kt, tbase, f, cb), dsf[f], acc[cb]);
+    }
+  }
+
+  if (ok) {
+    uint16_t* row = p.dq + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x8 x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = acc[cb][4 * g + r] * p.scale;
+          x[r + 4] = 0.f;
+        }
+        const i16x8 y = T::cvt(x);
+        const u32x2 w = {(unsigned)(uint16_t)y[0] | ((unsigned)(uint16_t)y[1] << 16),
+                         (unsigned)(uint16_t)y[2] | ((unsigned)(uint16_t)y[3] << 16)};
+        *(u32x2*)(row + cb * 32 + 8 * g + 4 * hh) = w;
+      }
+  }
+}
+
+// ------------------------------------------------------------ dK, dV
+//
+// Workgroup: 4 waves x 32 keys = 128 keys of one (batch, kv head).  It walks
+// the query tiles (64 rows) that see any of its keys, for every query head
+// of the kv head's group; tile t of the walk sits in LDS buffer t & 1 (Q and
+// dO tiles double-buffered, with the rows' lse * log2(e) and D).
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  using T = Ty<DT>;
+  constexpr int CB = D / 32;
+  constexpr int KK = D / 16;
+  constexpr int TB = 64 * D * 2;
+  __shared__ __attribute__((aligned(1024))) char lds_q0[TB], lds_q1[TB], lds_o0[TB], lds_o1[TB];
+  __shared__ __attribute__((aligned(256))) float lds_l2[2][64], lds_d[2][64];
+  auto qbuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_q1 : (LDS_PTR(char))lds_q0; };
+  auto obuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_o1 : (LDS_PTR(char))lds_o0; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // key blocks in order (the first ones see the most query rows when causal)
+  const int ncol = p.B * p.Hkv;
+  const int kblk = blockIdx.x / ncol;
+  const int col = blockIdx.x % ncol;
+  const int b = col / p.Hkv;
+  const int kvh = col % p.Hkv;
+  const int k0 = kblk * 128;
+  const int kj = k0 + wave * 32 + l32;
+  const bool kok = kj < p.Sk;
+
+  // this lane's key: K and V rows as B operands (d as k)
+  i16x8 kf[KK], vf[KK];
+  {
+    const int64_t r = ((int64_t)b * p.Sk + (kok ? kj : 0)) * p.Hkv + kvh;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (kok) {
+        x = *(const u32x4*)(p.k + r * D + kk * 16 + hh * 8);
+        y = *(const u32x4*)(p.v + r * D + kk * 16 + hh * 8);
+      }
+      kf[kk] = __builtin_bit_cast(i16x8, x);
+      vf[kk] = __builtin_bit_cast(i16x8, y);
+    }
+  }
+
+  // query tiles that see a key of the block: i + off >= k0 when causal
+  const int nqt = (p.Sq + 63) / 64;
+  int qt0 = 0;
+  if (CAUSAL) {
+    const int first = k0 - p.off;
+    qt0 = first > 0 ? first / 64 : 0;
+  }
+  const int per_head = nqt > qt0 ? nqt - qt0 : 0;
+  const int steps = per_head * p.group;
+  const uint32_t rbq = (uint32_t)p.Hq * D * 2;
+
+  auto issue = [&](int t) {
+    const int h = kvh * p.group + t / per_head;
+    const int qt = qt0 + t % per_head;
+    const int64_t head0 = (int64_t)b * p.Sq * p.Hq + h;
+    load_tile<D>((const char*)(p.q + head0 * D), rbq, qt, p.Sq, qbuf(t), wave, lane);
+    load_tile<D>((const char*)(p.dout + head0 * D), rbq, qt, p.Sq, obuf(t), wave, lane);
+    // the 64 rows' lse * log2(e) (wave 0) and D (wave 1), rows clamped to
+    // Sq - 1 (rows past Sq are masked below)
+    if (wave < 2) {
+      const float* src = (wave == 0 ? p.l2 : p.dvec) + ((int64_t)b * p.Hq + h) * p.Sq;
+      const uint32_t r = (uint32_t)min(qt * 64 + lane, p.Sq - 1);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, p.Sq * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (LDS_PTR(void))(wave == 0 ? &lds_l2[t & 1][0] : &lds_d[t & 1][0]), 4, r * 4, 0, 0,
+          0);
+    }
+  };
+
+  uint32_t rbase[2], tbase[2];
+  row_frag_bases(lane, rbase);
+  tr_frag_bases(lane, tbase);
+
+  f32x16 adk[CB], adv[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      adk[cb][r] = 0.f;
+      adv[cb][r] = 0.f;
+    }
+
+  if (steps > 0) issue(0);
+  for (int t = 0; t < steps; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < steps) issue(t + 1);
+    const int qt = qt0 + t % per_head;
+    LDS_PTR(char) const qtile = qbuf(t);
+    LDS_PTR(char) const otile = obuf(t);
+    LDS_PTR(const float) const l2t = (LDS_PTR(const float)) & lds_l2[t & 1][0];
+    LDS_PTR(const float) const dtt = (LDS_PTR(const float)) & lds_d[t & 1][0];
+    // rows of this tile need masking: a causal row that does not see every
+    // key of the wave, or a row past Sq
+    const int kmax = k0 + wave * 32 + 31;
+    const bool edge = (CAUSAL && qt * 64 + p.off < kmax) || qt * 64 + 64 > p.Sq;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // S = Q K^T and dP = dO V^T: rows = 32 query rows in the sigma order,
+      // columns = this wave's 32 keys (lane)
+      f32x16 S, dP;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        S[r] = 0.f;
+        dP[r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        S = T::mfma(read_row_frag(qtile, rbase, qb, kk), kf[kk], S);
+        dP = T::mfma(read_row_frag(otile, rbase, qb, kk), vf[kk], dP);
+      }
+      // register r holds query row 32qb + key_of_reg(r) + 8hh of the tile;
+      // registers 4g .. 4g+3 are 4 consecutive rows
+      i16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        f32x8 pe, de;
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * f + g2;
+          const int row0 = 32 * qb + key_of_reg(4 * g) + 8 * hh;
+          const f32x4 l4 = *(LDS_PTR(const f32x4))(l2t + row0);
+          const f32x4 d4 = *(LDS_PTR(const f32x4))(dtt + row0);
+#pragma unroll
+          for (int r3 = 0; r3 < 4; ++r3) {
+            const int r = 4 * g + r3;
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -l4[r3]));
+            if (edge) {
+              const int qi = qt * 64 + row0 + r3;
+              if (qi >= p.Sq || (CAUSAL && kj > qi + p.off)) pr = 0.f;
+            }
+            pe[4 * g2 + r3] = pr;
+            de[4 * g2 + r3] = pr * (dP[r] - d4[r3]);
+          }
+        }
+        pf[f] = T::cvt(pe);
+        dsf[f] = T::cvt(de);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (two 16-row steps)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          adv[cb] = T::mfma(read_tr_frag(otile, tbase, 2 * qb + f, cb), pf[f], adv[cb]);
+          adk[cb] = T::mfma(read_tr_frag(qtile, tbase, 2 * qb + f, cb), dsf[f], adk[cb]);
+        }
+    }
+  }
+
+  if (kok) {
+    const int64_t r = ((int64_t)b * p.Sk + kj) * p.Hkv + kvh;
+    uint16_t* dkrow = p.dk + r * D;
+    uint16_t* dvrow = p.dv + r * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x8 x, y;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          x[r4] = adk[cb][4 * g + r4] * p.scale;
+          y[r4] = adv[cb][4 * g + r4];
+          x[r4 + 4] = 0.f;
+          y[r4 + 4] = 0.f;
+        }
+        const i16x8 xk = T::cvt(x);
+        const i16x8 yv = T::cvt(y);
+        const u32x2 wk = {(unsigned)(uint16_t)xk[0] | ((unsigned)(uint16_t)xk[1] << 16),
+                          (unsigned)(uint16_t)xk[2] | ((unsigned)(uint16_t)xk[3] << 16)};
+        const u32x2 wv = {(unsigned)(uint16_t)yv[0] | ((unsigned)(uint16_t)yv[1] << 16),
+                          (unsigned)(uint16_t)yv[2] | ((unsigned)(uint16_t)yv[3] << 16)};
+        *(u32x2*)(dkrow + cb * 32 + 8 * g + 4 * hh) = wk;
+        *(u32x2*)(dvrow + cb * 32 + 8 * g + 4 * hh) = wv;
+      }
+  }
+}
+
+// ------------------------------------------------------------ host side
+attn_status validate_bwd(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                         int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal,
+                         int dtype) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  if (!sizes_ok(B, Sq, Sk, Hq, Hkv) || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+    return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)lse) & 3u) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)Sq + Sk >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)Hq * d * 2 * 64 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31))
+    return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)Sq * 4 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
+  if (pl.grid <= 0) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+size_t bwd_workspace_bytes(int B, int Sq, int Hq) {
+  const size_t n = (size_t)B * Hq * Sq;
+  return 2 * ((n * 4 + 255) & ~(size_t)255);
+}
+
+template <int DT, int D, bool CAUSAL>
+hipError_t launch_bwd_t(const Plan& pl, const BwdParams& p, hipStream_t st) {
+  const long long rows = (long long)p.B * p.Sq * p.Hq;
+  hipLaunchKernelGGL((attn_bwd_prep_kernel<DT, D>), dim3((unsigned)((rows + 31) / 32)), dim3(256),
+                     0, st, p);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3(pl.grid), dim3(256), 0, st, p);
+  const long long kgrid = (long long)p.B * p.Hkv * ((p.Sk + 127) / 128);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)kgrid), dim3(256), 0,
+                     st, p);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_bwd_d(int d, bool causal, const Plan& pl, const BwdParams& p, hipStream_t st) {
+  if (d == 128)
+    return causal ? launch_bwd_t<DT, 128, true>(pl, p, st) : launch_bwd_t<DT, 128, false>(pl, p, st);
+  return causal ? launch_bwd_t<DT, 64, true>(pl, p, st) : launch_bwd_t<DT, 64, false>(pl, p, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_bwd_check(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int Sq, int Sk, int Hq, int Hkv, int d, float scale,
+                           int causal, int dtype) {
+  return validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Sk, Hq, Hkv, d, scale, causal,
+                      dtype);
+}
+
+attn_status attn_bwd_workspace(int B, int Sq, int Hq, size_t* bytes) {
+  if (bytes == nullptr || B < 1 || Sq < 1 || Hq < 1) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * Sq * Hq >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  *bytes = bwd_workspace_bytes(B, Sq, Hq);
+  return ATTN_OK;
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                     int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Sk, Hq, Hkv, d, scale,
+                                causal, dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = bwd_workspace_bytes(B, Sq, Hq);
+  if (workspace == nullptr || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return ATTN_ERR_INVALID_ARG;
+  const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
+  BwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)o;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.dvec = (float*)workspace;
+  p.l2 = (float*)((char*)workspace + need / 2);
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.gh = pl.gh;
+  p.hsub = p.group / pl.gh;
+  p.rows_wg = pl.rows_wg;
+  p.qtiles = pl.qtiles;
+  p.ncols = pl.ncols;
+  p.xcd_cols = pl.xcd_cols;
+  p.off = Sk - Sq;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = dtype == ATTN_DTYPE_BF16 ? launch_bwd_d<ATTN_DTYPE_BF16>(d, causal != 0, pl, p, hs)
+                                          : launch_bwd_d<ATTN_DTYPE_F16>(d, causal != 0, pl, p, hs);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

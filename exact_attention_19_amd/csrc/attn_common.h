@@ -1,0 +1,238 @@
+// Device and host pieces shared by the forward and backward attention
+// kernels for gfx950 (CDNA4): vector types, the 16-bit MFMA wrappers, the
+// key order that lets an S^T accumulator feed the next MFMA as its B operand,
+// the column-blocked LDS tile layout with its two fragment read patterns and
+// the direct-to-LDS tile load, and the query-block launch plan.
+//
+// Internal header of the library (not part of the C ABI in attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+#define LDS_PTR(T) __attribute__((address_space(3))) T*
+#define GLOBAL_PTR(T) __attribute__((address_space(1))) T*
+
+constexpr int BC = 64;              // keys per K/V tile
+constexpr float LN2 = 0.693147180559945309417f;
+
+// ---------------------------------------------------------------- dtypes
+template <int DT>
+struct Ty;
+
+template <>
+struct Ty<ATTN_DTYPE_BF16> {
+  static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ i16x8 cvt(f32x8 x) {
+    return __builtin_bit_cast(i16x8, __builtin_convertvector(x, bf16x8));
+  }
+  // acc + the sum of the 8 bf16 values of x (v_dot2_f32_bf16 against 1.0:
+  // exact products, fp32 accumulate)
+  static __device__ __forceinline__ float sum8(i16x8 x, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(
+          __builtin_bit_cast(bf16x2, (short __attribute__((ext_vector_type(2)))){x[2 * i], x[2 * i + 1]}),
+          one, acc, false);
+    return acc;
+  }
+  static constexpr bool SPLIT_P = false;
+  // The sum of the bf16-rounded P normalises O, but one rounded dominant
+  // weight can move it by 2^-9 relative: the LSE uses an fp32 sum of the
+  // unrounded P instead.
+  static constexpr bool LSE_FROM_FP32_SUM = true;
+};
+
+template <>
+struct Ty<ATTN_DTYPE_F16> {
+  static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+        __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // fp32 -> fp16, round to nearest even (v_cvt_pk_f16_f32)
+  static __device__ __forceinline__ i16x8 cvt(f32x8 x) {
+    return __builtin_bit_cast(i16x8, __builtin_convertvector(x, f16x8));
+  }
+  static __device__ __forceinline__ f32x8 widen(i16x8 x) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x8, x), f32x8);
+  }
+  // acc + the sum of the 8 fp16 values of x (v_dot2_f32_f16 against 1.0)
+  static __device__ __forceinline__ float sum8(i16x8 x, float acc) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2(
+          __builtin_bit_cast(f16x2, (short __attribute__((ext_vector_type(2)))){x[2 * i], x[2 * i + 1]}),
+          one, acc, false);
+    return acc;
+  }
+  // fp16 probabilities are carried as hi + lo halves (P = hi + lo to about
+  // 22 bits), so the P V product keeps fp32-level accuracy: the fp16
+  // tolerance leaves almost no room beside the output rounding of |O| >= 4.
+  static constexpr bool SPLIT_P = true;
+  static constexpr bool LSE_FROM_FP32_SUM = false;  // hi + lo sum is exact enough
+};
+
+// Position of accumulator row m (of a 32x32 MFMA block) in the key order.
+// m = 8g + 4h + r  ->  key 16(g>>1) + 8h + 4(g&1) + r.  With this order the
+// 8 registers 8t'..8t'+7 of the S^T accumulator hold, in lane half h, keys
+// 16t' + 8h + 0..7: exactly the B-operand layout of a 32x32x16 MFMA over the
+// 16 keys 16t'..16t'+15.
+__device__ __forceinline__ int sigma(int m) {
+  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+}
+
+// Key offset (inside a 32-key block, minus 8*h) of accumulator register
+// 4g + r: the compile-time part of sigma.
+__device__ __forceinline__ constexpr int key_of_reg(int reg) {
+  return 16 * ((reg >> 2) >> 1) + 4 * ((reg >> 2) & 1) + (reg & 3);
+}
+
+// ------------------------------------------------------------ causal range
+// K/V tiles visited by the query rows [q0, q0 + rows) (clipped to Sq): the
+// causal limit of the last row, or all of K.
+__host__ __device__ inline int block_tiles(int q0, int rows, int Sq, int Sk, int off,
+                                           bool causal) {
+  const int q_last = (q0 + rows < Sq ? q0 + rows : Sq) - 1;
+  int kv_end = Sk;
+  if (causal && q_last + off + 1 < kv_end) kv_end = q_last + off + 1;
+  return kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+}
+
+// Pieces of a row block of `tiles` tiles under a split of `chunk` tiles per
+// piece (a block that fits one piece is not split).
+__host__ __device__ inline int block_pieces(int tiles, int chunk) {
+  return (chunk > 0 && tiles > chunk) ? (tiles + chunk - 1) / chunk : 1;
+}
+
+// ------------------------------------------------------------ LDS tiles
+//
+// A 64-row tile of d columns (16-bit) is stored as d/32 column blocks; block
+// cb holds the 64 rows of those 32 columns, 64 bytes (four 16-byte chunks)
+// per row, and chunk c of row r sits at slot c ^ ((r >> 2) & 3).  Both read
+// patterns below are free of bank conflicts: the 16 rows of a row-fragment
+// read land on 16 distinct 16-byte slots of one 256-byte bank cycle, and the
+// 4 rows x 64 bytes of a transposed read of 32 lanes fill one bank cycle.
+constexpr int TILE_BLK = 64 * 64;  // bytes per column block of a tile
+
+// Row fragment (A or B operand with the d dimension as k): rows
+// 32 rb + sigma(l32) of the tile, 16-column chunk kk, lane half hh taking
+// columns 16 kk + 8 hh .. +7.  Per-lane bases for the two parities of kk.
+__device__ __forceinline__ void row_frag_bases(int lane, uint32_t (&base)[2]) {
+  const int row = sigma(lane & 31);
+  const int sw = (row >> 2) & 3;
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    base[par] = (uint32_t)(row * 64 + (((2 * par + (lane >> 5)) ^ sw) << 4));
+}
+__device__ __forceinline__ uint32_t row_frag_off(const uint32_t (&base)[2], int rb, int kk) {
+  return (uint32_t)((kk >> 1) * TILE_BLK + rb * 32 * 64) + base[kk & 1];
+}
+
+// Transposed fragment (A or B operand with the tile's rows as k):
+// ds_read_b64_tr_b16 of rows 16t + 8(g16>>1) + 4half + (s16>>2) and columns
+// 32cb + 16(g16&1) + 4(s16&3) gives lane l the 4 rows of one column; the two
+// halves together are the 8 consecutive rows 16t + 8(l>>5) .. +7 of column
+// 32cb + (l&31).
+__device__ __forceinline__ void tr_frag_bases(int lane, uint32_t (&base)[2]) {
+  const int g16 = lane >> 4;
+  const int s16 = lane & 15;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = 8 * (g16 >> 1) + 4 * half + (s16 >> 2);
+    const int cc = 16 * (g16 & 1) + 4 * (s16 & 3);
+    base[half] = (uint32_t)(row * 64 + ((((cc >> 3) ^ ((row >> 2) & 3))) << 4) + (cc & 7) * 2);
+  }
+}
+__device__ __forceinline__ i16x8 read_tr_frag(LDS_PTR(char) tile, const uint32_t (&base)[2],
+                                              int t, int cb) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_PTR(i16x4))(tile + (cb * TILE_BLK + t * 16 * 64 + base[0])));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_PTR(i16x4))(tile + (cb * TILE_BLK + t * 16 * 64 + base[1])));
+  return (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ i16x8 read_row_frag(LDS_PTR(char) tile, const uint32_t (&base)[2],
+                                               int rb, int kk) {
+  return *(LDS_PTR(const i16x8))(tile + row_frag_off(base, rb, kk));
+}
+
+// Direct global -> LDS load of tile rows [64 n, 64 n + 64) of a row-strided
+// slice (row_bytes apart, d contiguous) by the 4 waves of a workgroup: round
+// u of a wave writes LDS bytes [(4u + wave) * 1024, +1024), i.e. column block
+// (4u + wave) / 4, rows 16 ((4u + wave) % 4) + lane / 4, slot lane % 4.  Rows
+// at or past nrows re-read row nrows - 1 (finite values; the caller masks
+// them).  MUBUF loads through a buffer descriptor of the tile (64 rows x
+// row_bytes, which the host keeps below 2^31).
+template <int D>
+__device__ __forceinline__ void load_tile(const char* slice, uint32_t row_bytes, int n, int nrows,
+                                          LDS_PTR(char) buf, int wave, int lane) {
+  constexpr int CB = D / 32;
+  const int ld_row = 16 * wave + (lane >> 2);
+  const int ld_chunk = (lane & 3) ^ ((ld_row >> 2) & 3);
+  const int r = min(64 * n + ld_row, nrows - 1) - 64 * n;
+  const uint32_t off = (uint32_t)r * row_bytes + (uint32_t)ld_chunk * 16;
+  const char* tile = slice + (int64_t)n * 64 * row_bytes;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)(64 * row_bytes), 0x00020000);
+#pragma unroll
+  for (int u = 0; u < CB; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_PTR(void))(buf + (u * 4 + wave) * 1024), 16,
+                                             off, 64 * u, 0, 0);
+}
+
+// ------------------------------------------------------------ launch plan
+struct Plan {
+  int nw, qb, gh, rows_wg, qtiles, ncols, xcd_cols, grid, lds_bytes, pipelined;
+};
+
+bool sizes_ok(int B, int Sq, int Sk, int Hq, int Hkv) {
+  return B >= 1 && Sq >= 1 && Sk >= 1 && Hq >= 1 && Hkv >= 1;
+}
+
+Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
+  (void)Sk;
+  (void)causal;
+  Plan pl{};
+  pl.nw = 4;
+  const int group = Hq / Hkv;
+  int gh = 1;
+  while (gh * 2 <= pl.nw && group % (gh * 2) == 0) gh *= 2;
+  pl.gh = gh;
+  const int hsub = group / gh;
+  pl.ncols = B * Hkv * hsub;
+  pl.qb = 1;
+  pl.pipelined = 1;
+  pl.rows_wg = (pl.nw / gh) * 32;
+  const long long qt = (Sq + pl.rows_wg - 1) / pl.rows_wg;
+  pl.qtiles = qt > 0x7fffffffll ? -1 : (int)qt;
+  pl.xcd_cols = (pl.ncols % 8 == 0) ? pl.ncols / 8 : 0;
+  const long long grid = qt * pl.ncols;
+  pl.grid = (grid > 0x7fffffffll || pl.qtiles < 0) ? -1 : (int)grid;
+  pl.lds_bytes = 4 * BC * d * 2;
+  return pl;
+}
+
+}  // namespace

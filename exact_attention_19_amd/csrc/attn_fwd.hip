@@ -63,89 +63,11 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "attn_common.h"
 
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-#define LDS_PTR(T) __attribute__((address_space(3))) T*
-#define GLOBAL_PTR(T) __attribute__((address_space(1))) T*
-
-constexpr int BC = 64;              // keys per K/V tile
 constexpr float RESCALE_TAU = 8.0f; // log2 headroom before the max is moved
-constexpr float LN2 = 0.693147180559945309417f;
-
-// ---------------------------------------------------------------- dtypes
-template <int DT>
-struct Ty;
-
-template <>
-struct Ty<ATTN_DTYPE_BF16> {
-  static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
-  static __device__ __forceinline__ i16x8 cvt(f32x8 x) {
-    return __builtin_bit_cast(i16x8, __builtin_convertvector(x, bf16x8));
-  }
-  // acc + the sum of the 8 bf16 values of x (v_dot2_f32_bf16 against 1.0:
-  // exact products, fp32 accumulate)
-  static __device__ __forceinline__ float sum8(i16x8 x, float acc) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(
-          __builtin_bit_cast(bf16x2, (short __attribute__((ext_vector_type(2)))){x[2 * i], x[2 * i + 1]}),
-          one, acc, false);
-    return acc;
-  }
-  static constexpr bool SPLIT_P = false;
-  // The sum of the bf16-rounded P normalises O, but one rounded dominant
-  // weight can move it by 2^-9 relative: the LSE uses an fp32 sum of the
-  // unrounded P instead.
-  static constexpr bool LSE_FROM_FP32_SUM = true;
-};
-
-template <>
-struct Ty<ATTN_DTYPE_F16> {
-  static __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(
-        __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  // fp32 -> fp16, round to nearest even (v_cvt_pk_f16_f32)
-  static __device__ __forceinline__ i16x8 cvt(f32x8 x) {
-    return __builtin_bit_cast(i16x8, __builtin_convertvector(x, f16x8));
-  }
-  static __device__ __forceinline__ f32x8 widen(i16x8 x) {
-    return __builtin_convertvector(__builtin_bit_cast(f16x8, x), f32x8);
-  }
-  // acc + the sum of the 8 fp16 values of x (v_dot2_f32_f16 against 1.0)
-  static __device__ __forceinline__ float sum8(i16x8 x, float acc) {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2(
-          __builtin_bit_cast(f16x2, (short __attribute__((ext_vector_type(2)))){x[2 * i], x[2 * i + 1]}),
-          one, acc, false);
-    return acc;
-  }
-  // fp16 probabilities are carried as hi + lo halves (P = hi + lo to about
-  // 22 bits), so the P V product keeps fp32-level accuracy: the fp16
-  // tolerance leaves almost no room beside the output rounding of |O| >= 4.
-  static constexpr bool SPLIT_P = true;
-  static constexpr bool LSE_FROM_FP32_SUM = false;  // hi + lo sum is exact enough
-};
 
 // ------------------------------------------------------------ parameters
 struct Params {
@@ -181,36 +103,6 @@ struct Params {
   float* part_lse;
 };
 
-// K/V tiles visited by the query rows [q0, q0 + rows) (clipped to Sq): the
-// causal limit of the last row, or all of K.
-__host__ __device__ inline int block_tiles(int q0, int rows, int Sq, int Sk, int off,
-                                           bool causal) {
-  const int q_last = (q0 + rows < Sq ? q0 + rows : Sq) - 1;
-  int kv_end = Sk;
-  if (causal && q_last + off + 1 < kv_end) kv_end = q_last + off + 1;
-  return kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
-}
-
-// Pieces of a row block of `tiles` tiles under a split of `chunk` tiles per
-// piece (a block that fits one piece is not split).
-__host__ __device__ inline int block_pieces(int tiles, int chunk) {
-  return (chunk > 0 && tiles > chunk) ? (tiles + chunk - 1) / chunk : 1;
-}
-
-// Position of accumulator row m (of a 32x32 MFMA block) in the key order.
-// m = 8g + 4h + r  ->  key 16(g>>1) + 8h + 4(g&1) + r.  With this order the
-// 8 registers 8t'..8t'+7 of the S^T accumulator hold, in lane half h, keys
-// 16t' + 8h + 0..7: exactly the B-operand layout of a 32x32x16 MFMA over the
-// 16 keys 16t'..16t'+15.
-__device__ __forceinline__ int sigma(int m) {
-  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
-}
-
-// Key offset (inside a 32-key block, minus 8*h) of accumulator register
-// 4g + r: the compile-time part of sigma.
-__device__ __forceinline__ constexpr int key_of_reg(int reg) {
-  return 16 * ((reg >> 2) >> 1) + 4 * ((reg >> 2) & 1) + (reg & 3);
-}
 
 __device__ __forceinline__ float other_half_max(float x) {
   // v_permlane32_swap(x, x) returns {x of lanes 0-31 in both halves,
@@ -806,14 +698,6 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
 }
 
 // ------------------------------------------------------------ host side
-struct Plan {
-  int nw, qb, gh, rows_wg, qtiles, ncols, xcd_cols, grid, lds_bytes, pipelined;
-};
-
-bool sizes_ok(int B, int Sq, int Sk, int Hq, int Hkv) {
-  return B >= 1 && Sq >= 1 && Sk >= 1 && Hq >= 1 && Hkv >= 1;
-}
-
 attn_status validate(const void* q, const void* k, const void* v, void* o,
                      const float* lse, int B, int Sq, int Sk, int Hq, int Hkv,
                      int d, float scale, int causal, int dtype) {
@@ -856,29 +740,6 @@ attn_status validate_strides(const int64_t* st) {
     if (st[i] < 0 || (st[i] & 7) != 0) return ATTN_ERR_INVALID_ARG;
   if (st[4] * 2 * 64 >= (1ll << 31) || st[7] * 2 * 64 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   return ATTN_OK;
-}
-
-Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
-  (void)Sk;
-  (void)causal;
-  Plan pl{};
-  pl.nw = 4;
-  const int group = Hq / Hkv;
-  int gh = 1;
-  while (gh * 2 <= pl.nw && group % (gh * 2) == 0) gh *= 2;
-  pl.gh = gh;
-  const int hsub = group / gh;
-  pl.ncols = B * Hkv * hsub;
-  pl.qb = 1;
-  pl.pipelined = 1;
-  pl.rows_wg = (pl.nw / gh) * 32;
-  const long long qt = (Sq + pl.rows_wg - 1) / pl.rows_wg;
-  pl.qtiles = qt > 0x7fffffffll ? -1 : (int)qt;
-  pl.xcd_cols = (pl.ncols % 8 == 0) ? pl.ncols / 8 : 0;
-  const long long grid = qt * pl.ncols;
-  pl.grid = (grid > 0x7fffffffll || pl.qtiles < 0) ? -1 : (int)grid;
-  pl.lds_bytes = 4 * BC * d * 2;
-  return pl;
 }
 
 // Key split.  One workgroup of the attention kernel already draws most of a

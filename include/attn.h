@@ -60,7 +60,7 @@ typedef enum {
 /* F32 is accepted only for the partial outputs passed to attn_merge. */
 typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1, ATTN_DTYPE_F32 = 2 } attn_dtype;
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /*
  * attn_fwd -- fused attention forward.
@@ -241,6 +241,49 @@ attn_status attn_merge(const void* o_parts, const float* lse_parts,
 attn_status attn_merge_check(const void* o_parts, const float* lse_parts,
                              int n_parts, int parts_dtype, int B, int Sq,
                              int Hq, int d, void* o, float* lse, int dtype);
+
+/*
+ * attn_bwd -- gradients of L = sum(dO * O) with respect to q, k and v, for
+ * O = attn_fwd(q, k, v) and its LSE (the reason the forward returns the LSE:
+ * "CuTe DSL example", docstring).  The pages name FlashAttention 1 and 2 for
+ * the backward algorithm; this is that recomputation: P is rebuilt tile by
+ * tile from the scores and the LSE and never stored, with
+ *     D_i = dO_i . O_i,  dS_ij = P_ij (dO_i . v_j - D_i),
+ *     dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q.
+ * GQA gradients of a kv head sum over its query heads.  Rows that see no key
+ * (LSE = -inf) get dq = 0 and add nothing to dk, dv.
+ *
+ *   q, k, v, o, lse   the forward's inputs, output and LSE (as attn_fwd
+ *                     writes them; dense (B, S, H, d) layouts, lse
+ *                     (B, Hq, Sq) fp32)
+ *   dout              dO, (B, Sq, Hq, d), the dtype of q
+ *   dq                (B, Sq, Hq, d); written
+ *   dk, dv            (B, Sk, Hkv, d); written
+ *   B ... dtype       as for attn_fwd; d must be 64 or 128
+ *   workspace         device pointer, 256-byte aligned, of at least
+ *                     attn_bwd_workspace bytes (two fp32 values per query row)
+ *   stream            as for attn_fwd; three kernels are queued on it
+ *
+ * Every pointer but lse must be 16-byte aligned (lse 4-byte).  Each gradient
+ * element is written once (no atomics): results are deterministic.
+ * Returns ATTN_ERR_INVALID_ARG for a missing or short workspace and as
+ * attn_fwd otherwise; attn_bwd_check validates without a device call.
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, int B, int Sq, int Sk,
+                     int Hq, int Hkv, int d, float scale, int causal,
+                     int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+attn_status attn_bwd_check(const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv, int B, int Sq, int Sk,
+                           int Hq, int Hkv, int d, float scale, int causal,
+                           int dtype);
+
+/* Workspace bytes attn_bwd needs for B * Hq * Sq query rows (no device call). */
+attn_status attn_bwd_workspace(int B, int Sq, int Hq, size_t* bytes);
 
 /* Human-readable name of a status code (static string). */
 const char* attn_status_str(int status);

@@ -313,3 +313,47 @@ def test_strided_rejects_before_any_device_call():
     st = binding._strides_arg(_dense(1, 8, 8, 4, 4, 64))
     assert lib.attn_fwd_strided(A, A, A, A, None, 1, 8, 8, 4, 4, 64, ctypes.c_float(1.0), 0,
                                 ATTN_DTYPE_F16, st, -1, None, 0, None) == ATTN_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------- backward
+
+BG = dict(B=2, Sq=100, Sk=120, Hq=8, Hkv=2, d=128, scale=0.125, causal=1, dtype=ATTN_DTYPE_BF16)
+
+
+def _bcheck(ptrs=None, **over):
+    a = dict(BG, **over)
+    p = ptrs or [A + 0x1000 * i for i in range(9)]
+    p[4] = p[4] if ptrs else A + 0x4000  # lse
+    return binding.attn_bwd_check(*p, a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hkv"], a["d"],
+                                  a["scale"], a["causal"], a["dtype"])
+
+
+def test_bwd_validation():
+    _lib()
+    assert _bcheck() == ATTN_OK
+    assert _bcheck(d=64, dtype=ATTN_DTYPE_F16, causal=0) == ATTN_OK
+    for i in range(9):
+        p = [A + 0x1000 * j for j in range(9)]
+        p[i] = None
+        assert _bcheck(p) == ATTN_ERR_INVALID_ARG, i
+        if i != 4:
+            p[i] = A + 0x1000 * i + 8  # 16-byte alignment (lse: 4-byte)
+            assert _bcheck(p) == ATTN_ERR_INVALID_ARG, i
+    for over in (dict(Hq=7), dict(B=0), dict(Sk=0), dict(scale=0.0), dict(causal=3)):
+        assert _bcheck(**over) == ATTN_ERR_INVALID_ARG, over
+    for over in (dict(d=96), dict(d=256), dict(dtype=2)):
+        assert _bcheck(**over) == ATTN_ERR_UNSUPPORTED, over
+
+
+def test_bwd_workspace_and_early_rejection():
+    lib = _lib()
+    n = 2 * 8 * 100
+    assert binding.attn_bwd_workspace(2, 100, 8) == 2 * (-(-n * 4 // 256) * 256)
+    with pytest.raises(binding.AttnError):
+        binding.attn_bwd_workspace(0, 100, 8)
+    p = [A + 0x1000 * i for i in range(9)]
+    need = binding.attn_bwd_workspace(2, 100, 8)
+    args = (*p, 2, 100, 120, 8, 2, 128, ctypes.c_float(0.125), 1, ATTN_DTYPE_BF16)
+    assert lib.attn_bwd(*args, None, need, None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_bwd(*args, 0x200000, need - 4, None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_bwd(*args, 0x200010, need, None) == ATTN_ERR_INVALID_ARG

@@ -1,0 +1,196 @@
+"""GPU parity of the backward pass (attn_bwd, through the C ABI) against the
+fp64 oracle's gradients.
+
+Bound.  No page fixes a precision for gradients, so each element's bound is
+derived from the arithmetic (and written out below): with u the unit
+roundoff of the 16-bit type (2^-8 bf16, 2^-11 fp16),
+  P       is recomputed in fp32 from the forward's LSE: relative error
+          e_P = |dLSE| + 2^-20 (the measured LSE error of the same forward
+          call, plus exp2 and fp32 rounding);
+  D_i     = dO_i . O_i uses the forward's 16-bit O: |dD_i| =
+          |dO_i . (O_gpu - O)| + d 2^-24 |dO_i| . |O_i|;
+  dS_ij   = P (dP - D), rounded to 16 bit once: |d dS| <= e_P |dS| +
+          P |dD_i| + P d 2^-24 |dO_i| . |v_j| + u |dS| + t/2, with t the
+          smallest spacing of the format (2^-24 for fp16, whose subnormals
+          tiny dS and P values fall among);
+  dV_j    = sum_i round16(P_ij) dO_i: |d dV_j| <= sum_i ((u + e_P) P_ij +
+          t/2) |dO_i|;
+  dQ, dK  = scale sums of the rounded dS times 16-bit K or Q:
+          |d dQ_i| <= scale sum_j |d dS_ij| |k_j|, the same for dK;
+plus fp32 accumulation (n 2^-24 of the sums of magnitudes) and the rounding
+of the result to 16 bit (u |x|, and half the smallest spacing of the format
+for results in the fp16 subnormal range).  The test allows twice that bound.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attn_bwd_oracle, attn_fwd_oracle
+from exact_attention_19_amd.workloads import WORKLOADS, Workload, make_inputs
+from parity_common import _say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_attention_19_amd import load_library
+    load_library()  # fail loudly if the HIP library is missing
+
+
+U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+TINY = {"bf16": 2.0 ** -133, "f16": 2.0 ** -24}
+
+
+def _f64(t):
+    return t.detach().to("cpu").to(torch.float64)
+
+
+def error_bounds(q, k, v, do, o_gpu, lse_gpu, scale, causal, dt):
+    """Elementwise bounds (dq, dk, dv) as derived in the module docstring,
+    from fp64 quantities computed here with torch on the CPU."""
+    u = U[dt]
+    acc = 2.0 ** -24
+    qd, kd, vd, dod, og = (_f64(t) for t in (q, k, v, do, o_gpu))
+    B, Sq, Hq, d = qd.shape
+    Sk, Hkv = kd.shape[1], kd.shape[2]
+    g = Hq // Hkv
+    qh = qd.permute(0, 2, 1, 3)                                   # (B, Hq, Sq, d)
+    kh = kd.repeat_interleave(g, dim=2).permute(0, 2, 1, 3)       # (B, Hq, Sk, d)
+    vh = vd.repeat_interleave(g, dim=2).permute(0, 2, 1, 3)
+    doh = dod.permute(0, 2, 1, 3)
+    s = torch.matmul(qh, kh.transpose(-1, -2)) * scale
+    if causal:
+        i = torch.arange(Sq)[:, None]
+        j = torch.arange(Sk)[None, :]
+        s = s.masked_fill(j > i + (Sk - Sq), float("-inf"))
+    m = s.amax(dim=-1, keepdim=True)
+    m = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
+    e = torch.exp(s - m)
+    z = e.sum(dim=-1, keepdim=True)
+    p = torch.where(z > 0, e / torch.where(z > 0, z, torch.ones_like(z)), torch.zeros_like(e))
+    lse_ref = torch.where(z[..., 0] > 0, m[..., 0] + torch.log(torch.where(z[..., 0] > 0, z[..., 0], torch.ones_like(z[..., 0]))),
+                          torch.full_like(z[..., 0], float("-inf")))
+    o = torch.matmul(p, vh)
+    dp = torch.matmul(doh, vh.transpose(-1, -2))
+    dD = (doh * (og.permute(0, 2, 1, 3) - o)).sum(-1).abs() \
+        + d * acc * (doh.abs() * o.abs()).sum(-1)
+    D = (p * dp).sum(-1)
+    ds = p * (dp - D[..., None])
+    fin = torch.isfinite(lse_ref)
+    lg = _f64(lse_gpu)
+    dl = (lg[fin] - lse_ref[fin]).abs().max().item() if fin.any() else 0.0
+    e_p = dl + 2.0 ** -20
+    dds = e_p * ds.abs() + p * dD[..., None] \
+        + p * d * acc * torch.matmul(doh.abs(), vh.abs().transpose(-1, -2)) + u * ds.abs()
+    # rounding to 16 bit: relative u, or half the smallest spacing where the
+    # value falls among the fp16 subnormals
+    dds = dds + acc * ds.abs() + 0.5 * TINY[dt]
+    # dV: (B, Hq, Sk, d) summed over the query heads of each kv head
+    bv = torch.matmul(p.transpose(-1, -2), doh.abs()) * (u + e_p + Sq * acc) \
+        + 0.5 * TINY[dt] * doh.abs().sum(dim=-2, keepdim=True)
+    bq = scale * torch.matmul(dds, kh.abs()) + scale * Sk * acc * torch.matmul(ds.abs(), kh.abs())
+    bk = scale * torch.matmul(dds.transpose(-1, -2), qh.abs()) \
+        + scale * Sq * acc * torch.matmul(ds.abs().transpose(-1, -2), qh.abs())
+    bv = bv.reshape(B, Hkv, g, Sk, d).sum(2).permute(0, 2, 1, 3)
+    bk = bk.reshape(B, Hkv, g, Sk, d).sum(2).permute(0, 2, 1, 3)
+    bq = bq.permute(0, 2, 1, 3)
+    return bq.numpy(), bk.numpy(), bv.numpy()
+
+
+def _run(w: Workload, seed=0, dout_scale=1.0):
+    from exact_attention_19_amd import attn_bwd, attn_fwd
+    q, k, v = make_inputs(w, seed=seed)
+    gen = torch.Generator().manual_seed(seed + 1000)
+    do = (dout_scale * torch.randn(q.shape, generator=gen)).to(q.dtype)
+    qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    _say(f"[gpu] attn_bwd {w.name} B={w.B} Sq={w.Sq} Sk={w.Sk} Hq={w.Hq} Hkv={w.Hkv} "
+         f"d={w.d} {w.dtype} causal={w.causal}")
+    o, lse = attn_fwd(qg, kg, vg, scale=w.scale, causal=w.causal)
+    dq, dk, dv = attn_bwd(qg, kg, vg, o, lse, dog, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    return q, k, v, do, o.cpu(), lse.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _check(w, q, k, v, do, o, lse, dq, dk, dv):
+    rq, rk, rv = attn_bwd_oracle(q, k, v, do, w.scale, w.causal)
+    bq, bk, bv = error_bounds(q, k, v, do, o, lse, w.scale, w.causal, w.dtype)
+    u = U[w.dtype]
+    worst = {}
+    for name, got, ref, bound in (("dq", dq, rq, bq), ("dk", dk, rk, bk), ("dv", dv, rv, bv)):
+        gd = got.double().numpy()
+        assert np.isfinite(gd).all(), f"{name} not finite"
+        # + half the format's smallest spacing (fp16 subnormals: 2^-24)
+        allowed = 2.0 * (bound + u * np.abs(ref)) + 0.5 * TINY[w.dtype]
+        diff = np.abs(gd - ref)
+        ratio = diff / allowed
+        at = np.unravel_index(np.argmax(ratio), ratio.shape)
+        worst[name] = (float(diff.max()), float(ratio.max()))
+        assert np.all(diff <= allowed), (
+            f"{w.name} {name}: |d| = {diff[at]:.3e} at {at} > bound {allowed[at]:.3e} "
+            f"(ref {ref[at]:.4e}, got {gd[at]:.4e}); max|d| = {diff.max():.3e}")
+    _say(f"{w.name}: " + ", ".join(f"{n} max|d| {a:.2e} (bound use {r:.2f})"
+                                    for n, (a, r) in worst.items()))
+
+
+def _cases():
+    cases = []
+    for dt in ("bf16", "f16"):
+        cases += [
+            Workload(f"bwd_mha_nc_{dt}", 1, 2, 2, 128, 128, 64, dt, False, 0.125),
+            Workload(f"bwd_causal_sq_{dt}", 2, 4, 4, 257, 257, 128, dt, True, 1 / math.sqrt(128)),
+            Workload(f"bwd_causal_off_{dt}", 1, 8, 2, 200, 333, 128, dt, True, 1 / math.sqrt(128)),
+            Workload(f"bwd_causal_empty_rows_{dt}", 1, 4, 1, 333, 200, 64, dt, True, 0.2),
+            Workload(f"bwd_gqa_nc_{dt}", 2, 8, 2, 190, 450, 128, dt, False, 1 / math.sqrt(128)),
+        ]
+    cases += [Workload("bwd_scale1_f16", 1, 4, 4, 300, 300, 128, "f16", True, 1.0),
+              Workload("bwd_one_row_bf16", 2, 8, 4, 1, 700, 128, "bf16", True, 1 / math.sqrt(128)),
+              Workload("bwd_one_key_bf16", 1, 4, 2, 100, 1, 64, "bf16", False, 0.3)]
+    return cases
+
+
+@pytest.mark.parametrize("w", _cases(), ids=lambda w: w.name)
+def test_bwd_parity(w):
+    _check(w, *_run(w))
+
+
+def test_bwd_1k_causal_workload():
+    """The 2 x 1024 causal fp16 MHA workload, every gradient element."""
+    w = WORKLOADS["mha_causal_f16_b2_h16_s1024_d128"]
+    _check(w, *_run(w))
+
+
+def test_bwd_deterministic():
+    from exact_attention_19_amd import attn_bwd, attn_fwd
+    w = Workload("bwd_det", 1, 8, 2, 333, 517, 128, "bf16", True, 0.1)
+    q, k, v = (t.cuda() for t in make_inputs(w, seed=3))
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(4)).to(q.dtype).cuda()
+    o, lse = attn_fwd(q, k, v, scale=w.scale, causal=True)
+    a = attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True)
+    b = attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_no_writes_outside_outputs():
+    from exact_attention_19_amd import attn_bwd, attn_fwd
+    w = Workload("bwd_canary", 1, 4, 2, 150, 170, 64, "f16", True, 0.2)
+    q, k, v = (t.cuda() for t in make_inputs(w, seed=5))
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(6)).to(q.dtype).cuda()
+    o, lse = attn_fwd(q, k, v, scale=w.scale, causal=True)
+    pad = 4096
+    bufs = []
+    for ref in (q, k, v):
+        n = ref.numel()
+        buf = torch.full((n + 2 * pad,), 1234.0, dtype=ref.dtype, device="cuda")
+        bufs.append((buf, buf[pad:pad + n].view(ref.shape), n))
+    attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True,
+             dq=bufs[0][1], dk=bufs[1][1], dv=bufs[2][1])
+    torch.cuda.synchronize()
+    for buf, _, n in bufs:
+        assert torch.all(buf[:pad] == 1234.0) and torch.all(buf[pad + n:] == 1234.0)
