@@ -108,6 +108,14 @@ def cpu_baseline(w, q, k, v, budget_s: float = 15.0):
             "seconds": round(dt, 2)}
 
 
+def bwd_bytes(w) -> int:
+    """Algorithmic bytes of the backward pass: Q, O, dO, dQ (query side) and
+    K, V, dK, dV (key side) once each at 2 bytes per element, plus the LSE."""
+    q = w.B * w.Sq * w.Hq * w.d * 2
+    kv = w.B * w.Sk * w.Hkv * w.d * 2
+    return 4 * q + 4 * kv + w.B * w.Hq * w.Sq * 4
+
+
 def board_power():
     """Socket power and core clocks as amd-smi reports them (text), or None."""
     import subprocess
@@ -214,6 +222,10 @@ def main():
     ap.add_argument("--kv-split", type=int, default=0,
                     help="key split of attn_fwd_split: 0 = the library's choice, "
                          "1 = none, N = at most N pieces per query block")
+    ap.add_argument("--backward", action="store_true",
+                    help="time attn_bwd (dQ, dK, dV from O, LSE and a seeded dO) instead of "
+                         "the forward; FLOPs are 2.5x the forward's (five products of the "
+                         "forward's two-product size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--board-sample", action="store_true",
                     help="after the timed steps, keep stepping for about 3 s while "
@@ -238,7 +250,8 @@ def main():
         return
 
     import torch
-    from exact_attention_19_amd import (attn_fwd_plan, attn_fwd_split, attn_fwd_split_plan,
+    from exact_attention_19_amd import (attn_bwd, attn_bwd_workspace, attn_fwd, attn_fwd_plan,
+                                        attn_fwd_split, attn_fwd_split_plan,
                                         attn_fwd_split_workspace, load_library)
     from exact_attention_19_amd.binding import ATTN_DTYPE_BF16, ATTN_DTYPE_F16
     from exact_attention_19_amd.workloads import WORKLOADS, input_digest, make_inputs
@@ -262,6 +275,17 @@ def main():
         attn_fwd_split(q, k, v, scale=w.scale, causal=w.causal, kv_split=args.kv_split,
                        out=o, lse=lse, workspace=ws, stream=stream)
 
+    if args.backward:
+        attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+        gen = torch.Generator().manual_seed(1)
+        dout = torch.randn(q.shape, generator=gen).to(q.dtype).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = torch.empty(attn_bwd_workspace(w.B, w.Sq, w.Hq), dtype=torch.uint8, device=dev)
+
+        def step():  # noqa: F811 (the backward step replaces the forward one)
+            attn_bwd(q, k, v, o, lse, dout, scale=w.scale, causal=w.causal, dq=dq, dk=dk,
+                     dv=dv, workspace=bws, stream=stream)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -283,14 +307,14 @@ def main():
     kern_med_s = sorted(kern_ms)[len(kern_ms) // 2] / 1e3
     ms_per_step = wall / args.steps * 1e3
 
-    flops = w.metric_flops()
+    flops = w.metric_flops() * (2.5 if args.backward else 1.0)
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / kern_avg_s / 1e12
     plan = attn_fwd_plan(*shape)
     # the bound: arithmetic intensity (exact FLOPs per algorithmic byte)
     # against the ridge point of the two MI355X peaks
     ridge = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if w.exact_flops() / w.algorithmic_bytes() >= ridge:
+    if args.backward or w.exact_flops() / w.algorithmic_bytes() >= ridge:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4)}
     else:
@@ -313,7 +337,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) / outlier recipe, resident in HBM)",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+        "config": {"workload": w.name, "pass": "backward" if args.backward else "forward",
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Sq": w.Sq, "Sk": w.Sk, "d": w.d, "causal": w.causal,
                    "scale": w.scale, "input_sha256": digest[:16]},
         "pct_of_peak": round(100.0 * value / PEAK_MFMA_TFLOPS, 2),
@@ -321,13 +346,15 @@ def main():
             "traffic": measured_traffic(w.name),
             # with a key split the step is two launches (attention, merge):
             # the event pair then times both
-            "launches_per_step": 2 if split["keys_per_piece"] > 0 else 1,
+            "launches_per_step": 3 if args.backward else (2 if split["keys_per_piece"] > 0 else 1),
             "kernel_avg_us": round(kern_avg_s * 1e6, 2),
             "kernel_min_us": round(kern_min_s * 1e6, 2),
             "kernel_median_us": round(kern_med_s * 1e6, 2),
             "flops_per_launch": flops,
-            "exact_visible_flops_per_launch": w.exact_flops(),
-            "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
+            "exact_visible_flops_per_launch": w.exact_flops() * (2.5 if args.backward else 1.0),
+            # backward: Q, K, V, O, dO and the LSE read, dQ, dK, dV written
+            "algorithmic_bytes_per_launch": (bwd_bytes(w) if args.backward
+                                             else w.algorithmic_bytes()),
         }),
         "launch": plan,
         "split": dict(split, kv_split_arg=args.kv_split, workspace_bytes=ws_bytes),
@@ -341,7 +368,7 @@ def main():
                 step()
             torch.cuda.synchronize()
         result["device"]["board_under_load"] = board.loaded()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.backward:
         result["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu)
     print(json.dumps(result), flush=True)
 
