@@ -42,7 +42,8 @@ DEFAULT_WORKLOAD = "gqa4_causal_bf16_b1_hq32_hkv8_s8192_d128"
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for p in ("exact_attention_19_amd/csrc/attn_fwd.hip", "include/attn.h"):
+    for p in ("exact_attention_19_amd/csrc/attn_fwd.hip",
+              "exact_attention_19_amd/csrc/attn_common.h", "include/attn.h"):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
