@@ -205,10 +205,19 @@ def copy_probe(mib: int, steps: int):
     n = mib << 20
     src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
     for _ in range(steps):
         dst.copy_(src)
+    e.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes": n, "launches": steps}), flush=True)
+    ms = s.elapsed_time(e) / steps
+    # read n and write n bytes per launch
+    print(json.dumps({"copy_probe_bytes": n, "launches": steps + 1, "ms_per_copy": round(ms, 4),
+                      "read_plus_write_GBps": round(2 * n / ms / 1e6, 1)}), flush=True)
 
 
 def main():

@@ -99,12 +99,12 @@ def _dtype_code(t, allow_f32: bool = False) -> int:
 
 def attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype_code) -> dict:
     """The launch attn_fwd would make (no device call)."""
-    out = (ctypes.c_int * 9)()
-    st = load_library().attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), dtype_code, out, 9)
+    out = (ctypes.c_int * 10)()
+    st = load_library().attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), dtype_code, out, 10)
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_plan")
     keys = ("grid", "threads", "rows_per_wg", "keys_per_tile", "heads_per_wg",
-            "rows_per_wave", "lds_bytes", "xcd_ordered", "pipelined")
+            "rows_per_wave", "lds_bytes", "xcd_ordered", "pipelined", "decode")
     return dict(zip(keys, list(out)))
 
 

@@ -13,6 +13,35 @@
 
 #include "attn.h"
 
+// ------------------------------------------------------------ decode path
+// Arguments of the decode kernel (attn_decode.hip): g * Sq <= 32 query rows
+// per kv head, all in one wave.  In a named namespace: the launcher is
+// shared between translation units.
+namespace attn_detail {
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int B, Sq, Sk, Hq, Hkv;
+  int piece_tiles;   // 32-key tiles per piece
+  long long grid;    // B * Hkv * pieces
+  float scale_log2;
+  float* part_o;     // pieces > 1: [piece][b][i][h][d] fp32, else null
+  float* part_lse;   // pieces > 1: [piece][b][h][i]
+};
+
+// Launch of the decode kernel (defined in attn_decode.hip).
+__attribute__((visibility("hidden"))) hipError_t launch_decode(int dtype, int d, int causal,
+                                                               const DecodeArgs& a,
+                                                               hipStream_t st);
+}  // namespace attn_detail
+
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -108,6 +137,16 @@ __device__ __forceinline__ int sigma(int m) {
 // 4g + r: the compile-time part of sigma.
 __device__ __forceinline__ constexpr int key_of_reg(int reg) {
   return 16 * ((reg >> 2) >> 1) + 4 * ((reg >> 2) & 1) + (reg & 3);
+}
+
+// Max over the lane pair (l, l + 32): v_permlane32_swap(x, x) returns {x of
+// lanes 0-31 in both halves, x of lanes 32-63 in both halves}.
+__device__ __forceinline__ float other_half_max(float x) {
+  // v_permlane32_swap(x, x) returns {x of lanes 0-31 in both halves,
+  // x of lanes 32-63 in both halves}: their max is the max over the lane pair.
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                            __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // ------------------------------------------------------------ causal range
@@ -235,4 +274,54 @@ Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
   return pl;
 }
 
+using attn_detail::DecodeArgs;
+using attn_detail::launch_decode;
+
+// The decode kernel takes shapes whose query rows per kv head fit one wave
+// (g * Sq <= 32) at d = 64 or 128.
+inline bool decode_eligible(int Sq, int Hq, int Hkv, int d) {
+  return (long long)(Hq / Hkv) * Sq <= 32 && (d == 64 || d == 128);
+}
+
+struct DecodePlan {
+  int pieces;
+  int piece_tiles;
+  long long grid;
+  size_t lse_offset;  // workspace: part_o then part_lse (256-byte aligned)
+  size_t ws_bytes;
+};
+
+// Pieces per (batch, kv head): kv_split 1 = none; k > 1 = k; 0 = the
+// library's choice.  Measured on MI355X: one decode workgroup per CU already
+// streams K and V at the chip's practical rate (5.5 TB/s with 256 of them; a
+// second workgroup per CU, or cutting into more pieces, was slower), and a
+// piece pays a fixed start-up and merge cost, so the choice splits only when
+// there are fewer than 128 (batch, kv head) pairs, into about 128 workgroups
+// with at least 32 tiles (8 per wave) each.
+inline DecodePlan make_decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int kv_split) {
+  DecodePlan dp{};
+  const int ntiles = (Sk + 31) / 32;
+  const long long cols = (long long)B * Hkv;
+  long long pieces = 1;
+  if (kv_split == 0) {
+    if (cols < 128) pieces = (128 + cols - 1) / cols;
+    const long long most = ntiles / 32 > 1 ? ntiles / 32 : 1;
+    if (pieces > most) pieces = most;
+  } else if (kv_split > 1) {
+    pieces = kv_split;
+  }
+  if (pieces > ntiles) pieces = ntiles;
+  dp.piece_tiles = (int)((ntiles + pieces - 1) / pieces);
+  dp.pieces = (ntiles + dp.piece_tiles - 1) / dp.piece_tiles;
+  dp.grid = cols * dp.pieces;
+  if (dp.pieces > 1) {
+    const size_t rows = (size_t)B * Sq * Hq;
+    dp.lse_offset = ((size_t)dp.pieces * rows * d * 4 + 255) & ~(size_t)255;
+    dp.ws_bytes = dp.lse_offset + (size_t)dp.pieces * rows * 4;
+  }
+  if (dp.grid > 0x7fffffffll) dp.grid = -1;
+  return dp;
+}
+
 }  // namespace
+

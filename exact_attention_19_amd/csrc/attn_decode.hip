@@ -1,0 +1,347 @@
+// Decode-shaped attention forward for AMD Instinct MI355X (gfx950): a few new
+// query rows per sequence (g * Sq <= 32 rows per kv head, g = Hq / Hkv) over
+// a long K/V cache.
+//
+// The MiniPaged-Qwen page (section 19) sets decode apart from prefill: the
+// query side has almost no parallelism and the work becomes reading the K/V
+// cache.  The computation is the forward's (online softmax over K/V tiles,
+// personal-notes page section "Online Softmax"), mapped for that regime:
+//
+// * All g * Sq query rows of one (batch, kv head) -- every query head of the
+//   GQA group and every new token -- are the 32 rows of ONE wave: row r is
+//   query head h0 + r / Sq, token r % Sq.  The prefill kernel would give each
+//   query head its own 32-row wave, mostly empty.
+// * The 4 waves of a workgroup walk different 32-key tiles of the key range
+//   (tile w, w + 4, ...), each with its own softmax state, and the states are
+//   merged through LDS at the end (the online-softmax rescale).  A key range
+//   can further be cut into pieces over workgroups, merged by the merge
+//   kernel, when (batch, kv head) pairs are too few to fill the GPU.
+// * The work is bound by reading K and V: K rows go straight from global
+//   memory into registers as the A operand of S^T = K Q^T (lane l loads key
+//   row sigma(l & 31)); V tiles go to LDS by buffer DMA for the transposed
+//   reads of O^T += V^T P^T.  Each wave keeps the next tile's K and V in
+//   flight while it computes the current one; two workgroups per CU.
+//
+// Rounding and normalisation follow the prefill kernel: P rounded to the
+// input type before P V (fp16 as hi + lo), O normalised by the sum of the
+// rounded P, LSE from the fp32 sum (bf16) or the hi + lo sum (fp16).
+
+#include "attn_common.h"
+
+namespace {
+
+constexpr int DBC = 32;                    // keys per tile
+constexpr float DEC_RESCALE_TAU = 8.0f;    // lazy max update, as the prefill kernel
+
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
+  using T = Ty<DT>;
+  constexpr int CB = D / 32;
+  constexpr int KK = D / 16;
+  constexpr int VBLK = DBC * 64;           // bytes per 32-column block of a V tile
+  constexpr int VTB = DBC * D * 2;         // bytes per V tile
+  // per wave: two V tile stages; reused at the end for the merge (4 x 32
+  // rows x D floats = exactly the same size)
+  __shared__ __attribute__((aligned(1024))) char lds_v[4][2][VTB];
+  __shared__ float lds_m[4][32], lds_lr[4][32], lds_lf[4][32];
+  static_assert(4 * 2 * VTB == 4 * 32 * D * 4, "merge area = tile area");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int ncol = p.B * p.Hkv;
+  const int col = blockIdx.x % ncol;
+  const int piece = blockIdx.x / ncol;
+  const int b = col / p.Hkv;
+  const int kvh = col % p.Hkv;
+  const int g = p.Hq / p.Hkv;
+  const int M = g * p.Sq;
+
+  // this lane's query row
+  const int r = l32;
+  const bool rok = r < M;
+  const int hq = kvh * g + (rok ? r / p.Sq : 0);
+  const int qi = rok ? r % p.Sq : 0;
+  i16x8 qf[KK];
+  {
+    const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)qi * p.q_ss + (int64_t)hq * p.q_sh;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (rok) x = *(const u32x4*)(qrow + kk * 16 + hh * 8);
+      qf[kk] = __builtin_bit_cast(i16x8, x);
+    }
+  }
+  // keys this row sees: j < Sk, and j <= qi + Sk - Sq when causal
+  int lim = p.Sk - 1;
+  if (CAUSAL) lim = min(lim, qi + p.Sk - p.Sq);
+  if (!rok) lim = -1;
+
+  // the piece's tiles [t_lo, t_hi); this wave takes t_lo + wave, + 4, ...
+  const int ntiles = (p.Sk + DBC - 1) / DBC;
+  const int t_lo = piece * p.piece_tiles;
+  const int t_hi = min(ntiles, t_lo + p.piece_tiles);
+  // last key seen by any row of the group (tiles past it are skipped)
+  int kv_last = p.Sk - 1;
+  if (CAUSAL) kv_last = min(kv_last, p.Sq - 1 + p.Sk - p.Sq);
+  const int t_end = min(t_hi, kv_last / DBC + 1);
+
+  const char* kbase = (const char*)(p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh);
+  const char* vbase = (const char*)(p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh);
+  const uint32_t rbk = (uint32_t)(p.k_ss * 2);
+  const uint32_t rbv = (uint32_t)(p.v_ss * 2);
+
+  // K fragments of tile n: key row sigma(l32) of the tile, chunks kk
+  auto load_k = [&](int n, i16x8 (&kf)[KK]) {
+    const int key = min(n * DBC + sigma(l32), p.Sk - 1);
+    const uint16_t* krow = (const uint16_t*)(kbase + (int64_t)key * rbk);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      kf[kk] = __builtin_bit_cast(i16x8, *(const u32x4*)(krow + kk * 16 + hh * 8));
+  };
+  // V tile n -> this wave's LDS stage: column-blocked, 32 rows x 64 bytes per
+  // block, chunk c of row r at slot c ^ ((r >> 2) & 3); round u covers block
+  // u >> 1, rows 16 (u & 1) + lane / 4
+  auto load_v = [&](int n, LDS_PTR(char) buf) {
+    const int row = lane >> 2;
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    const char* tile = vbase + (int64_t)n * DBC * rbv;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int rr = min(n * DBC + 16 * h2 + row, p.Sk - 1) - n * DBC;
+      const uint32_t off = (uint32_t)rr * rbv + (uint32_t)chunk * 16;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)(DBC * rbv), 0x00020000);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (LDS_PTR(void))(buf + cb * VBLK + h2 * 1024), 16, off, 64 * cb, 0, 0);
+    }
+  };
+  // transposed V fragment (A operand of O^T += V^T P^T): rows 16t + 8hh ..
+  // +7 of column 32cb + l32
+  uint32_t tb[2];
+  {
+    const int g16 = lane >> 4;
+    const int s16 = lane & 15;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 8 * (g16 >> 1) + 4 * half + (s16 >> 2);
+      const int cc = 16 * (g16 & 1) + 4 * (s16 & 3);
+      tb[half] = (uint32_t)(row * 64 + ((((cc >> 3) ^ ((row >> 2) & 3))) << 4) + (cc & 7) * 2);
+    }
+  }
+  auto read_vt = [&](LDS_PTR(char) buf, int t, int cb) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_PTR(i16x4))(buf + (cb * VBLK + t * 16 * 64 + tb[0])));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_PTR(i16x4))(buf + (cb * VBLK + t * 16 * 64 + tb[1])));
+    return (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+
+  f32x16 acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[cb][q] = 0.f;
+  float m_run = -1e30f, l_rnd = 0.f, l_fp32 = 0.f;
+
+  LDS_PTR(char) const vb0 = (LDS_PTR(char))lds_v[wave][0];
+  LDS_PTR(char) const vb1 = (LDS_PTR(char))lds_v[wave][1];
+  int n = t_lo + wave;
+  i16x8 kA[KK], kB[KK];
+  if (n < t_end) {
+    load_k(n, kA);
+    load_v(n, vb0);
+  }
+  // one tile: kf holds K(n), vbuf V(n); the next tile's loads are in flight
+  auto tile = [&](int nn, const i16x8 (&kf)[KK], LDS_PTR(char) vbuf) {
+    f32x16 S;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) S[q] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) S = T::mfma(kf[kk], qf[kk], S);
+    // mask keys past this row's limit (ragged end, causal tail)
+    if (nn * DBC + DBC - 1 > min(lim, p.Sk - 1) || !rok) {
+      const int L = lim - nn * DBC - 8 * hh;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (key_of_reg(q) > L) S[q] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mx = fmaxf(mx, S[q]);
+    mx = other_half_max(mx) * p.scale_log2;
+    const bool resc = __builtin_amdgcn_ballot_w64(mx > m_run + DEC_RESCALE_TAU) != 0;
+    float alpha = 1.f;
+    if (resc) {
+      const float m_new = fmaxf(m_run, mx);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+    }
+    float ls = 0.f, lr = 0.f;
+    i16x8 ph[2], pl[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      f32x8 e;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        e[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * f + q], p.scale_log2, -m_run));
+        ls += e[q];
+      }
+      ph[f] = T::cvt(e);
+      lr = T::sum8(ph[f], lr);
+      if constexpr (T::SPLIT_P) {
+        pl[f] = T::cvt(e - T::widen(ph[f]));
+        lr = T::sum8(pl[f], lr);
+      }
+    }
+    if (resc) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[cb][q] *= alpha;
+    }
+    l_rnd = l_rnd * alpha + lr;
+    l_fp32 = l_fp32 * alpha + ls;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const i16x8 vf = read_vt(vbuf, t, cb);
+        acc[cb] = T::mfma(vf, ph[t], acc[cb]);
+        if constexpr (T::SPLIT_P) acc[cb] = T::mfma(vf, pl[t], acc[cb]);
+      }
+  };
+  // s_waitcnt immediate for vmcnt(KK + 2 CB), expcnt and lgkmcnt untouched
+  // (gfx9 encoding: vmcnt bits 3:0 and 15:14)
+  constexpr int VMN = KK + 2 * CB;
+  constexpr int VM_NEXT = 0x0F70 | (VMN & 15) | ((VMN >> 4) << 14);
+  static_assert(VMN < 64, "vmcnt range");
+  // tiles n, n + 4, ... alternate between the (kA, stage 0) and (kB,
+  // stage 1) register/LDS sets, so the loop body is unrolled by two
+  for (; n < t_end; n += 8) {
+    if (n + 4 < t_end) {
+      load_k(n + 4, kB);
+      load_v(n + 4, vb1);
+    }
+    // K(n) and V(n) (issued one tile earlier) have landed: wait for all but
+    // the loads just issued
+    if (n + 4 < t_end)
+      __builtin_amdgcn_s_waitcnt(VM_NEXT);  // vmcnt(KK + 2 CB)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    tile(n, kA, vb0);
+    if (n + 4 >= t_end) break;
+    if (n + 8 < t_end) {
+      load_k(n + 8, kA);
+      load_v(n + 8, vb0);
+      __builtin_amdgcn_s_waitcnt(VM_NEXT);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    tile(n + 4, kB, vb1);
+  }
+
+  // ---- merge the 4 waves' states through LDS
+  auto pair_sum = [](float x) {
+    auto rr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                               false);
+    return __uint_as_float(rr[0]) + __uint_as_float(rr[1]);
+  };
+  const float lr_tot = pair_sum(l_rnd);
+  const float lf_tot = T::LSE_FROM_FP32_SUM ? pair_sum(l_fp32) : lr_tot;
+  __syncthreads();  // every wave is done with its V stages: reuse them
+  float* mo = (float*)&lds_v[0][0][0];  // [wave][row][D]
+  if (hh == 0) {
+    lds_m[wave][l32] = m_run;
+    lds_lr[wave][l32] = lr_tot;
+    lds_lf[wave][l32] = lf_tot;
+  }
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      // acc[cb] register 4 g4 + q is row d = 32 cb + 8 g4 + 4 hh + q of O^T
+      f32x4 x;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = acc[cb][4 * g4 + q];
+      *(f32x4*)(mo + ((wave * 32 + l32) * D + 32 * cb + 8 * g4 + 4 * hh)) = x;
+    }
+  __syncthreads();
+  // thread: row tid / 8, columns (tid % 8) * D / 8 .. + D / 8
+  {
+    const int rr = tid >> 3;
+    const int c0 = (tid & 7) * (D / 8);
+    if (rr < M) {
+      float mmax = -1e30f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mmax = fmaxf(mmax, lds_m[w][rr]);
+      float wgt[4], lr_s = 0.f, lf_s = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        wgt[w] = __builtin_amdgcn_exp2f(lds_m[w][rr] - mmax);
+        lr_s += wgt[w] * lds_lr[w][rr];
+        lf_s += wgt[w] * lds_lf[w][rr];
+      }
+      const bool has = lr_s > 0.f;
+      const float inv = has ? 1.f / lr_s : 0.f;
+      const float lse = has ? (mmax + __builtin_amdgcn_logf(lf_s)) * LN2 : -INFINITY;
+      const int h = kvh * g + rr / p.Sq;
+      const int i = rr % p.Sq;
+      if (p.part_o == nullptr) {
+        uint16_t* orow = p.o + (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh;
+#pragma unroll
+        for (int c = 0; c < D / 8; c += 8) {
+          f32x8 x;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) s += wgt[w] * mo[(w * 32 + rr) * D + c0 + c + e];
+            x[e] = s * inv;
+          }
+          *(i16x8*)(orow + c0 + c) = T::cvt(x);
+        }
+        if (p.lse != nullptr && (tid & 7) == 0)
+          p.lse[((int64_t)b * p.Hq + h) * p.Sq + i] = lse;
+      } else {
+        // a piece of a split key range: fp32 state normalised over its keys
+        float* prow = p.part_o + ((((int64_t)piece * p.B + b) * p.Sq + i) * p.Hq + h) * D;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+          float s = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) s += wgt[w] * mo[(w * 32 + rr) * D + c0 + c];
+          prow[c0 + c] = s * inv;
+        }
+        if ((tid & 7) == 0)
+          p.part_lse[(((int64_t)piece * p.B + b) * p.Hq + h) * p.Sq + i] = lse;
+      }
+    }
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_decode_d(bool causal, const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.grid), block(256);
+  if (causal)
+    hipLaunchKernelGGL((attn_decode_kernel<DT, D, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<DT, D, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+__attribute__((visibility("hidden"))) hipError_t attn_detail::launch_decode(
+    int dtype, int d, int causal, const DecodeArgs& a, hipStream_t st) {
+  if (dtype == ATTN_DTYPE_BF16)
+    return d == 128 ? launch_decode_d<ATTN_DTYPE_BF16, 128>(causal != 0, a, st)
+                    : launch_decode_d<ATTN_DTYPE_BF16, 64>(causal != 0, a, st);
+  return d == 128 ? launch_decode_d<ATTN_DTYPE_F16, 128>(causal != 0, a, st)
+                  : launch_decode_d<ATTN_DTYPE_F16, 64>(causal != 0, a, st);
+}

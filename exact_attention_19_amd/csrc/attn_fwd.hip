@@ -104,13 +104,6 @@ struct Params {
 };
 
 
-__device__ __forceinline__ float other_half_max(float x) {
-  // v_permlane32_swap(x, x) returns {x of lanes 0-31 in both halves,
-  // x of lanes 32-63 in both halves}: their max is the max over the lane pair.
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
-                                            __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 
 // ------------------------------------------------------------ the kernel
 //
@@ -910,10 +903,68 @@ hipError_t launch_attn(int dtype, int d, int causal, const Plan& pl, long long n
 
 // The forward pass with strides and an optional key split.  Arguments are
 // validated by the callers.
+// Decode shapes (every query row of a kv head fits one wave): the decode
+// kernel, with its key range cut into pieces over workgroups when the
+// (batch, kv head) pairs are too few, merged by the merge kernel.
+attn_status run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal,
+                       int dtype, const Strides& st, int kv_split, void* workspace,
+                       size_t workspace_bytes, hipStream_t hs) {
+  const DecodePlan dp = make_decode_plan(B, Sq, Sk, Hq, Hkv, d, kv_split);
+  if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
+  if (dp.pieces > 1 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
+                        workspace_bytes < dp.ws_bytes))
+    return ATTN_ERR_INVALID_ARG;
+  DecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.q_sb = st.s[0], a.q_ss = st.s[1], a.q_sh = st.s[2];
+  a.k_sb = st.s[3], a.k_ss = st.s[4], a.k_sh = st.s[5];
+  a.v_sb = st.s[6], a.v_ss = st.s[7], a.v_sh = st.s[8];
+  a.o_sb = st.s[9], a.o_ss = st.s[10], a.o_sh = st.s[11];
+  a.B = B;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.piece_tiles = dp.piece_tiles;
+  a.grid = dp.grid;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  if (dp.pieces > 1) {
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((char*)workspace + dp.lse_offset);
+  }
+  hipError_t e = launch_decode(dtype, d, causal, a, hs);
+  if (e != hipSuccess) return ATTN_ERR_LAUNCH;
+  if (dp.pieces == 1) return ATTN_OK;
+  MergeParams mp{};
+  mp.parts = a.part_o;
+  mp.parts_lse = a.part_lse;
+  mp.o = (uint16_t*)o;
+  mp.o_sb = a.o_sb, mp.o_ss = a.o_ss, mp.o_sh = a.o_sh;
+  mp.lse = lse;
+  mp.B = B;
+  mp.Sq = Sq;
+  mp.Hq = Hq;
+  mp.n_parts = dp.pieces;
+  mp.q_first = 0;
+  mp.sq_rows = Sq;
+  mp.rows = (long long)B * Sq * Hq;
+  const int rpb = 256 / (d / 4);
+  e = launch_merge_any(ATTN_DTYPE_F32, dtype, d, (mp.rows + rpb - 1) / rpb, mp, hs);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 attn_status run_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal,
                         int dtype, const Strides& st, int kv_split, void* workspace,
                         size_t workspace_bytes, hipStream_t hs) {
+  if (decode_eligible(Sq, Hq, Hkv, d))
+    return run_decode(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype, st, kv_split,
+                      workspace, workspace_bytes, hs);
   const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split);
   if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   if (sp.chunk > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
@@ -976,9 +1027,16 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
                                   Hkv, d, 1.0f, causal, dtype);
   if (st != ATTN_OK) return st;
   const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
-  const int vals[9] = {pl.grid, pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
-                       pl.lds_bytes, pl.xcd_cols > 0 ? 1 : 0, pl.pipelined};
-  for (int i = 0; i < n && i < 9; ++i) out[i] = vals[i];
+  int vals[10] = {pl.grid, pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
+                  pl.lds_bytes, pl.xcd_cols > 0 ? 1 : 0, pl.pipelined, 0};
+  if (decode_eligible(Sq, Hq, Hkv, d)) {
+    // the decode kernel, unsplit: a workgroup per (batch, kv head) with all
+    // g * Sq rows in one wave, 4 waves over the keys
+    const int g = Hq / Hkv;
+    const int vals_dec[10] = {B * Hkv, 256, Sq, 32, g, 32, 4 * 2 * 32 * d * 2, 0, 0, 1};
+    for (int i = 0; i < 10; ++i) vals[i] = vals_dec[i];
+  }
+  for (int i = 0; i < n && i < 10; ++i) out[i] = vals[i];
   return ATTN_OK;
 }
 
@@ -997,6 +1055,17 @@ attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, i
   int base[9];
   attn_status st = attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype, base, 9);
   if (st != ATTN_OK) return st;
+  if (decode_eligible(Sq, Hq, Hkv, d)) {
+    const DecodePlan dp = make_decode_plan(B, Sq, Sk, Hq, Hkv, d, kv_split);
+    if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
+    const long long mrows = (long long)B * Sq * Hq;
+    const int rpb = 256 / (d / 4);
+    const int vals[5] = {(int)dp.grid, dp.pieces, dp.pieces > 1 ? dp.piece_tiles * 32 : 0,
+                         dp.pieces > 1 ? 0 : Sq,
+                         dp.pieces > 1 ? (int)((mrows + rpb - 1) / rpb) : 0};
+    for (int i = 0; i < n && i < 5; ++i) out[i] = vals[i];
+    return ATTN_OK;
+  }
   const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split);
   if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   const int vals[5] = {(int)sp.grid, sp.npieces, sp.chunk * BC, sp.q_first,
@@ -1011,7 +1080,9 @@ attn_status attn_fwd_split_workspace(int B, int Sq, int Sk, int Hq, int Hkv, int
   int out[5];
   attn_status st = attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype, kv_split, out, 5);
   if (st != ATTN_OK) return st;
-  *bytes = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split).ws_bytes;
+  *bytes = decode_eligible(Sq, Hq, Hkv, d)
+               ? make_decode_plan(B, Sq, Sk, Hq, Hkv, d, kv_split).ws_bytes
+               : make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split).ws_bytes;
   return ATTN_OK;
 }
 

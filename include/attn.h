@@ -97,7 +97,7 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
 
 /*
  * attn_fwd_plan -- describe the launch attn_fwd would make for these sizes,
- * without any device call.  Writes up to n (at most 9) ints into `out`:
+ * without any device call.  Writes up to n (at most 10) ints into `out`:
  *   [0] workgroups in the grid   [1] threads per workgroup
  *   [2] query rows per workgroup [3] keys per K/V tile
  *   [4] query heads per workgroup (GQA packing)
@@ -106,6 +106,10 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
  *   [8] 1 if the software-pipelined kernel (the softmax of one K/V tile
  *       overlapping the matrix products of the previous and next tiles) is
  *       used
+ *   [9] 1 if the decode kernel is used: when the query rows of a kv head
+ *       (Hq / Hkv * Sq) number at most 32 and d is 64 or 128, all of them
+ *       share one wave and the 4 waves of a workgroup split the keys (then
+ *       [2] is Sq and [4] the GQA group size)
  * Returns the status attn_fwd_check would return.
  */
 attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
@@ -128,7 +132,10 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
  *   q ... dtype  as for attn_fwd (same validation, same status codes)
  *   kv_split     0 = the library's choice: split only when there are fewer
  *                query blocks than the 256 CUs of the device, into the
- *                shortest pieces that still number at most 256;
+ *                shortest pieces that still number at most 256 (for decode
+ *                shapes, see attn_fwd_plan [9]: only below 128 (batch, kv
+ *                head) pairs, into about 128 workgroups of at least 32
+ *                32-key tiles);
  *                1 = never split (exactly attn_fwd);
  *                k > 1 = cut the longest query block into at most k pieces
  *                (pieces hold a whole, even number of 64-key tiles)

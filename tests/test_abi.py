@@ -201,7 +201,6 @@ def test_split_automatic_choice():
                 (1, 1280, 1536, 16, 16, 128, 1, ATTN_DTYPE_F16),
                 (1, 1237, 1531, 16, 16, 128, 1, ATTN_DTYPE_F16),
                 (1, 64, 4096, 1, 1, 128, 0, ATTN_DTYPE_F16),
-                (16, 1, 8192, 32, 8, 128, 0, ATTN_DTYPE_BF16),
                 (1, 300, 300, 4, 2, 64, 1, ATTN_DTYPE_F16),
                 (1, 128, 128, 2, 2, 64, 0, ATTN_DTYPE_F16)):
         B, Sq, Sk, Hq, Hkv, d, causal, dt = cfg
@@ -357,3 +356,51 @@ def test_bwd_workspace_and_early_rejection():
     assert lib.attn_bwd(*args, None, need, None) == ATTN_ERR_INVALID_ARG
     assert lib.attn_bwd(*args, 0x200000, need - 4, None) == ATTN_ERR_INVALID_ARG
     assert lib.attn_bwd(*args, 0x200010, need, None) == ATTN_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------- decode plan
+
+@pytest.mark.parametrize("cfg", [
+    (32, 1, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16),
+    (1, 1, 32768, 32, 8, 128, 1, ATTN_DTYPE_BF16),
+    (32, 4, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16),
+    (2, 8, 1000, 8, 2, 64, 0, ATTN_DTYPE_F16),
+    (1, 32, 100, 4, 4, 128, 1, ATTN_DTYPE_F16),
+])
+@pytest.mark.parametrize("kv_split", [0, 1, 3])
+def test_decode_plan(cfg, kv_split):
+    """Decode shapes (g * Sq <= 32, d 64 or 128) take the decode kernel: one
+    workgroup per (batch, kv head) and key piece; automatic pieces only below
+    128 (batch, kv head) pairs, about 128 workgroups of at least 32 tiles;
+    the workspace holds one fp32 row state per piece and query row."""
+    _lib()
+    B, Sq, Sk, Hq, Hkv, d, causal, dt = cfg
+    plan = binding.attn_fwd_plan(*cfg)
+    assert plan["decode"] == 1 and plan["grid"] == B * Hkv and plan["rows_per_wave"] == 32
+    sp = binding.attn_fwd_split_plan(*cfg, kv_split)
+    ws = binding.attn_fwd_split_workspace(*cfg, kv_split)
+    ntiles = -(-Sk // 32)
+    cols = B * Hkv
+    if kv_split == 0:
+        pieces = -(-128 // cols) if cols < 128 else 1
+        pieces = min(pieces, max(ntiles // 32, 1))
+    else:
+        pieces = kv_split if kv_split > 1 else 1
+    pieces = min(pieces, ntiles)
+    per = -(-ntiles // pieces)
+    pieces = -(-ntiles // per)
+    assert sp["pieces"] == pieces and sp["grid"] == cols * pieces
+    if pieces > 1:
+        assert sp["keys_per_piece"] == per * 32 and sp["first_split_row"] == 0
+        rows = B * Sq * Hq
+        assert ws == -(-pieces * rows * d * 4 // 256) * 256 + pieces * rows * 4
+    else:
+        assert sp["keys_per_piece"] == 0 and ws == 0 and sp["merge_grid"] == 0
+
+
+def test_prefill_shapes_do_not_take_the_decode_kernel():
+    _lib()
+    for cfg in ((1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16),
+                (1, 9, 100, 32, 8, 128, 1, ATTN_DTYPE_BF16),     # 4 x 9 = 36 rows
+                (1, 1, 1000, 8, 8, 96, 0, ATTN_DTYPE_BF16)):     # d = 96
+        assert binding.attn_fwd_plan(*cfg)["decode"] == 0
