@@ -236,6 +236,10 @@ def main():
                     help="time attn_bwd (dQ, dK, dV from O, LSE and a seeded dO) instead of "
                          "the forward; FLOPs are 2.5x the forward's (five products of the "
                          "forward's two-product size)")
+    ap.add_argument("--cold", type=int, default=1, metavar="N",
+                    help="rotate N copies of the inputs and outputs across steps, so that a "
+                         "step's data is not left in the 256 MB MALL by the step before "
+                         "(forward only; default 1 = warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--board-sample", action="store_true",
                     help="after the timed steps, keep stepping for about 3 s while "
@@ -281,9 +285,16 @@ def main():
     ws_bytes = attn_fwd_split_workspace(*shape, kv_split=args.kv_split)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
+    sets = [(q, k, v, o, lse)]
+    for _ in range(max(args.cold, 1) - 1):
+        sets.append((q.clone(), k.clone(), v.clone(), torch.empty_like(o), torch.empty_like(lse)))
+    turn = [0]
+
     def step():
-        attn_fwd_split(q, k, v, scale=w.scale, causal=w.causal, kv_split=args.kv_split,
-                       out=o, lse=lse, workspace=ws, stream=stream)
+        qs, ks, vs, os_, ls = sets[turn[0] % len(sets)]
+        turn[0] += 1
+        attn_fwd_split(qs, ks, vs, scale=w.scale, causal=w.causal, kv_split=args.kv_split,
+                       out=os_, lse=ls, workspace=ws, stream=stream)
 
     if args.backward:
         attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
@@ -368,6 +379,7 @@ def main():
         }),
         "launch": plan,
         "split": dict(split, kv_split_arg=args.kv_split, workspace_bytes=ws_bytes),
+        "input_sets_rotated": len(sets),
         "device": {"name": props.name, "cus": props.multi_processor_count},
         "kernel_source_digest": kernel_source_digest(),
     }
