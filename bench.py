@@ -240,6 +240,9 @@ def main():
                     help="rotate N copies of the inputs and outputs across steps, so that a "
                          "step's data is not left in the 256 MB MALL by the step before "
                          "(forward only; default 1 = warm)")
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
+                    help="decode workloads: time attn_decode_paged with K and V in a "
+                         "shuffled pool of BLOCK-token blocks (every sequence Sk long)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--board-sample", action="store_true",
                     help="after the timed steps, keep stepping for about 3 s while "
@@ -295,6 +298,20 @@ def main():
         turn[0] += 1
         attn_fwd_split(qs, ks, vs, scale=w.scale, causal=w.causal, kv_split=args.kv_split,
                        out=os_, lse=ls, workspace=ws, stream=stream)
+
+    if args.paged:
+        from exact_attention_19_amd import attn_decode_paged, attn_decode_paged_workspace
+        from exact_attention_19_amd.workloads import make_paged_cache
+        kp, vp, table, seqlens = (t.to(dev) for t in make_paged_cache(
+            k_cpu, v_cpu, [w.Sk] * w.B, args.paged, seed=1))
+        pws = torch.empty(max(attn_decode_paged_workspace(w.B, w.Sq, w.Hq, w.Hkv, w.d, w.Sk,
+                                                          args.kv_split), 1),
+                          dtype=torch.uint8, device=dev)
+
+        def step():  # noqa: F811 (the paged step replaces the dense one)
+            attn_decode_paged(q, kp, vp, table, seqlens, scale=w.scale, causal=w.causal,
+                              max_seqlen=w.Sk, kv_split=args.kv_split, out=o, lse=lse,
+                              workspace=pws, stream=stream)
 
     if args.backward:
         attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
@@ -359,6 +376,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) / outlier recipe, resident in HBM)",
         "config": {"workload": w.name, "pass": "backward" if args.backward else "forward",
+                   "kv_cache": f"paged, {args.paged}-token blocks" if args.paged else "dense",
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Sq": w.Sq, "Sk": w.Sk, "d": w.d, "causal": w.causal,
                    "scale": w.scale, "input_sha256": digest[:16]},

@@ -19,7 +19,9 @@ ATTN_DTYPE_F16, ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1, 2
 EXPORTED = ("attn_fwd", "attn_fwd_check", "attn_fwd_plan", "attn_fwd_split",
             "attn_fwd_split_workspace", "attn_fwd_split_plan", "attn_fwd_strided",
             "attn_fwd_strided_check", "attn_merge", "attn_merge_check", "attn_bwd",
-            "attn_bwd_check", "attn_bwd_workspace", "attn_status_str", "attn_abi_version")
+            "attn_bwd_check", "attn_bwd_workspace", "attn_decode_paged",
+            "attn_decode_paged_check", "attn_decode_paged_workspace", "attn_status_str",
+            "attn_abi_version")
 
 _lib = None
 
@@ -70,6 +72,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_merge.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i, vp]
     lib.attn_merge_check.restype = i
     lib.attn_merge_check.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i]
+    lib.attn_decode_paged.restype = i
+    lib.attn_decode_paged.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, i, vp, sz, vp]
+    lib.attn_decode_paged_check.restype = i
+    lib.attn_decode_paged_check.argtypes = [vp] * 7 + [i] * 9 + [f, i, i]
+    lib.attn_decode_paged_workspace.restype = i
+    lib.attn_decode_paged_workspace.argtypes = [i] * 7 + [ctypes.POINTER(sz)]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [i]
     lib.attn_abi_version.restype = i
@@ -400,3 +408,81 @@ def attn_bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = F
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+def attn_decode_paged_check(q_ptr, k_ptr, v_ptr, table_ptr, lens_ptr, o_ptr, lse_ptr, B, Sq,
+                            Hq, Hkv, d, num_blocks, block_size, max_blocks, max_seqlen, scale,
+                            causal, dtype_code) -> int:
+    """attn_decode_paged's validation on raw integer addresses; returns the status."""
+    return int(load_library().attn_decode_paged_check(
+        q_ptr, k_ptr, v_ptr, table_ptr, lens_ptr, o_ptr, lse_ptr, B, Sq, Hq, Hkv, d,
+        num_blocks, block_size, max_blocks, max_seqlen, float(scale), int(causal), dtype_code))
+
+
+def attn_decode_paged_workspace(B, Sq, Hq, Hkv, d, max_seqlen, kv_split=0) -> int:
+    """Workspace bytes attn_decode_paged needs (0 when it does not split)."""
+    n = ctypes.c_size_t(0)
+    st = load_library().attn_decode_paged_workspace(B, Sq, Hq, Hkv, d, max_seqlen,
+                                                    int(kv_split), ctypes.byref(n))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_paged_workspace")
+    return int(n.value)
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seqlens, scale: float | None = None,
+                      causal: bool = True, max_seqlen: int | None = None, kv_split: int = 0,
+                      out=None, lse=None, return_lse: bool = True, workspace=None,
+                      stream=None):
+    """Decode attention over a paged K/V cache.
+
+    q: (B, Sq, Hq, d); k_cache, v_cache: (num_blocks, block_size, Hkv, d);
+    block_table: int32 (B, max_blocks); seqlens: int32 (B,), all on the GPU.
+    Sequence b attends to its first seqlens[b] tokens, token t at
+    block_table[b, t // block_size], slot t % block_size; its Sq queries are
+    its last Sq positions.  ``max_seqlen`` (default: the table's capacity,
+    max_blocks * block_size) bounds the lengths and sizes the key split;
+    it is never read from the device.  Returns (o, lse) as attn_fwd does."""
+    import torch
+    if q.dim() != 4 or k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q must be (B, Sq, Hq, d) and k_cache, v_cache one "
+                         "(num_blocks, block_size, Hkv, d) shape")
+    B, Sq, Hq, d = q.shape
+    num_blocks, block_size, Hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError(f"head size mismatch: q {d}, cache {dk}")
+    code = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if block_table.dtype != torch.int32 or seqlens.dtype != torch.int32:
+        raise TypeError("block_table and seqlens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seqlens.shape) != (B,):
+        raise ValueError("block_table must be (B, max_blocks) and seqlens (B,)")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seqlens", seqlens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    max_blocks = block_table.shape[1]
+    if max_seqlen is None:
+        max_seqlen = max_blocks * block_size
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse, return_lse)
+    if workspace is None:
+        need = attn_decode_paged_workspace(B, Sq, Hq, Hkv, d, int(max_seqlen), kv_split)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().attn_decode_paged(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        seqlens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, Sq, Hq, Hkv, d, num_blocks, block_size, max_blocks, int(max_seqlen), float(scale),
+        int(bool(causal)), code, int(kv_split), ws_ptr, ws_bytes,
+        ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_paged")
+    return out, lse

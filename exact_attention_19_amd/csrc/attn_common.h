@@ -34,6 +34,14 @@ struct DecodeArgs {
   float scale_log2;
   float* part_o;     // pieces > 1: [piece][b][i][h][d] fp32, else null
   float* part_lse;   // pieces > 1: [piece][b][h][i]
+  // paged K/V cache (block_table != null): K and V rows of token t of
+  // sequence b are row (block_table[b][t / block_size] * block_size +
+  // t % block_size) of the pools, whose rows are k_ss / v_ss elements apart
+  // (k_sb, v_sb unused); sequence b has min(seqlens[b], Sk) keys, and Sk
+  // is at most max_blocks * block_size
+  const int* block_table;  // [B][max_blocks]
+  const int* seqlens;      // [B]
+  int block_size, max_blocks, num_blocks;
 };
 
 // Launch of the decode kernel (defined in attn_decode.hip).

@@ -59,6 +59,10 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
   const int kvh = col % p.Hkv;
   const int g = p.Hq / p.Hkv;
   const int M = g * p.Sq;
+  // keys of this sequence (paged cache: its own length, at most Sk, which
+  // the host keeps within the block table)
+  int Sk = p.Sk;
+  if (p.seqlens != nullptr) Sk = max(0, min(p.seqlens[b], p.Sk));
 
   // this lane's query row
   const int r = l32;
@@ -76,28 +80,46 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
     }
   }
   // keys this row sees: j < Sk, and j <= qi + Sk - Sq when causal
-  int lim = p.Sk - 1;
-  if (CAUSAL) lim = min(lim, qi + p.Sk - p.Sq);
+  int lim = Sk - 1;
+  if (CAUSAL) lim = min(lim, qi + Sk - p.Sq);
   if (!rok) lim = -1;
 
   // the piece's tiles [t_lo, t_hi); this wave takes t_lo + wave, + 4, ...
-  const int ntiles = (p.Sk + DBC - 1) / DBC;
+  const int ntiles = (Sk + DBC - 1) / DBC;
   const int t_lo = piece * p.piece_tiles;
   const int t_hi = min(ntiles, t_lo + p.piece_tiles);
   // last key seen by any row of the group (tiles past it are skipped)
-  int kv_last = p.Sk - 1;
-  if (CAUSAL) kv_last = min(kv_last, p.Sq - 1 + p.Sk - p.Sq);
-  const int t_end = min(t_hi, kv_last / DBC + 1);
+  // (bottom-right alignment: the last query row sees every key)
+  const int t_end = Sk > 0 ? min(t_hi, (Sk - 1) / DBC + 1) : 0;
 
-  const char* kbase = (const char*)(p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh);
-  const char* vbase = (const char*)(p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh);
+  const bool paged = p.block_table != nullptr;
+  const char* kbase =
+      (const char*)(p.k + (paged ? 0 : (int64_t)b * p.k_sb) + (int64_t)kvh * p.k_sh);
+  const char* vbase =
+      (const char*)(p.v + (paged ? 0 : (int64_t)b * p.v_sb) + (int64_t)kvh * p.v_sh);
   const uint32_t rbk = (uint32_t)(p.k_ss * 2);
   const uint32_t rbv = (uint32_t)(p.v_ss * 2);
+  // row (of the K and V row arrays) of the first key of tile n: the tile's
+  // 32 keys are consecutive rows (block_size is a multiple of 32)
+  // (the entry is read through the constant address space with a
+  // wave-uniform index, so it is a scalar load: a vector load would join the
+  // vmcnt queue of the K/V tiles in flight and force a wait on all of them)
+  using const_int = const __attribute__((address_space(4))) int;
+  auto tile_row = [&](int n) -> int64_t {
+    if (!paged) return (int64_t)n * DBC;
+    const int t0 = n * DBC;
+    const int idx = __builtin_amdgcn_readfirstlane(b * p.max_blocks + t0 / p.block_size);
+    int blk = ((const_int*)p.block_table)[idx];
+    blk = min(max(blk, 0), p.num_blocks - 1);
+    return (int64_t)blk * p.block_size + t0 % p.block_size;
+  };
 
-  // K fragments of tile n: key row sigma(l32) of the tile, chunks kk
-  auto load_k = [&](int n, i16x8 (&kf)[KK]) {
-    const int key = min(n * DBC + sigma(l32), p.Sk - 1);
-    const uint16_t* krow = (const uint16_t*)(kbase + (int64_t)key * rbk);
+  // K fragments of tile n (first row `row0`): key row sigma(l32) of the
+  // tile, chunks kk
+  auto load_k = [&](int n, int64_t row0, i16x8 (&kf)[KK]) {
+    const int key = min(n * DBC + sigma(l32), Sk - 1);
+    const uint16_t* krow =
+        (const uint16_t*)(kbase + (row0 + (key - n * DBC)) * (int64_t)rbk);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       kf[kk] = __builtin_bit_cast(i16x8, *(const u32x4*)(krow + kk * 16 + hh * 8));
@@ -105,13 +127,13 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
   // V tile n -> this wave's LDS stage: column-blocked, 32 rows x 64 bytes per
   // block, chunk c of row r at slot c ^ ((r >> 2) & 3); round u covers block
   // u >> 1, rows 16 (u & 1) + lane / 4
-  auto load_v = [&](int n, LDS_PTR(char) buf) {
+  auto load_v = [&](int n, int64_t row0, LDS_PTR(char) buf) {
     const int row = lane >> 2;
     const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-    const char* tile = vbase + (int64_t)n * DBC * rbv;
+    const char* tile = vbase + row0 * (int64_t)rbv;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int rr = min(n * DBC + 16 * h2 + row, p.Sk - 1) - n * DBC;
+      const int rr = min(n * DBC + 16 * h2 + row, Sk - 1) - n * DBC;
       const uint32_t off = (uint32_t)rr * rbv + (uint32_t)chunk * 16;
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)(DBC * rbv), 0x00020000);
@@ -154,8 +176,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
   int n = t_lo + wave;
   i16x8 kA[KK], kB[KK];
   if (n < t_end) {
-    load_k(n, kA);
-    load_v(n, vb0);
+    const int64_t r0 = tile_row(n);
+    load_k(n, r0, kA);
+    load_v(n, r0, vb0);
   }
   // one tile: kf holds K(n), vbuf V(n); the next tile's loads are in flight
   auto tile = [&](int nn, const i16x8 (&kf)[KK], LDS_PTR(char) vbuf) {
@@ -165,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) S = T::mfma(kf[kk], qf[kk], S);
     // mask keys past this row's limit (ragged end, causal tail)
-    if (nn * DBC + DBC - 1 > min(lim, p.Sk - 1) || !rok) {
+    if (nn * DBC + DBC - 1 > min(lim, Sk - 1) || !rok) {
       const int L = lim - nn * DBC - 8 * hh;
 #pragma unroll
       for (int q = 0; q < 16; ++q)
@@ -225,8 +248,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
   // stage 1) register/LDS sets, so the loop body is unrolled by two
   for (; n < t_end; n += 8) {
     if (n + 4 < t_end) {
-      load_k(n + 4, kB);
-      load_v(n + 4, vb1);
+      const int64_t r0 = tile_row(n + 4);
+      load_k(n + 4, r0, kB);
+      load_v(n + 4, r0, vb1);
     }
     // K(n) and V(n) (issued one tile earlier) have landed: wait for all but
     // the loads just issued
@@ -237,8 +261,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
     tile(n, kA, vb0);
     if (n + 4 >= t_end) break;
     if (n + 8 < t_end) {
-      load_k(n + 8, kA);
-      load_v(n + 8, vb0);
+      const int64_t r0 = tile_row(n + 8);
+      load_k(n + 8, r0, kA);
+      load_v(n + 8, r0, vb0);
       __builtin_amdgcn_s_waitcnt(VM_NEXT);
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);

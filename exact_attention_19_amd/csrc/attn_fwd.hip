@@ -906,10 +906,20 @@ hipError_t launch_attn(int dtype, int d, int causal, const Plan& pl, long long n
 // Decode shapes (every query row of a kv head fits one wave): the decode
 // kernel, with its key range cut into pieces over workgroups when the
 // (batch, kv head) pairs are too few, merged by the merge kernel.
+//
+// A paged K/V cache (pg != null) replaces the dense key range of each
+// sequence by a block table and a length; Sk is then the longest length the
+// plan covers.
+struct PagedKV {
+  const int* block_table;
+  const int* seqlens;
+  int num_blocks, block_size, max_blocks;
+};
+
 attn_status run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                        int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal,
                        int dtype, const Strides& st, int kv_split, void* workspace,
-                       size_t workspace_bytes, hipStream_t hs) {
+                       size_t workspace_bytes, hipStream_t hs, const PagedKV* pg = nullptr) {
   const DecodePlan dp = make_decode_plan(B, Sq, Sk, Hq, Hkv, d, kv_split);
   if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   if (dp.pieces > 1 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
@@ -933,6 +943,13 @@ attn_status run_decode(const void* q, const void* k, const void* v, void* o, flo
   a.piece_tiles = dp.piece_tiles;
   a.grid = dp.grid;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  if (pg != nullptr) {
+    a.block_table = pg->block_table;
+    a.seqlens = pg->seqlens;
+    a.num_blocks = pg->num_blocks;
+    a.block_size = pg->block_size;
+    a.max_blocks = pg->max_blocks;
+  }
   if (dp.pieces > 1) {
     a.part_o = (float*)workspace;
     a.part_lse = (float*)((char*)workspace + dp.lse_offset);
@@ -1163,6 +1180,65 @@ attn_status attn_merge(const void* o_parts, const float* lse_parts, int n_parts,
   const long long grid = (mp.rows + rpb - 1) / rpb;
   hipError_t e = launch_merge_any(parts_dtype, dtype, d, grid, mp, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status attn_decode_paged_check(const void* q, const void* k_cache, const void* v_cache,
+                                    const int* block_table, const int* seqlens, void* o,
+                                    float* lse, int B, int Sq, int Hq, int Hkv, int d,
+                                    int num_blocks, int block_size, int max_blocks,
+                                    int max_seqlen, float scale, int causal, int dtype) {
+  if (!q || !k_cache || !v_cache || !block_table || !seqlens || !o) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Sq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (num_blocks < 1 || max_blocks < 1 || block_size < 32 || block_size % 32 != 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (max_seqlen < 1 || (long long)max_seqlen > (long long)max_blocks * block_size)
+    return ATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)o) & 15u)
+    return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)block_table | (uintptr_t)seqlens | (uintptr_t)lse) & 3u)
+    return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!decode_eligible(Sq, Hq, Hkv, d)) return ATTN_ERR_UNSUPPORTED;
+  // index space: query rows (merge), block-table entries, pool elements
+  if ((long long)B * Sq * Hq >= (1ll << 31) || (long long)B * max_blocks >= (1ll << 31) ||
+      (long long)num_blocks * block_size >= (1ll << 31) ||
+      (long long)Hkv * d * 2 * 64 >= (1ll << 31))
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+attn_status attn_decode_paged_workspace(int B, int Sq, int Hq, int Hkv, int d, int max_seqlen,
+                                        int kv_split, size_t* bytes) {
+  if (bytes == nullptr || kv_split < 0 || B < 1 || Sq < 1 || Hkv < 1 || Hq < 1 ||
+      Hq % Hkv != 0 || max_seqlen < 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (!decode_eligible(Sq, Hq, Hkv, d)) return ATTN_ERR_UNSUPPORTED;
+  const DecodePlan dp = make_decode_plan(B, Sq, max_seqlen, Hq, Hkv, d, kv_split);
+  if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
+  *bytes = dp.ws_bytes;
+  return ATTN_OK;
+}
+
+attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                              const int* block_table, const int* seqlens, void* o, float* lse,
+                              int B, int Sq, int Hq, int Hkv, int d, int num_blocks,
+                              int block_size, int max_blocks, int max_seqlen, float scale,
+                              int causal, int dtype, int kv_split, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  attn_status st = attn_decode_paged_check(q, k_cache, v_cache, block_table, seqlens, o, lse, B,
+                                           Sq, Hq, Hkv, d, num_blocks, block_size, max_blocks,
+                                           max_seqlen, scale, causal, dtype);
+  if (st != ATTN_OK) return st;
+  if (kv_split < 0) return ATTN_ERR_INVALID_ARG;
+  // q, o dense (B, Sq, Hq, d); pool rows (block, slot) hold Hkv heads of d
+  Strides sv = dense_strides(Sq, 1, Hq, Hkv, d);
+  sv.s[3] = 0, sv.s[4] = (int64_t)Hkv * d, sv.s[5] = d;
+  sv.s[6] = 0, sv.s[7] = (int64_t)Hkv * d, sv.s[8] = d;
+  const PagedKV pg{block_table, seqlens, num_blocks, block_size, max_blocks};
+  return run_decode(q, k_cache, v_cache, o, lse, B, Sq, max_seqlen, Hq, Hkv, d, scale, causal,
+                    dtype, sv, kv_split, workspace, workspace_bytes, (hipStream_t)stream, &pg);
 }
 
 const char* attn_status_str(int status) {

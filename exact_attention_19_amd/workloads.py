@@ -176,3 +176,46 @@ def small_integer_inputs(w: Workload, seed: int = 0, device="cpu"):
     if str(device) != "cpu":
         q, k, v = q.to(device), k.to(device), v.to(device)
     return q, k, v
+
+
+def make_paged_cache(k, v, lens, block_size: int, num_blocks: int | None = None,
+                     seed: int = 0, fill: float = float("nan")):
+    """Lay K and V out as a paged cache: pools of fixed-size blocks and a
+    block table (the layout of attn_decode_paged).
+
+    k, v: (B, S, Hkv, d) CPU tensors; sequence b keeps its first lens[b]
+    rows.  Its j-th block of block_size tokens goes to a pool block whose id
+    is drawn without replacement by ``randperm`` from a generator seeded
+    with ``seed``, so the blocks of a sequence are scattered over the pool.
+    Slots that hold no token are ``fill`` (NaN by default: a read of one
+    shows in the result); table entries past a sequence's blocks are -1.
+    num_blocks defaults to the blocks needed plus one per sequence.
+
+    Returns (k_pool, v_pool, block_table, seqlens): pools (num_blocks,
+    block_size, Hkv, d) of k's dtype, block_table int32 (B, max_blocks) with
+    max_blocks the most blocks any sequence needs (at least 1), seqlens
+    int32 (B,)."""
+    B, S, Hkv, d = k.shape
+    lens = [int(x) for x in lens]
+    need = [max(0, -(-L // block_size)) for L in lens]
+    total = sum(need)
+    if num_blocks is None:
+        num_blocks = total + B
+    if num_blocks < max(total, 1):
+        raise ValueError(f"{num_blocks} blocks cannot hold {total}")
+    max_blocks = max(max(need), 1)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    ids = torch.randperm(num_blocks, generator=g)[:total].tolist()
+    kp = torch.full((num_blocks, block_size, Hkv, d), fill, dtype=k.dtype)
+    vp = torch.full((num_blocks, block_size, Hkv, d), fill, dtype=v.dtype)
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    n = 0
+    for b in range(B):
+        for j in range(need[b]):
+            lo, hi = j * block_size, min((j + 1) * block_size, lens[b])
+            kp[ids[n], :hi - lo] = k[b, lo:hi]
+            vp[ids[n], :hi - lo] = v[b, lo:hi]
+            table[b, j] = ids[n]
+            n += 1
+    return kp, vp, table, torch.tensor(lens, dtype=torch.int32)

@@ -53,14 +53,15 @@ typedef enum {
   ATTN_ERR_INVALID_ARG = 1, /* null pointer, size < 1, Hq % Hkv != 0, bad
                                scale, causal not 0/1, misaligned pointer,
                                index space too large */
-  ATTN_ERR_UNSUPPORTED = 2, /* d or dtype outside the built set */
+  ATTN_ERR_UNSUPPORTED = 2, /* d, dtype or (paged decode) shape outside the
+                               built set */
   ATTN_ERR_LAUNCH = 3       /* HIP reported an error for the launch */
 } attn_status;
 
 /* F32 is accepted only for the partial outputs passed to attn_merge. */
 typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1, ATTN_DTYPE_F32 = 2 } attn_dtype;
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /*
  * attn_fwd -- fused attention forward.
@@ -291,6 +292,69 @@ attn_status attn_bwd_check(const void* q, const void* k, const void* v,
 
 /* Workspace bytes attn_bwd needs for B * Hq * Sq query rows (no device call). */
 attn_status attn_bwd_workspace(int B, int Sq, int Hq, size_t* bytes);
+
+/*
+ * attn_decode_paged -- decode attention over a paged K/V cache: each of B
+ * sequences has Sq new query tokens (its last Sq positions) and a history of
+ * seqlens[b] keys kept in fixed-size blocks of a shared pool, listed by a
+ * block table.  The MiniPaged-Qwen page (section 19, prefill vs. decode) has
+ * decode read the K/V cache through Paged Attention; it gives no layout, and
+ * this is the plainest one: an address translation in front of attn_fwd, so
+ * the result is attn_fwd's on the gathered keys of each sequence (same
+ * rounding, same masking; causal is bottom-right aligned to seqlens[b]).
+ *
+ *   q            (B, Sq, Hq, d), dense; query i of sequence b is position
+ *                seqlens[b] - Sq + i
+ *   k_cache, v_cache  the pools, (num_blocks, block_size, Hkv, d) each,
+ *                dense: token t of sequence b is at block
+ *                block_table[b * max_blocks + t / block_size], slot
+ *                t % block_size
+ *   block_table  device int32, (B, max_blocks), row-major; only the entries
+ *                of blocks that hold one of the sequence's first
+ *                min(seqlens[b], max_seqlen) tokens are read, and an entry
+ *                outside [0, num_blocks) is clamped into it (wrong values, no
+ *                out-of-range read)
+ *   seqlens      device int32, (B): keys of each sequence; a length <= 0
+ *                gives its rows O = 0 and LSE = -inf, and one above
+ *                max_seqlen is taken as max_seqlen
+ *   o, lse       as for attn_fwd: (B, Sq, Hq, d); lse (B, Hq, Sq) fp32 or NULL
+ *   num_blocks   >= 1 blocks in each pool
+ *   block_size   tokens per block, a multiple of 32
+ *   max_blocks   >= 1 columns of the block table
+ *   max_seqlen   the longest length to cover, 1 .. max_blocks * block_size;
+ *                it sizes the key split (no device read of seqlens is made)
+ *   B ... dtype  as for attn_fwd, restricted to the decode kernel's shapes:
+ *                d = 64 or 128 and (Hq / Hkv) * Sq <= 32, else
+ *                ATTN_ERR_UNSUPPORTED
+ *   kv_split, workspace, workspace_bytes  as for attn_fwd_split, with the
+ *                decode rule for kv_split = 0; the workspace size is
+ *                attn_decode_paged_workspace's
+ *   stream       as for attn_fwd; up to two kernels are queued on it
+ *
+ * Pointers: q, the pools and o 16-byte aligned; block_table, seqlens and lse
+ * 4-byte aligned.  attn_decode_paged_check validates without a device call.
+ */
+attn_status attn_decode_paged(const void* q, const void* k_cache,
+                              const void* v_cache, const int* block_table,
+                              const int* seqlens, void* o, float* lse, int B,
+                              int Sq, int Hq, int Hkv, int d, int num_blocks,
+                              int block_size, int max_blocks, int max_seqlen,
+                              float scale, int causal, int dtype,
+                              int kv_split, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+attn_status attn_decode_paged_check(const void* q, const void* k_cache,
+                                    const void* v_cache, const int* block_table,
+                                    const int* seqlens, void* o, float* lse,
+                                    int B, int Sq, int Hq, int Hkv, int d,
+                                    int num_blocks, int block_size,
+                                    int max_blocks, int max_seqlen, float scale,
+                                    int causal, int dtype);
+
+/* Workspace bytes attn_decode_paged needs (0 when it does not split). */
+attn_status attn_decode_paged_workspace(int B, int Sq, int Hq, int Hkv, int d,
+                                        int max_seqlen, int kv_split,
+                                        size_t* bytes);
 
 /* Human-readable name of a status code (static string). */
 const char* attn_status_str(int status);

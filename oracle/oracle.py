@@ -106,6 +106,56 @@ def attn_fwd_oracle(q, k, v, scale: float, causal: bool, rows=None,
     return o, lse
 
 
+def gather_paged_oracle(cache, block_table, b: int, length: int) -> np.ndarray:
+    """The first ``length`` tokens of sequence b from a paged pool, in order.
+
+    cache: (num_blocks, block_size, Hkv, d); block_table: (B, max_blocks)
+    integers.  Token t of sequence b sits in block block_table[b, t //
+    block_size] at slot t % block_size: a paged K/V cache is an address
+    translation in front of a dense per-sequence key array (the MiniPaged-
+    Qwen page, section 19, names Paged Attention for decode and gives no
+    layout; this is the plainest one).  cache may be a numpy array or a CPU
+    torch tensor of any float dtype.  Returns (length, Hkv, d) fp64."""
+    bt = np.asarray(block_table, dtype=np.int64)
+    bs = cache.shape[1]
+    t = np.arange(length)
+    blocks, slots = bt[b, t // bs], t % bs  # where token t lives
+    if hasattr(cache, "detach"):  # torch tensor: index it before widening
+        import torch
+        rows = cache.detach()[torch.from_numpy(blocks), torch.from_numpy(slots)]
+    else:
+        rows = np.asarray(cache)[blocks, slots]
+    return _as_f64(rows)
+
+
+def attn_decode_paged_oracle(q, k_cache, v_cache, block_table, seqlens, scale: float,
+                             causal: bool, max_seqlen: int | None = None):
+    """Attention of each sequence's Sq query tokens over its paged K/V history.
+
+    q: (B, Sq, Hq, d); k_cache, v_cache: (num_blocks, block_size, Hkv, d);
+    block_table: (B, max_blocks); seqlens: (B,).  Sequence b has L_b =
+    min(seqlens[b], max_seqlen) keys (max_seqlen defaults to no bound; a
+    length <= 0 means none), gathered by ``gather_paged_oracle``; its queries
+    are its last Sq positions, so the causal mask is bottom-right aligned to
+    L_b.  Each sequence is then exactly the dense forward: attn_fwd_oracle
+    with Sk = L_b.  Returns o (B, Sq, Hq, d), lse (B, Hq, Sq); rows that see
+    no key get o = 0, lse = -inf."""
+    qd = _as_f64(q)
+    B, Sq, Hq, d = qd.shape
+    lens = np.asarray(seqlens, dtype=np.int64).reshape(-1)
+    o = np.zeros((B, Sq, Hq, d), np.float64)
+    lse = np.full((B, Hq, Sq), -np.inf)
+    for b in range(B):
+        L = int(lens[b]) if max_seqlen is None else min(int(lens[b]), int(max_seqlen))
+        if L <= 0:
+            continue
+        kb = gather_paged_oracle(k_cache, block_table, b, L)[None]
+        vb = gather_paged_oracle(v_cache, block_table, b, L)[None]
+        ob, lb = attn_fwd_oracle(qd[b:b + 1], kb, vb, scale, causal)
+        o[b], lse[b] = ob[0], lb[0]
+    return o, lse
+
+
 def merge_partials_oracle(o_parts, lse_parts):
     """Combine partial attention states over disjoint key subsets, in fp64.
 

@@ -404,3 +404,71 @@ def test_prefill_shapes_do_not_take_the_decode_kernel():
                 (1, 9, 100, 32, 8, 128, 1, ATTN_DTYPE_BF16),     # 4 x 9 = 36 rows
                 (1, 1, 1000, 8, 8, 96, 0, ATTN_DTYPE_BF16)):     # d = 96
         assert binding.attn_fwd_plan(*cfg)["decode"] == 0
+
+
+# ------------------------------------------------------------- paged decode
+
+PG = dict(B=4, Sq=1, Hq=32, Hkv=8, d=128, num_blocks=100, block_size=64, max_blocks=20,
+          max_seqlen=1200, scale=0.088, causal=1, dtype=ATTN_DTYPE_BF16)
+
+
+def _pcheck(ptrs=None, **over):
+    a = dict(PG, **over)
+    p = ptrs or [A + 0x1000 * i for i in range(7)]
+    return binding.attn_decode_paged_check(*p, *(a[k] for k in PG))
+
+
+def test_paged_decode_validation():
+    _lib()
+    assert _pcheck() == ATTN_OK
+    assert _pcheck(d=64, dtype=ATTN_DTYPE_F16, causal=0, Sq=8, Hq=16, Hkv=4) == ATTN_OK
+    assert _pcheck(block_size=32, max_seqlen=20 * 32) == ATTN_OK
+    for i in range(7):
+        p = [A + 0x1000 * j for j in range(7)]
+        if i != 6:  # lse may be NULL
+            p[i] = None
+            assert _pcheck(p) == ATTN_ERR_INVALID_ARG, i
+        # q, pools, o: 16-byte aligned; table, lengths, lse: 4-byte
+        p[i] = A + 0x1000 * i + (2 if i in (3, 4, 6) else 8)
+        assert _pcheck(p) == ATTN_ERR_INVALID_ARG, i
+    p = [A + 0x1000 * j for j in range(7)]
+    p[6] = None
+    assert _pcheck(p) == ATTN_OK
+    for over in (dict(Hq=30), dict(B=0), dict(Sq=0), dict(num_blocks=0), dict(max_blocks=0),
+                 dict(block_size=16), dict(block_size=48), dict(max_seqlen=0),
+                 dict(max_seqlen=20 * 64 + 1), dict(scale=0.0), dict(causal=2)):
+        assert _pcheck(**over) == ATTN_ERR_INVALID_ARG, over
+    # outside the decode kernel's shapes: (Hq / Hkv) * Sq > 32, d not 64/128
+    for over in (dict(Sq=9), dict(d=96), dict(d=256), dict(dtype=2)):
+        assert _pcheck(**over) == ATTN_ERR_UNSUPPORTED, over
+
+
+@pytest.mark.parametrize("B,max_seqlen,kv_split", [(4, 1200, 0), (32, 8192, 0), (1, 32768, 0),
+                                                   (4, 1200, 1), (4, 1200, 5)])
+def test_paged_decode_workspace_follows_the_decode_plan(B, max_seqlen, kv_split):
+    """The paged kernel is the decode kernel over max_seqlen keys: the same
+    pieces and workspace as a dense decode call of that length."""
+    _lib()
+    dense = binding.attn_fwd_split_workspace(B, 1, max_seqlen, 32, 8, 128, 1,
+                                             ATTN_DTYPE_BF16, kv_split)
+    assert binding.attn_decode_paged_workspace(B, 1, 32, 8, 128, max_seqlen, kv_split) == dense
+    with pytest.raises(binding.AttnError):
+        binding.attn_decode_paged_workspace(B, 1, 32, 8, 128, max_seqlen, -1)
+    with pytest.raises(binding.AttnError):
+        binding.attn_decode_paged_workspace(B, 9, 32, 8, 128, max_seqlen, 0)
+
+
+def test_paged_decode_rejects_before_any_device_call():
+    lib = _lib()
+    p = [A + 0x1000 * i for i in range(7)]
+    vals = [PG[k] for k in PG]
+    vals[9] = ctypes.c_float(PG["scale"])
+    need = binding.attn_decode_paged_workspace(1, 1, 32, 8, 128, 32768, 0)
+    assert need > 0
+    a = list(vals)
+    a[0], a[8] = 1, 32768  # B = 1, max_seqlen = 32768: split, needs a workspace
+    a[7] = 512
+    assert lib.attn_decode_paged(*p, *a, 0, None, need, None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_decode_paged(*p, *a, 0, 0x200000, need - 4, None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_decode_paged(*p, *a, 0, 0x200010, need, None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_decode_paged(*p, *vals, -1, None, 0, None) == ATTN_ERR_INVALID_ARG

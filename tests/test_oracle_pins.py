@@ -606,3 +606,129 @@ def test_backward_bad_arguments_rejected():
     q, k, v = _rand(59, 1, 3, 5, 2, 2, 4)
     with pytest.raises(ValueError):
         attn_bwd_oracle(q, k, v, q[:, :2], 1.0, False)
+
+
+# ---------------------------------------------------------------- paged K/V
+# Decode over a paged K/V cache: token t of sequence b lives in block
+# block_table[b, t // block_size], slot t % block_size (the plainest reading
+# of Paged Attention, which the MiniPaged-Qwen page, section 19, names for
+# decode without a layout).  The pins build pools by scattering dense
+# sequences into shuffled blocks (the inverse of the gather), with every
+# other slot NaN, so a wrong block, slot or length shows as a wrong or NaN
+# value.
+
+def _scatter_paged(k_dense, lens, block_size, num_blocks, rng):
+    """Pool (num_blocks, block_size, H, d) of NaN holding sequence b's first
+    lens[b] rows of k_dense[b] in randomly chosen blocks; returns (pool,
+    block_table) with unused table entries -1."""
+    B, _, H, d = k_dense.shape
+    need = [-(-int(L) // block_size) for L in lens]
+    max_blocks = max(max(need), 1)
+    ids = rng.permutation(num_blocks)[:sum(need)]
+    pool = np.full((num_blocks, block_size, H, d), np.nan)
+    table = np.full((B, max_blocks), -1, np.int64)
+    n = 0
+    for b in range(B):
+        for j in range(need[b]):
+            table[b, j] = ids[n]
+            rows = k_dense[b, j * block_size:min((j + 1) * block_size, lens[b])]
+            pool[ids[n], :rows.shape[0]] = rows
+            n += 1
+    return pool, table
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_paged_gather_equals_dense_per_sequence(causal):
+    from oracle import attn_decode_paged_oracle
+    rng = np.random.default_rng(31)
+    B, Sq, Hq, Hkv, d, bs = 4, 3, 4, 2, 8, 4
+    lens = [13, 4, 1, 9]
+    Smax = max(lens)
+    q = rng.standard_normal((B, Sq, Hq, d))
+    k = rng.standard_normal((B, Smax, Hkv, d))
+    v = rng.standard_normal((B, Smax, Hkv, d))
+    kp, table = _scatter_paged(k, lens, bs, 20, rng)
+    # V goes into a pool of its own at the same block ids (one table)
+    vp = np.full_like(kp, np.nan)
+    for b in range(B):
+        for t in range(lens[b]):
+            vp[table[b, t // bs], t % bs] = v[b, t]
+    o, lse = attn_decode_paged_oracle(q, kp, vp, table, lens, 0.4, causal)
+    assert np.all(np.isfinite(o))
+    for b in range(B):
+        L = lens[b]
+        ob, lb = attn_fwd_oracle(q[b:b + 1], k[b:b + 1, :L], v[b:b + 1, :L], 0.4, causal)
+        np.testing.assert_array_equal(o[b], ob[0])
+        np.testing.assert_array_equal(lse[b], lb[0])
+
+
+def test_paged_brute_force_python_loops():
+    """Scores, softmax and P V with Python loops, reading the pool through
+    the table directly (no gather, no dense oracle)."""
+    from oracle import attn_decode_paged_oracle
+    rng = np.random.default_rng(32)
+    B, Sq, Hq, Hkv, d, bs = 2, 2, 2, 1, 3, 2
+    lens = [5, 3]
+    kp = rng.standard_normal((6, bs, Hkv, d))
+    vp = rng.standard_normal((6, bs, Hkv, d))
+    table = np.array([[4, 0, 2], [5, 1, -1]])
+    q = rng.standard_normal((B, Sq, Hq, d))
+    scale = 0.7
+    o, lse = attn_decode_paged_oracle(q, kp, vp, table, lens, scale, True)
+    for b in range(B):
+        L = lens[b]
+        for h in range(Hq):
+            for i in range(Sq):
+                pos = L - Sq + i  # the query's position in its sequence
+                s = []
+                for j in range(pos + 1):
+                    kr = kp[table[b, j // bs], j % bs, 0]
+                    s.append(scale * sum(q[b, i, h, c] * kr[c] for c in range(d)))
+                m = max(s)
+                den = sum(math.exp(x - m) for x in s)
+                for c in range(d):
+                    num = sum(math.exp(s[j] - m) * vp[table[b, j // bs], j % bs, 0, c]
+                              for j in range(pos + 1))
+                    assert abs(o[b, i, h, c] - num / den) < 1e-12
+                assert abs(lse[b, h, i] - (m + math.log(den))) < 1e-12
+
+
+def test_paged_empty_short_and_clamped_lengths():
+    from oracle import attn_decode_paged_oracle
+    rng = np.random.default_rng(33)
+    B, Sq, Hq, Hkv, d, bs = 3, 4, 2, 2, 4, 4
+    kp = rng.standard_normal((8, bs, Hkv, d))
+    vp = rng.standard_normal((8, bs, Hkv, d))
+    table = np.array([[0, 1, 2], [3, 4, 5], [6, 7, 0]])
+    q = rng.standard_normal((B, Sq, Hq, d))
+    # length 0 and a negative length: no key at all
+    o, lse = attn_decode_paged_oracle(q, kp, vp, table, [0, -3, 2], 0.5, True)
+    assert np.all(o[:2] == 0) and np.all(lse[:2] == -np.inf)
+    # length 2 < Sq = 4, causal: query i sees keys j <= i - 2, so rows 0 and 1
+    # see nothing, row 2 sees key 0 (o = v of token 0), row 3 sees keys 0, 1
+    assert np.all(o[2, :2] == 0) and np.all(lse[2, :, :2] == -np.inf)
+    v0 = vp[6, 0]  # token 0 of sequence 2: block 6, slot 0
+    np.testing.assert_allclose(o[2, 2], v0, rtol=0, atol=1e-15)
+    # non-causal: every row sees both keys
+    o2, lse2 = attn_decode_paged_oracle(q, kp, vp, table, [0, -3, 2], 0.5, False)
+    assert np.all(np.isfinite(lse2[2]))
+    # lengths above max_seqlen are taken as max_seqlen
+    oa, la = attn_decode_paged_oracle(q, kp, vp, table, [10, 12, 7], 0.5, True, max_seqlen=6)
+    ob, lb = attn_decode_paged_oracle(q, kp, vp, table, [6, 6, 6], 0.5, True)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_paged_identity_table_is_dense_layout():
+    """With block_size = S and table[b] = [b], the pool is the dense (B, S,
+    Hkv, d) K array itself: the paged result is attn_fwd_oracle's."""
+    from oracle import attn_decode_paged_oracle
+    rng = np.random.default_rng(34)
+    B, Sq, S, Hq, Hkv, d = 3, 2, 11, 4, 1, 8
+    q = rng.standard_normal((B, Sq, Hq, d))
+    k = rng.standard_normal((B, S, Hkv, d))
+    v = rng.standard_normal((B, S, Hkv, d))
+    o, lse = attn_decode_paged_oracle(q, k, v, np.arange(B)[:, None], [S] * B, 0.3, True)
+    od, ld = attn_fwd_oracle(q, k, v, 0.3, True)
+    np.testing.assert_array_equal(o, od)
+    np.testing.assert_array_equal(lse, ld)
