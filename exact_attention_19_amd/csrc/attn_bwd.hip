@@ -18,10 +18,11 @@
 //   dq     query-row outer, like the forward: one wave owns 32 query rows,
 //          K and V tiles stream through LDS, dQ^T = K^T dS^T accumulates in
 //          registers,
-//   dkdv   key outer: one wave owns 32 keys of one kv head, the Q and dO
-//          tiles of every query row (and every query head of the GQA group)
-//          that sees them stream through LDS, dK^T = Q^T dS and dV^T = dO^T P
-//          accumulate in registers.
+//   dkdv   key outer: two waves own 32 keys of one kv head (each half of
+//          the rows of every query tile), the Q and dO tiles of every query
+//          row (and every query head of the GQA group) that sees them stream
+//          through LDS, dK^T = Q^T dS and dV^T = dO^T P accumulate in
+//          registers and the two halves are added at the end.
 // Each gradient element is written once by one lane: no atomics, and the
 // results do not depend on scheduling.
 //
@@ -274,24 +275,36 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
 
 // ------------------------------------------------------------ dK, dV
 //
-// Workgroup: 4 waves x 32 keys = 128 keys of one (batch, kv head).  It walks
-// the query tiles (64 rows) that see any of its keys, for every query head
-// of the kv head's group; tile t of the walk sits in LDS buffer t & 1 (Q and
-// dO tiles double-buffered, with the rows' lse * log2(e) and D).
+// Workgroup: 8 waves over 128 keys of one (batch, kv head).  Wave w owns the
+// 32 keys 32 (w & 3) .. +31 and, of every 64-row query tile, the rows
+// 32 (w >> 2) .. +31: the two waves of a key group run on one SIMD side by
+// side (one's softmax beside the other's MFMAs) and split the rows, and
+// their dK/dV partial sums are added through LDS at the end.  The keys' K
+// and V rows stay in LDS for the whole walk (the B operands of S and dP,
+// read as row fragments).  The walk covers the query tiles that see any of
+// the keys, for every query head of the kv head's group; tile t sits in LDS
+// buffer t & 1 (Q and dO double-buffered, with the rows' lse * log2(e) and
+// D).
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   using T = Ty<DT>;
   constexpr int CB = D / 32;
   constexpr int KK = D / 16;
   constexpr int TB = 64 * D * 2;
   __shared__ __attribute__((aligned(1024))) char lds_q0[TB], lds_q1[TB], lds_o0[TB], lds_o1[TB];
+  __shared__ __attribute__((aligned(1024))) char lds_k[2][TB], lds_v[2][TB];
   __shared__ __attribute__((aligned(256))) float lds_l2[2][64], lds_d[2][64];
+  // a wave's dK (or dV) partial sums, CB x 16 floats per lane, fill exactly
+  // one tile buffer
+  static_assert(CB * 16 * 64 * 4 == TB, "reduction area = tile area");
   auto qbuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_q1 : (LDS_PTR(char))lds_q0; };
   auto obuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_o1 : (LDS_PTR(char))lds_o0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3;   // key group
+  const int qh = wave >> 2;  // row half of each query tile
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -302,22 +315,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int b = col / p.Hkv;
   const int kvh = col % p.Hkv;
   const int k0 = kblk * 128;
-  const int kj = k0 + wave * 32 + l32;
+  const int kj = k0 + kg * 32 + l32;  // this lane's key
   const bool kok = kj < p.Sk;
 
-  // this lane's key: K and V rows as B operands (d as k)
-  i16x8 kf[KK], vf[KK];
+  // K rows (waves 0-3) and V rows (waves 4-7) of the 128 keys into LDS, as
+  // two 64-row tiles each; a tile wholly past Sk is zeroed instead
   {
-    const int64_t r = ((int64_t)b * p.Sk + (kok ? kj : 0)) * p.Hkv + kvh;
+    const uint32_t rbk = (uint32_t)p.Hkv * D * 2;
+    const char* slice =
+        (const char*)((qh == 0 ? p.k : p.v) + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (kok) {
-        x = *(const u32x4*)(p.k + r * D + kk * 16 + hh * 8);
-        y = *(const u32x4*)(p.v + r * D + kk * 16 + hh * 8);
+    for (int i = 0; i < 2; ++i) {
+      LDS_PTR(char) const dst = (LDS_PTR(char))(qh == 0 ? lds_k[i] : lds_v[i]);
+      if (k0 + 64 * i < p.Sk) {
+        load_tile<D>(slice, rbk, 2 * kblk + i, p.Sk, dst, kg, lane);
+      } else {
+        LDS_PTR(u32x4) z = (LDS_PTR(u32x4))dst;
+        for (int e = kg * 64 + lane; e < TB / 16; e += 256) z[e] = (u32x4){0u, 0u, 0u, 0u};
       }
-      kf[kk] = __builtin_bit_cast(i16x8, x);
-      vf[kk] = __builtin_bit_cast(i16x8, y);
     }
   }
 
@@ -332,28 +347,38 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int steps = per_head * p.group;
   const uint32_t rbq = (uint32_t)p.Hq * D * 2;
 
+  // tile t: Q by waves 0-3, dO by waves 4-7, and the 64 rows' lse * log2(e)
+  // (wave 0) and D (wave 4), rows clamped to Sq - 1 (rows past Sq are
+  // masked below)
   auto issue = [&](int t) {
     const int h = kvh * p.group + t / per_head;
     const int qt = qt0 + t % per_head;
     const int64_t head0 = (int64_t)b * p.Sq * p.Hq + h;
-    load_tile<D>((const char*)(p.q + head0 * D), rbq, qt, p.Sq, qbuf(t), wave, lane);
-    load_tile<D>((const char*)(p.dout + head0 * D), rbq, qt, p.Sq, obuf(t), wave, lane);
-    // the 64 rows' lse * log2(e) (wave 0) and D (wave 1), rows clamped to
-    // Sq - 1 (rows past Sq are masked below)
-    if (wave < 2) {
-      const float* src = (wave == 0 ? p.l2 : p.dvec) + ((int64_t)b * p.Hq + h) * p.Sq;
+    load_tile<D>((const char*)((qh == 0 ? p.q : p.dout) + head0 * D), rbq, qt, p.Sq,
+                 qh == 0 ? qbuf(t) : obuf(t), kg, lane);
+    if (kg == 0) {
+      const float* src = (qh == 0 ? p.l2 : p.dvec) + ((int64_t)b * p.Hq + h) * p.Sq;
       const uint32_t r = (uint32_t)min(qt * 64 + lane, p.Sq - 1);
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, p.Sq * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (LDS_PTR(void))(wave == 0 ? &lds_l2[t & 1][0] : &lds_d[t & 1][0]), 4, r * 4, 0, 0,
-          0);
+          rs, (LDS_PTR(void))(qh == 0 ? &lds_l2[t & 1][0] : &lds_d[t & 1][0]), 4, r * 4, 0, 0, 0);
     }
   };
 
-  uint32_t rbase[2], tbase[2];
+  uint32_t rbase[2], tbase[2], kbase[2];
   row_frag_bases(lane, rbase);
   tr_frag_bases(lane, tbase);
+  {
+    // row fragments of the keys in natural order: lane l32 reads key row
+    // 32 (kg & 1) + l32 of K (V) tile kg >> 1, so its S and dP column is key kj
+    const int sw = (l32 >> 2) & 3;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      kbase[par] = (uint32_t)(l32 * 64 + (((2 * par + hh) ^ sw) << 4));
+  }
+  LDS_PTR(char) const ktile = (LDS_PTR(char))lds_k[kg >> 1];
+  LDS_PTR(char) const vtile = (LDS_PTR(char))lds_v[kg >> 1];
 
   f32x16 adk[CB], adv[CB];
 #pragma unroll
@@ -370,68 +395,92 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     __syncthreads();
     if (t + 1 < steps) issue(t + 1);
     const int qt = qt0 + t % per_head;
+    const int i0 = qt * 64 + 32 * qh;  // first query row of this wave
+    // rows that see none of the wave's keys, or lie past Sq: nothing to add
+    if (i0 >= p.Sq || (CAUSAL && i0 + 31 + p.off < k0 + 32 * kg)) continue;
     LDS_PTR(char) const qtile = qbuf(t);
     LDS_PTR(char) const otile = obuf(t);
     LDS_PTR(const float) const l2t = (LDS_PTR(const float)) & lds_l2[t & 1][0];
     LDS_PTR(const float) const dtt = (LDS_PTR(const float)) & lds_d[t & 1][0];
-    // rows of this tile need masking: a causal row that does not see every
-    // key of the wave, or a row past Sq
-    const int kmax = k0 + wave * 32 + 31;
-    const bool edge = (CAUSAL && qt * 64 + p.off < kmax) || qt * 64 + 64 > p.Sq;
+    // rows need masking: a causal row that does not see every key of the
+    // wave, or a row past Sq
+    const int kmax = k0 + 32 * kg + 31;
+    const bool edge = (CAUSAL && i0 + p.off < kmax) || i0 + 32 > p.Sq;
+    // S = Q K^T and dP = dO V^T: rows = the wave's 32 query rows in the
+    // sigma order, columns = its 32 keys (lane)
+    f32x16 S, dP;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // S = Q K^T and dP = dO V^T: rows = 32 query rows in the sigma order,
-      // columns = this wave's 32 keys (lane)
-      f32x16 S, dP;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        S[r] = 0.f;
-        dP[r] = 0.f;
-      }
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        S = T::mfma(read_row_frag(qtile, rbase, qb, kk), kf[kk], S);
-        dP = T::mfma(read_row_frag(otile, rbase, qb, kk), vf[kk], dP);
-      }
-      // register r holds query row 32qb + key_of_reg(r) + 8hh of the tile;
-      // registers 4g .. 4g+3 are 4 consecutive rows
-      i16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        f32x8 pe, de;
-#pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) {
-          const int g = 2 * f + g2;
-          const int row0 = 32 * qb + key_of_reg(4 * g) + 8 * hh;
-          const f32x4 l4 = *(LDS_PTR(const f32x4))(l2t + row0);
-          const f32x4 d4 = *(LDS_PTR(const f32x4))(dtt + row0);
-#pragma unroll
-          for (int r3 = 0; r3 < 4; ++r3) {
-            const int r = 4 * g + r3;
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -l4[r3]));
-            if (edge) {
-              const int qi = qt * 64 + row0 + r3;
-              if (qi >= p.Sq || (CAUSAL && kj > qi + p.off)) pr = 0.f;
-            }
-            pe[4 * g2 + r3] = pr;
-            de[4 * g2 + r3] = pr * (dP[r] - d4[r3]);
-          }
-        }
-        pf[f] = T::cvt(pe);
-        dsf[f] = T::cvt(de);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (two 16-row steps)
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          adv[cb] = T::mfma(read_tr_frag(otile, tbase, 2 * qb + f, cb), pf[f], adv[cb]);
-          adk[cb] = T::mfma(read_tr_frag(qtile, tbase, 2 * qb + f, cb), dsf[f], adk[cb]);
-        }
+    for (int r = 0; r < 16; ++r) {
+      S[r] = 0.f;
+      dP[r] = 0.f;
     }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint32_t ko = row_frag_off(kbase, kg & 1, kk);
+      S = T::mfma(read_row_frag(qtile, rbase, qh, kk), *(LDS_PTR(const i16x8))(ktile + ko), S);
+      dP = T::mfma(read_row_frag(otile, rbase, qh, kk), *(LDS_PTR(const i16x8))(vtile + ko), dP);
+    }
+    // register r holds query row 32 qh + key_of_reg(r) + 8 hh of the tile;
+    // registers 4g .. 4g+3 are 4 consecutive rows
+    i16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      f32x8 pe, de;
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int g = 2 * f + g2;
+        const int row0 = 32 * qh + key_of_reg(4 * g) + 8 * hh;
+        const f32x4 l4 = *(LDS_PTR(const f32x4))(l2t + row0);
+        const f32x4 d4 = *(LDS_PTR(const f32x4))(dtt + row0);
+#pragma unroll
+        for (int r3 = 0; r3 < 4; ++r3) {
+          const int r = 4 * g + r3;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -l4[r3]));
+          if (edge) {
+            const int qi = qt * 64 + row0 + r3;
+            if (qi >= p.Sq || (CAUSAL && kj > qi + p.off)) pr = 0.f;
+          }
+          pe[4 * g2 + r3] = pr;
+          de[4 * g2 + r3] = pr * (dP[r] - d4[r3]);
+        }
+      }
+      pf[f] = T::cvt(pe);
+      dsf[f] = T::cvt(de);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (two 16-row steps)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        adv[cb] = T::mfma(read_tr_frag(otile, tbase, 2 * qh + f, cb), pf[f], adv[cb]);
+        adk[cb] = T::mfma(read_tr_frag(qtile, tbase, 2 * qh + f, cb), dsf[f], adk[cb]);
+      }
   }
 
-  if (kok) {
+  // add the row halves: waves 4-7 hand their sums to waves 0-3 through LDS
+  // (dK into the K/V area, dV into the Q/dO area; lane-contiguous 16-byte
+  // slots)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  LDS_PTR(char) const red_k = (LDS_PTR(char))(kg < 2 ? lds_k[kg] : lds_v[kg - 2]);
+  LDS_PTR(char) const red_v = kg == 0   ? (LDS_PTR(char))lds_q0
+                              : kg == 1 ? (LDS_PTR(char))lds_q1
+                              : kg == 2 ? (LDS_PTR(char))lds_o0
+                                        : (LDS_PTR(char))lds_o1;
+  if (qh == 1) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t o = (uint32_t)(((cb * 4 + g) * 64 + lane) * 16);
+        *(LDS_PTR(f32x4))(red_k + o) =
+            (f32x4){adk[cb][4 * g], adk[cb][4 * g + 1], adk[cb][4 * g + 2], adk[cb][4 * g + 3]};
+        *(LDS_PTR(f32x4))(red_v + o) =
+            (f32x4){adv[cb][4 * g], adv[cb][4 * g + 1], adv[cb][4 * g + 2], adv[cb][4 * g + 3]};
+      }
+  }
+  __syncthreads();
+  if (qh == 0 && kok) {
     const int64_t r = ((int64_t)b * p.Sk + kj) * p.Hkv + kvh;
     uint16_t* dkrow = p.dk + r * D;
     uint16_t* dvrow = p.dv + r * D;
@@ -439,11 +488,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        const uint32_t o = (uint32_t)(((cb * 4 + g) * 64 + lane) * 16);
+        const f32x4 ok = *(LDS_PTR(const f32x4))(red_k + o);
+        const f32x4 ov = *(LDS_PTR(const f32x4))(red_v + o);
         f32x8 x, y;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          x[r4] = adk[cb][4 * g + r4] * p.scale;
-          y[r4] = adv[cb][4 * g + r4];
+          x[r4] = (adk[cb][4 * g + r4] + ok[r4]) * p.scale;
+          y[r4] = adv[cb][4 * g + r4] + ov[r4];
           x[r4 + 4] = 0.f;
           y[r4 + 4] = 0.f;
         }
@@ -497,7 +549,7 @@ hipError_t launch_bwd_t(const Plan& pl, const BwdParams& p, hipStream_t st) {
                      0, st, p);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3(pl.grid), dim3(256), 0, st, p);
   const long long kgrid = (long long)p.B * p.Hkv * ((p.Sk + 127) / 128);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)kgrid), dim3(256), 0,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)kgrid), dim3(512), 0,
                      st, p);
   return hipGetLastError();
 }
