@@ -350,9 +350,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   // tile t: Q by waves 0-3, dO by waves 4-7, and the 64 rows' lse * log2(e)
   // (wave 0) and D (wave 4), rows clamped to Sq - 1 (rows past Sq are
   // masked below)
+  // walk position of the next tile to load: query head kvh * group + nh,
+  // tile qt0 + nq (counters, not divisions: the scalar unit is busy enough)
+  int nh = 0, nq = 0;
   auto issue = [&](int t) {
-    const int h = kvh * p.group + t / per_head;
-    const int qt = qt0 + t % per_head;
+    const int h = kvh * p.group + nh;
+    const int qt = qt0 + nq;
     const int64_t head0 = (int64_t)b * p.Sq * p.Hq + h;
     load_tile<D>((const char*)((qh == 0 ? p.q : p.dout) + head0 * D), rbq, qt, p.Sq,
                  qh == 0 ? qbuf(t) : obuf(t), kg, lane);
@@ -390,11 +393,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     }
 
   if (steps > 0) issue(0);
+  int cq = 0;  // tile index within its head of the tile being computed
   for (int t = 0; t < steps; ++t) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < steps) issue(t + 1);
-    const int qt = qt0 + t % per_head;
+    if (t + 1 < steps) {
+      if (++nq == per_head) {
+        nq = 0;
+        ++nh;
+      }
+      issue(t + 1);
+    }
+    const int qt = qt0 + cq;
+    if (++cq == per_head) cq = 0;
     const int i0 = qt * 64 + 32 * qh;  // first query row of this wave
     // rows that see none of the wave's keys, or lie past Sq: nothing to add
     if (i0 >= p.Sq || (CAUSAL && i0 + 31 + p.off < k0 + 32 * kg)) continue;
