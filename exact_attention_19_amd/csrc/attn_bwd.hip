@@ -446,13 +446,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int r3 = 0; r3 < 4; ++r3) {
           const int r = 4 * g + r3;
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -l4[r3]));
-          if (edge) {
-            const int qi = qt * 64 + row0 + r3;
-            if (qi >= p.Sq || (CAUSAL && kj > qi + p.off)) pr = 0.f;
-          }
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -l4[r3]));
           pe[4 * g2 + r3] = pr;
           de[4 * g2 + r3] = pr * (dP[r] - d4[r3]);
+        }
+      }
+      // masked rows and keys, in one branch per 8 scores (a test per score
+      // would cut the body into a branch per score); the empty volatile asm
+      // keeps it a branch, so that tiles without masked scores skip the
+      // compares instead of running them under a select
+      if (edge) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int qi = qt * 64 + 32 * qh + key_of_reg(4 * (2 * f + e / 4)) + 8 * hh + e % 4;
+          if (qi >= p.Sq || (CAUSAL && kj > qi + p.off)) {
+            pe[e] = 0.f;
+            de[e] = 0.f;
+          }
         }
       }
       pf[f] = T::cvt(pe);
