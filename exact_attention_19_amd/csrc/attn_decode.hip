@@ -280,7 +280,11 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
   const float lr_tot = pair_sum(l_rnd);
   const float lf_tot = T::LSE_FROM_FP32_SUM ? pair_sum(l_fp32) : lr_tot;
   __syncthreads();  // every wave is done with its V stages: reuse them
-  float* mo = (float*)&lds_v[0][0][0];  // [wave][row][D]
+  // [wave][row][D] floats; the float4 at column c of row r sits at column
+  // c ^ 4 (r % 16), so that 16 rows written at one column, and one row read
+  // by 16 lanes, each fill all 64 banks once
+  float* mo = (float*)&lds_v[0][0][0];
+  auto mo_at = [&](int row, int c) { return mo + row * D + (c ^ ((row & 15) << 2)); };
   if (hh == 0) {
     lds_m[wave][l32] = m_run;
     lds_lr[wave][l32] = lr_tot;
@@ -294,13 +298,14 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
       f32x4 x;
 #pragma unroll
       for (int q = 0; q < 4; ++q) x[q] = acc[cb][4 * g4 + q];
-      *(f32x4*)(mo + ((wave * 32 + l32) * D + 32 * cb + 8 * g4 + 4 * hh)) = x;
+      *(f32x4*)mo_at(wave * 32 + l32, 32 * cb + 8 * g4 + 4 * hh) = x;
     }
   __syncthreads();
-  // thread: row tid / 8, columns (tid % 8) * D / 8 .. + D / 8
-  {
-    const int rr = tid >> 3;
-    const int c0 = (tid & 7) * (D / 8);
+  // thread: rows tid / 16 and tid / 16 + 16, float4 columns 4 (tid % 16) + 64 j
+  const int l16 = tid & 15;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rr = (tid >> 4) + 16 * pass;
     if (rr < M) {
       float mmax = -1e30f;
 #pragma unroll
@@ -317,34 +322,43 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
       const float lse = has ? (mmax + __builtin_amdgcn_logf(lf_s)) * LN2 : -INFINITY;
       const int h = kvh * g + rr / p.Sq;
       const int i = rr % p.Sq;
-      if (p.part_o == nullptr) {
-        uint16_t* orow = p.o + (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh;
+      uint16_t* orow = p.o + (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh;
+      // a piece of a split key range writes its fp32 state normalised over
+      // its keys instead
+      float* prow = p.part_o == nullptr
+                        ? nullptr
+                        : p.part_o + ((((int64_t)piece * p.B + b) * p.Sq + i) * p.Hq + h) * D;
 #pragma unroll
-        for (int c = 0; c < D / 8; c += 8) {
+      for (int j = 0; j < D / 64; ++j) {
+        const int c = 4 * l16 + 64 * j;
+        f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x4 y = *(const f32x4*)mo_at(w * 32 + rr, c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc4[e] += wgt[w] * y[e];
+        }
+        if (prow == nullptr) {
           f32x8 x;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float s = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) s += wgt[w] * mo[(w * 32 + rr) * D + c0 + c + e];
-            x[e] = s * inv;
+          for (int e = 0; e < 4; ++e) {
+            x[e] = acc4[e] * inv;
+            x[e + 4] = 0.f;
           }
-          *(i16x8*)(orow + c0 + c) = T::cvt(x);
+          const i16x8 hv = T::cvt(x);
+          const u32x2 w2 = {(unsigned)(uint16_t)hv[0] | ((unsigned)(uint16_t)hv[1] << 16),
+                            (unsigned)(uint16_t)hv[2] | ((unsigned)(uint16_t)hv[3] << 16)};
+          *(u32x2*)(orow + c) = w2;
+        } else {
+          *(f32x4*)(prow + c) = acc4 * inv;
         }
-        if (p.lse != nullptr && (tid & 7) == 0)
-          p.lse[((int64_t)b * p.Hq + h) * p.Sq + i] = lse;
-      } else {
-        // a piece of a split key range: fp32 state normalised over its keys
-        float* prow = p.part_o + ((((int64_t)piece * p.B + b) * p.Sq + i) * p.Hq + h) * D;
-#pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-          float s = 0.f;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) s += wgt[w] * mo[(w * 32 + rr) * D + c0 + c];
-          prow[c0 + c] = s * inv;
-        }
-        if ((tid & 7) == 0)
+      }
+      if (l16 == 0) {
+        if (prow == nullptr) {
+          if (p.lse != nullptr) p.lse[((int64_t)b * p.Hq + h) * p.Sq + i] = lse;
+        } else {
           p.part_lse[(((int64_t)piece * p.B + b) * p.Hq + h) * p.Sq + i] = lse;
+        }
       }
     }
   }
