@@ -287,6 +287,11 @@ using attn_detail::launch_decode;
 
 // The decode kernel takes shapes whose query rows per kv head fit one wave
 // (g * Sq <= 32) at d = 64 or 128.
+// Waves per decode workgroup, each walking its own key tiles.  Measured on
+// MI355X: 4 (two workgroups per CU) stream K and V at 5.5 TB/s; 8 (one
+// workgroup of two waves per SIMD) were 1-5 % slower.
+constexpr int DEC_WAVES = 4;
+
 inline bool decode_eligible(int Sq, int Hq, int Hkv, int d) {
   return (long long)(Hq / Hkv) * Sq <= 32 && (d == 64 || d == 128);
 }

@@ -11,9 +11,9 @@
 //   GQA group and every new token -- are the 32 rows of ONE wave: row r is
 //   query head h0 + r / Sq, token r % Sq.  The prefill kernel would give each
 //   query head its own 32-row wave, mostly empty.
-// * The 4 waves of a workgroup walk different 32-key tiles of the key range
-//   (tile w, w + 4, ...), each with its own softmax state, and the states are
-//   merged through LDS at the end (the online-softmax rescale).  A key range
+// * The DEC_WAVES (4) waves of a workgroup walk different 32-key tiles of the
+//   key range (tile w, w + 4, ...), each with its own softmax state, and the
+//   states are merged through LDS at the end (the online-softmax rescale).  A key range
 //   can further be cut into pieces over workgroups, merged by the merge
 //   kernel, when (batch, kv head) pairs are too few to fill the GPU.
 // * The work is bound by reading K and V: K rows go straight from global
@@ -34,17 +34,18 @@ constexpr int DBC = 32;                    // keys per tile
 constexpr float DEC_RESCALE_TAU = 8.0f;    // lazy max update, as the prefill kernel
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_kernel(DecodeArgs p) {
   using T = Ty<DT>;
   constexpr int CB = D / 32;
   constexpr int KK = D / 16;
   constexpr int VBLK = DBC * 64;           // bytes per 32-column block of a V tile
   constexpr int VTB = DBC * D * 2;         // bytes per V tile
-  // per wave: two V tile stages; reused at the end for the merge (4 x 32
+  constexpr int NW = DEC_WAVES;
+  // per wave: two V tile stages; reused at the end for the merge (NW x 32
   // rows x D floats = exactly the same size)
-  __shared__ __attribute__((aligned(1024))) char lds_v[4][2][VTB];
-  __shared__ float lds_m[4][32], lds_lr[4][32], lds_lf[4][32];
-  static_assert(4 * 2 * VTB == 4 * 32 * D * 4, "merge area = tile area");
+  __shared__ __attribute__((aligned(1024))) char lds_v[NW][2][VTB];
+  __shared__ float lds_m[NW][32], lds_lr[NW][32], lds_lf[NW][32];
+  static_assert(NW * 2 * VTB == NW * 32 * D * 4, "merge area = tile area");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
   if (CAUSAL) lim = min(lim, qi + Sk - p.Sq);
   if (!rok) lim = -1;
 
-  // the piece's tiles [t_lo, t_hi); this wave takes t_lo + wave, + 4, ...
+  // the piece's tiles [t_lo, t_hi); this wave takes t_lo + wave, + NW, ...
   const int ntiles = (Sk + DBC - 1) / DBC;
   const int t_lo = piece * p.piece_tiles;
   const int t_hi = min(ntiles, t_lo + p.piece_tiles);
@@ -244,34 +245,34 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
   constexpr int VMN = KK + 2 * CB;
   constexpr int VM_NEXT = 0x0F70 | (VMN & 15) | ((VMN >> 4) << 14);
   static_assert(VMN < 64, "vmcnt range");
-  // tiles n, n + 4, ... alternate between the (kA, stage 0) and (kB,
+  // tiles n, n + NW, ... alternate between the (kA, stage 0) and (kB,
   // stage 1) register/LDS sets, so the loop body is unrolled by two
-  for (; n < t_end; n += 8) {
-    if (n + 4 < t_end) {
-      const int64_t r0 = tile_row(n + 4);
-      load_k(n + 4, r0, kB);
-      load_v(n + 4, r0, vb1);
+  for (; n < t_end; n += 2 * NW) {
+    if (n + NW < t_end) {
+      const int64_t r0 = tile_row(n + NW);
+      load_k(n + NW, r0, kB);
+      load_v(n + NW, r0, vb1);
     }
     // K(n) and V(n) (issued one tile earlier) have landed: wait for all but
     // the loads just issued
-    if (n + 4 < t_end)
+    if (n + NW < t_end)
       __builtin_amdgcn_s_waitcnt(VM_NEXT);  // vmcnt(KK + 2 CB)
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     tile(n, kA, vb0);
-    if (n + 4 >= t_end) break;
-    if (n + 8 < t_end) {
-      const int64_t r0 = tile_row(n + 8);
-      load_k(n + 8, r0, kA);
-      load_v(n + 8, r0, vb0);
+    if (n + NW >= t_end) break;
+    if (n + 2 * NW < t_end) {
+      const int64_t r0 = tile_row(n + 2 * NW);
+      load_k(n + 2 * NW, r0, kA);
+      load_v(n + 2 * NW, r0, vb0);
       __builtin_amdgcn_s_waitcnt(VM_NEXT);
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
-    tile(n + 4, kB, vb1);
+    tile(n + NW, kB, vb1);
   }
 
-  // ---- merge the 4 waves' states through LDS
+  // ---- merge the NW waves' states through LDS
   auto pair_sum = [](float x) {
     auto rr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                false);
@@ -301,18 +302,19 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
       *(f32x4*)mo_at(wave * 32 + l32, 32 * cb + 8 * g4 + 4 * hh) = x;
     }
   __syncthreads();
-  // thread: rows tid / 16 and tid / 16 + 16, float4 columns 4 (tid % 16) + 64 j
+  // thread: rows tid / 16 (+ 4 NW per pass), float4 columns 4 (tid % 16) + 64 j
   const int l16 = tid & 15;
+  constexpr int RPP = 4 * NW;  // rows per pass
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int rr = (tid >> 4) + 16 * pass;
+  for (int pass = 0; pass < 32 / RPP; ++pass) {
+    const int rr = (tid >> 4) + RPP * pass;
     if (rr < M) {
       float mmax = -1e30f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) mmax = fmaxf(mmax, lds_m[w][rr]);
-      float wgt[4], lr_s = 0.f, lf_s = 0.f;
+      for (int w = 0; w < NW; ++w) mmax = fmaxf(mmax, lds_m[w][rr]);
+      float wgt[NW], lr_s = 0.f, lf_s = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         wgt[w] = __builtin_amdgcn_exp2f(lds_m[w][rr] - mmax);
         lr_s += wgt[w] * lds_lr[w][rr];
         lf_s += wgt[w] * lds_lf[w][rr];
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
         const int c = 4 * l16 + 64 * j;
         f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
           const f32x4 y = *(const f32x4*)mo_at(w * 32 + rr, c);
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc4[e] += wgt[w] * y[e];
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecodeArgs p) {
 
 template <int DT, int D>
 hipError_t launch_decode_d(bool causal, const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)a.grid), block(256);
+  const dim3 grid((unsigned)a.grid), block(DEC_WAVES * 64);
   if (causal)
     hipLaunchKernelGGL((attn_decode_kernel<DT, D, true>), grid, block, 0, st, a);
   else

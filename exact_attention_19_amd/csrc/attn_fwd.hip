@@ -1048,9 +1048,10 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
                   pl.lds_bytes, pl.xcd_cols > 0 ? 1 : 0, pl.pipelined, 0};
   if (decode_eligible(Sq, Hq, Hkv, d)) {
     // the decode kernel, unsplit: a workgroup per (batch, kv head) with all
-    // g * Sq rows in one wave, 4 waves over the keys
+    // g * Sq rows in one wave, DEC_WAVES waves over the keys
     const int g = Hq / Hkv;
-    const int vals_dec[10] = {B * Hkv, 256, Sq, 32, g, 32, 4 * 2 * 32 * d * 2, 0, 0, 1};
+    const int vals_dec[10] = {B * Hkv, DEC_WAVES * 64, Sq, 32, g, 32,
+                              DEC_WAVES * 2 * 32 * d * 2, 0, 0, 1};
     for (int i = 0; i < 10; ++i) vals[i] = vals_dec[i];
   }
   for (int i = 0; i < n && i < 10; ++i) out[i] = vals[i];
