@@ -38,7 +38,7 @@ struct DecodeArgs {
   // sequence b are row (block_table[b][t / block_size] * block_size +
   // t % block_size) of the pools, whose rows are k_ss / v_ss elements apart
   // (k_sb, v_sb unused); sequence b has min(seqlens[b], Sk) keys, and Sk
-  // is at most max_blocks * block_size
+  // is at most max_blocks * block_size; block_size is a multiple of 16
   const int* block_table;  // [B][max_blocks]
   const int* seqlens;      // [B]
   int block_size, max_blocks, num_blocks;

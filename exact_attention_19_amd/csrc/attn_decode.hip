@@ -100,27 +100,38 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
       (const char*)(p.v + (paged ? 0 : (int64_t)b * p.v_sb) + (int64_t)kvh * p.v_sh);
   const uint32_t rbk = (uint32_t)(p.k_ss * 2);
   const uint32_t rbv = (uint32_t)(p.v_ss * 2);
-  // row (of the K and V row arrays) of the first key of tile n: the tile's
-  // 32 keys are consecutive rows (block_size is a multiple of 32)
-  // (the entry is read through the constant address space with a
-  // wave-uniform index, so it is a scalar load: a vector load would join the
-  // vmcnt queue of the K/V tiles in flight and force a wait on all of them)
+  // Rows (of the K and V row arrays) of the two 16-key halves of tile n:
+  // each half is 16 consecutive rows (block_size is a multiple of 16).  r1
+  // is meaningful only when the second half holds a key below Sk.  A table
+  // entry is read through the constant address space with a wave-uniform
+  // index, so it is a scalar load: a vector load would join the vmcnt queue
+  // of the K/V tiles in flight and force a wait on all of them.
+  struct TileRows {
+    int64_t r0, r1;
+  };
   using const_int = const __attribute__((address_space(4))) int;
-  auto tile_row = [&](int n) -> int64_t {
-    if (!paged) return (int64_t)n * DBC;
-    const int t0 = n * DBC;
-    const int idx = __builtin_amdgcn_readfirstlane(b * p.max_blocks + t0 / p.block_size);
+  auto row_of = [&](int t) -> int64_t {  // paged: pool row of token t
+    const int idx = __builtin_amdgcn_readfirstlane(b * p.max_blocks + t / p.block_size);
     int blk = ((const_int*)p.block_table)[idx];
     blk = min(max(blk, 0), p.num_blocks - 1);
-    return (int64_t)blk * p.block_size + t0 % p.block_size;
+    return (int64_t)blk * p.block_size + t % p.block_size;
+  };
+  auto tile_rows = [&](int n) -> TileRows {
+    const int t0 = n * DBC;
+    if (!paged) return {(int64_t)t0, (int64_t)t0 + 16};
+    if (t0 > Sk - 1) return {0, 0};  // a tile past the sequence: no table read
+    const int64_t r0 = row_of(t0);
+    if (t0 + 16 > Sk - 1) return {r0, r0};              // no key in the second half
+    if (t0 % p.block_size + 16 < p.block_size) return {r0, r0 + 16};  // same block
+    return {r0, row_of(t0 + 16)};
   };
 
-  // K fragments of tile n (first row `row0`): key row sigma(l32) of the
-  // tile, chunks kk
-  auto load_k = [&](int n, int64_t row0, i16x8 (&kf)[KK]) {
-    const int key = min(n * DBC + sigma(l32), Sk - 1);
-    const uint16_t* krow =
-        (const uint16_t*)(kbase + (row0 + (key - n * DBC)) * (int64_t)rbk);
+  // K fragments of tile n: key row sigma(l32) of the tile (the last key for
+  // lanes past Sk), chunks kk
+  auto load_k = [&](int n, const TileRows& tr, i16x8 (&kf)[KK]) {
+    const int kidx = min(n * DBC + sigma(l32), Sk - 1) - n * DBC;  // 0 .. 31
+    const int64_t row = (kidx >= 16 ? tr.r1 : tr.r0) + (kidx & 15);
+    const uint16_t* krow = (const uint16_t*)(kbase + row * (int64_t)rbk);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       kf[kk] = __builtin_bit_cast(i16x8, *(const u32x4*)(krow + kk * 16 + hh * 8));
@@ -128,16 +139,21 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
   // V tile n -> this wave's LDS stage: column-blocked, 32 rows x 64 bytes per
   // block, chunk c of row r at slot c ^ ((r >> 2) & 3); round u covers block
   // u >> 1, rows 16 (u & 1) + lane / 4
-  auto load_v = [&](int n, int64_t row0, LDS_PTR(char) buf) {
+  // (rows past Sk re-read the last key's row, whose values are finite)
+  auto load_v = [&](int n, const TileRows& tr, LDS_PTR(char) buf) {
     const int row = lane >> 2;
     const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-    const char* tile = vbase + row0 * (int64_t)rbv;
+    const int last = Sk - 1 - n * DBC;  // last key of the tile, relative (>= 0)
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int rr = min(n * DBC + 16 * h2 + row, Sk - 1) - n * DBC;
+      // half h2 from its own 16 rows, or (second half wholly past Sk) the
+      // first half's last key
+      const bool own = h2 == 0 || last >= 16;
+      const int64_t base = (h2 == 0 || !own) ? tr.r0 : tr.r1;
+      const int rr = own ? min(row, last - 16 * h2) : last;
       const uint32_t off = (uint32_t)rr * rbv + (uint32_t)chunk * 16;
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)(DBC * rbv), 0x00020000);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(vbase + base * (int64_t)rbv), 0, (int)(16 * rbv), 0x00020000);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -177,9 +193,9 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
   int n = t_lo + wave;
   i16x8 kA[KK], kB[KK];
   if (n < t_end) {
-    const int64_t r0 = tile_row(n);
-    load_k(n, r0, kA);
-    load_v(n, r0, vb0);
+    const TileRows tr = tile_rows(n);
+    load_k(n, tr, kA);
+    load_v(n, tr, vb0);
   }
   // one tile: kf holds K(n), vbuf V(n); the next tile's loads are in flight
   auto tile = [&](int nn, const i16x8 (&kf)[KK], LDS_PTR(char) vbuf) {
@@ -247,12 +263,16 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
   static_assert(VMN < 64, "vmcnt range");
   // tiles n, n + NW, ... alternate between the (kA, stage 0) and (kB,
   // stage 1) register/LDS sets, so the loop body is unrolled by two
+  // The pool rows of a tile (table reads, when paged) are looked up one
+  // tile before its loads are issued, so the scalar loads land during the
+  // tile in between.
+  TileRows trB = tile_rows(n + NW < t_end ? n + NW : n);
   for (; n < t_end; n += 2 * NW) {
     if (n + NW < t_end) {
-      const int64_t r0 = tile_row(n + NW);
-      load_k(n + NW, r0, kB);
-      load_v(n + NW, r0, vb1);
+      load_k(n + NW, trB, kB);
+      load_v(n + NW, trB, vb1);
     }
+    const TileRows trA = tile_rows(n + 2 * NW < t_end ? n + 2 * NW : n);
     // K(n) and V(n) (issued one tile earlier) have landed: wait for all but
     // the loads just issued
     if (n + NW < t_end)
@@ -262,13 +282,13 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
     tile(n, kA, vb0);
     if (n + NW >= t_end) break;
     if (n + 2 * NW < t_end) {
-      const int64_t r0 = tile_row(n + 2 * NW);
-      load_k(n + 2 * NW, r0, kA);
-      load_v(n + 2 * NW, r0, vb0);
+      load_k(n + 2 * NW, trA, kA);
+      load_v(n + 2 * NW, trA, vb0);
       __builtin_amdgcn_s_waitcnt(VM_NEXT);
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
+    trB = tile_rows(n + 3 * NW < t_end ? n + 3 * NW : n);
     tile(n + NW, kB, vb1);
   }
 

@@ -1190,7 +1190,7 @@ attn_status attn_decode_paged_check(const void* q, const void* k_cache, const vo
                                     int max_seqlen, float scale, int causal, int dtype) {
   if (!q || !k_cache || !v_cache || !block_table || !seqlens || !o) return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Sq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
-  if (num_blocks < 1 || max_blocks < 1 || block_size < 32 || block_size % 32 != 0)
+  if (num_blocks < 1 || max_blocks < 1 || block_size < 16 || block_size % 16 != 0)
     return ATTN_ERR_INVALID_ARG;
   if (max_seqlen < 1 || (long long)max_seqlen > (long long)max_blocks * block_size)
     return ATTN_ERR_INVALID_ARG;

@@ -319,7 +319,7 @@ attn_status attn_bwd_workspace(int B, int Sq, int Hq, size_t* bytes);
  *                max_seqlen is taken as max_seqlen
  *   o, lse       as for attn_fwd: (B, Sq, Hq, d); lse (B, Hq, Sq) fp32 or NULL
  *   num_blocks   >= 1 blocks in each pool
- *   block_size   tokens per block, a multiple of 32
+ *   block_size   tokens per block, a multiple of 16
  *   max_blocks   >= 1 columns of the block table
  *   max_seqlen   the longest length to cover, 1 .. max_blocks * block_size;
  *                it sizes the key split (no device read of seqlens is made)

@@ -423,6 +423,8 @@ def test_paged_decode_validation():
     assert _pcheck() == ATTN_OK
     assert _pcheck(d=64, dtype=ATTN_DTYPE_F16, causal=0, Sq=8, Hq=16, Hkv=4) == ATTN_OK
     assert _pcheck(block_size=32, max_seqlen=20 * 32) == ATTN_OK
+    assert _pcheck(block_size=16, max_seqlen=20 * 16) == ATTN_OK
+    assert _pcheck(block_size=48, max_seqlen=20 * 48) == ATTN_OK
     for i in range(7):
         p = [A + 0x1000 * j for j in range(7)]
         if i != 6:  # lse may be NULL
@@ -435,7 +437,7 @@ def test_paged_decode_validation():
     p[6] = None
     assert _pcheck(p) == ATTN_OK
     for over in (dict(Hq=30), dict(B=0), dict(Sq=0), dict(num_blocks=0), dict(max_blocks=0),
-                 dict(block_size=16), dict(block_size=48), dict(max_seqlen=0),
+                 dict(block_size=8), dict(block_size=24), dict(block_size=0), dict(max_seqlen=0),
                  dict(max_seqlen=20 * 64 + 1), dict(scale=0.0), dict(causal=2)):
         assert _pcheck(**over) == ATTN_ERR_INVALID_ARG, over
     # outside the decode kernel's shapes: (Hq / Hkv) * Sq > 32, d not 64/128

@@ -5,8 +5,10 @@ keys gathered through its block table, then the dense forward).
 The caches come from make_paged_cache: each sequence's blocks scattered over
 a shuffled pool whose unused slots hold NaN, so a read of a wrong block, slot
 or of a token past a sequence's length shows as a wrong or NaN output.
-Sequences have ragged lengths (1, 31, 32, 33, block multiples, thousands, 0),
-the block sizes are 32 to 256, and the key range is split or not.
+Sequences have ragged lengths (1, 15, 16, 17, 31, 32, 33, block multiples,
+thousands, 0), the block sizes are 16 to 256 (16 and 48 put the two 16-key
+halves of a 32-key tile in different blocks), and the key range is split or
+not.
 Tolerances as for the forward (2e-3 fp16, 1e-2 bf16 on O, with the half-ulp
 allowance of the edge cases; 1e-3 on LSE).  Unsplit, a sequence's result is
 also bit-for-bit the dense decode kernel's on its gathered keys.
@@ -55,9 +57,9 @@ def _run(name, lens, block_size, Hq=32, Hkv=8, Sq=1, d=128, dt="bf16", causal=Tr
 
 
 @pytest.mark.parametrize("kv_split", [1, 0, 6])
-@pytest.mark.parametrize("block_size", [32, 64, 256])
+@pytest.mark.parametrize("block_size", [16, 32, 48, 64, 256])
 def test_paged_ragged_lengths(block_size, kv_split):
-    lens = [1, 31, 32, 33, 2 * block_size, 3000, 700, 4099]
+    lens = [1, 15, 16, 17, 31, 32, 33, 2 * block_size, 3000, 700, 4099]
     _run(f"paged_ragged_b{block_size}", lens, block_size, kv_split=kv_split, seed=block_size)
 
 
@@ -69,11 +71,12 @@ def test_paged_head_sizes_dtypes_masks(d, dt, causal):
          dt=dt, causal=causal, kv_split=0, seed=d + int(causal))
 
 
+@pytest.mark.parametrize("block_size", [16, 32])
 @pytest.mark.parametrize("Hq,Hkv,Sq", [(32, 8, 4), (8, 1, 4), (4, 4, 8), (1, 1, 32),
                                        (12, 3, 3)])
-def test_paged_group_sizes_and_tokens(Hq, Hkv, Sq):
+def test_paged_group_sizes_and_tokens(Hq, Hkv, Sq, block_size):
     # lengths shorter than Sq: the first rows see no key (O = 0, LSE = -inf)
-    _run(f"paged_g{Hq // Hkv}_sq{Sq}", [2, 1, 999, 32], 32, Hq=Hq, Hkv=Hkv, Sq=Sq,
+    _run(f"paged_g{Hq // Hkv}_sq{Sq}", [2, 1, 999, 32, 18], block_size, Hq=Hq, Hkv=Hkv, Sq=Sq,
          kv_split=3, seed=Hq + Sq)
 
 
@@ -88,10 +91,11 @@ def test_paged_max_seqlen_bounds_lengths():
     _run("paged_clamp", [5000, 300, 2048], 64, kv_split=0, seed=6, max_seqlen=2048)
 
 
-def test_paged_unsplit_equals_dense_decode_bit_for_bit():
+@pytest.mark.parametrize("block_size", [16, 64])
+def test_paged_unsplit_equals_dense_decode_bit_for_bit(block_size):
     from exact_attention_19_amd import attn_fwd_split
-    lens = [777, 64, 2049]
-    q, k, v, o, lse, w = _run("paged_vs_dense", lens, 64, kv_split=1, seed=7)
+    lens = [777, 64, 2049, 17]
+    q, k, v, o, lse, w = _run("paged_vs_dense", lens, block_size, kv_split=1, seed=7)
     for b, L in enumerate(lens):
         od, ld = attn_fwd_split(q[b:b + 1].cuda(), k[b:b + 1, :L].contiguous().cuda(),
                                 v[b:b + 1, :L].contiguous().cuda(), scale=w.scale,
