@@ -164,6 +164,15 @@ def test_bwd_1k_causal_workload():
     _check(w, *_run(w))
 
 
+def test_bwd_gqa_head_layout_at_1536():
+    """The 8K GQA workload's heads (Hq 32, Hkv 8, d 128, bf16, causal) at
+    1536 tokens: 12 key blocks of the dK/dV kernel, 24 query tiles per head,
+    four query heads per kv head; every gradient element."""
+    w = WORKLOADS["gqa4_causal_bf16_b1_hq32_hkv8_s8192_d128"].with_(
+        name="bwd_gqa4_bf16_s1536", Sq=1536, Sk=1536)
+    _check(w, *_run(w))
+
+
 def test_bwd_deterministic():
     from exact_attention_19_amd import attn_bwd, attn_fwd
     w = Workload("bwd_det", 1, 8, 2, 333, 517, 128, "bf16", True, 0.1)
