@@ -425,11 +425,28 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       S[r] = 0.f;
       dP[r] = 0.f;
     }
+    {
+      // fragments of step kk + 1 are read while the MFMAs of step kk run
+      auto rd = [&](int kk, i16x8 (&f)[4]) {
+        const uint32_t ko = row_frag_off(kbase, kg & 1, kk);
+        f[0] = read_row_frag(qtile, rbase, qh, kk);
+        f[1] = *(LDS_PTR(const i16x8))(ktile + ko);
+        f[2] = read_row_frag(otile, rbase, qh, kk);
+        f[3] = *(LDS_PTR(const i16x8))(vtile + ko);
+      };
+      i16x8 fa[4], fb[4];
+      rd(0, fa);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const uint32_t ko = row_frag_off(kbase, kg & 1, kk);
-      S = T::mfma(read_row_frag(qtile, rbase, qh, kk), *(LDS_PTR(const i16x8))(ktile + ko), S);
-      dP = T::mfma(read_row_frag(otile, rbase, qh, kk), *(LDS_PTR(const i16x8))(vtile + ko), dP);
+      for (int kk = 0; kk < KK; kk += 2) {
+        rd(kk + 1, fb);
+        __builtin_amdgcn_sched_barrier(0);
+        S = T::mfma(fa[0], fa[1], S);
+        dP = T::mfma(fa[2], fa[3], dP);
+        if (kk + 2 < KK) rd(kk + 2, fa);
+        __builtin_amdgcn_sched_barrier(0);
+        S = T::mfma(fb[0], fb[1], S);
+        dP = T::mfma(fb[2], fb[3], dP);
+      }
     }
     // register r holds query row 32 qh + key_of_reg(r) + 8 hh of the tile;
     // registers 4g .. 4g+3 are 4 consecutive rows
@@ -469,14 +486,28 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       pf[f] = T::cvt(pe);
       dsf[f] = T::cvt(de);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (two 16-row steps)
+    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (two 16-row steps);
+    // the fragments of the next step are read during the current one
+    {
+      constexpr int NS = 2 * CB;
+      auto rd = [&](int st, i16x8 (&f)[2]) {
+        f[0] = read_tr_frag(otile, tbase, 2 * qh + st / CB, st % CB);
+        f[1] = read_tr_frag(qtile, tbase, 2 * qh + st / CB, st % CB);
+      };
+      i16x8 fa[2], fb[2];
+      rd(0, fa);
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        adv[cb] = T::mfma(read_tr_frag(otile, tbase, 2 * qh + f, cb), pf[f], adv[cb]);
-        adk[cb] = T::mfma(read_tr_frag(qtile, tbase, 2 * qh + f, cb), dsf[f], adk[cb]);
+      for (int st = 0; st < NS; st += 2) {
+        rd(st + 1, fb);
+        __builtin_amdgcn_sched_barrier(0);
+        adv[st % CB] = T::mfma(fa[0], pf[st / CB], adv[st % CB]);
+        adk[st % CB] = T::mfma(fa[1], dsf[st / CB], adk[st % CB]);
+        if (st + 2 < NS) rd(st + 2, fa);
+        __builtin_amdgcn_sched_barrier(0);
+        adv[(st + 1) % CB] = T::mfma(fb[0], pf[(st + 1) / CB], adv[(st + 1) % CB]);
+        adk[(st + 1) % CB] = T::mfma(fb[1], dsf[(st + 1) / CB], adk[(st + 1) % CB]);
       }
+    }
   }
 
   // add the row halves: waves 4-7 hand their sums to waves 0-3 through LDS
