@@ -207,18 +207,33 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
       LDS_PTR(char) const kt = kbuf(j);
       LDS_PTR(char) const vt = vbuf(j);
       // S^T = K Q^T and dP^T = V dO^T for the 64 keys of the tile
+      // (the fragments of the next step are read during the current one)
       f32x16 S[2], dP[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           S[kb][r] = 0.f;
           dP[kb][r] = 0.f;
         }
+      {
+        constexpr int NS = 2 * KK;  // steps (kb, kk)
+        auto rd = [&](int st, i16x8 (&f)[2]) {
+          f[0] = read_row_frag(kt, rbase, st / KK, st % KK);
+          f[1] = read_row_frag(vt, rbase, st / KK, st % KK);
+        };
+        i16x8 fa[2], fb[2];
+        rd(0, fa);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          S[kb] = T::mfma(read_row_frag(kt, rbase, kb, kk), qf[kk], S[kb]);
-          dP[kb] = T::mfma(read_row_frag(vt, rbase, kb, kk), dof[kk], dP[kb]);
+        for (int st = 0; st < NS; st += 2) {
+          rd(st + 1, fb);
+          __builtin_amdgcn_sched_barrier(0);
+          S[st / KK] = T::mfma(fa[0], qf[st % KK], S[st / KK]);
+          dP[st / KK] = T::mfma(fa[1], dof[st % KK], dP[st / KK]);
+          if (st + 2 < NS) rd(st + 2, fa);
+          __builtin_amdgcn_sched_barrier(0);
+          S[(st + 1) / KK] = T::mfma(fb[0], qf[(st + 1) % KK], S[(st + 1) / KK]);
+          dP[(st + 1) / KK] = T::mfma(fb[1], dof[(st + 1) % KK], dP[(st + 1) / KK]);
         }
       }
       if (j >= n_full) {
@@ -244,12 +259,20 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
         }
         dsf[f] = T::cvt(e);
       }
-      // dQ^T += K^T dS^T
+      // dQ^T += K^T dS^T (fragments one step ahead)
+      {
+        constexpr int NS = 4 * CB;  // steps (f, cb)
+        i16x8 fa = read_tr_frag(kt, tbase, 0, 0), fb;
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[cb] = T::mfma(read_tr_frag(kt, tbase, f, cb), dsf[f], acc[cb]);
+        for (int st = 0; st < NS; st += 2) {
+          fb = read_tr_frag(kt, tbase, (st + 1) / CB, (st + 1) % CB);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[st % CB] = T::mfma(fa, dsf[st / CB], acc[st % CB]);
+          if (st + 2 < NS) fa = read_tr_frag(kt, tbase, (st + 2) / CB, (st + 2) % CB);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[(st + 1) % CB] = T::mfma(fb, dsf[(st + 1) / CB], acc[(st + 1) % CB]);
+        }
+      }
     }
   }
 
