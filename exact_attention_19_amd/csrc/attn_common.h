@@ -30,7 +30,10 @@ struct DecodeArgs {
   int64_t o_sb, o_ss, o_sh;
   int B, Sq, Sk, Hq, Hkv;
   int piece_tiles;   // 32-key tiles per piece
-  long long grid;    // B * Hkv * pieces
+  int rgroups;       // 32-row groups per kv head: ceil(g * Sq / 32)
+  int ucols;         // workgroups per piece: B * Hkv, or with several row
+                     // groups B * Hkv rounded up to 8, times rgroups
+  long long grid;    // ucols * pieces
   float scale_log2;
   float* part_o;     // pieces > 1: [piece][b][i][h][d] fp32, else null
   float* part_lse;   // pieces > 1: [piece][b][h][i]
@@ -292,13 +295,26 @@ using attn_detail::launch_decode;
 // workgroup of two waves per SIMD) were 1-5 % slower.
 constexpr int DEC_WAVES = 4;
 
+// Shapes the decode kernel takes: the query rows of a kv head (g * Sq) fit
+// one 32-row wave, or, up to four 32-row groups (each its own workgroup over
+// the same keys), when Sq <= 8.  Measured on MI355X (32 sequences x 8192
+// keys): with few tokens per head the prefill kernel, whose waves hold 32
+// rows of one head, leaves most rows empty (g 16, Sq 4: 302 us against 146
+// us); from about 9 tokens on it is the faster one (g 4, Sq 16: 245 us
+// against 288 us).
+constexpr int DEC_MAX_ROWS = 128;
+constexpr int DEC_MAX_SQ_GROUPED = 8;
+
 inline bool decode_eligible(int Sq, int Hq, int Hkv, int d) {
-  return (long long)(Hq / Hkv) * Sq <= 32 && (d == 64 || d == 128);
+  const long long rows = (long long)(Hq / Hkv) * Sq;
+  if (d != 64 && d != 128) return false;
+  return rows <= 32 || (rows <= DEC_MAX_ROWS && Sq <= DEC_MAX_SQ_GROUPED);
 }
 
 struct DecodePlan {
   int pieces;
   int piece_tiles;
+  int rgroups, ucols;
   long long grid;
   size_t lse_offset;  // workspace: part_o then part_lse (256-byte aligned)
   size_t ws_bytes;
@@ -309,12 +325,25 @@ struct DecodePlan {
 // streams K and V at the chip's practical rate (5.5 TB/s with 256 of them; a
 // second workgroup per CU, or cutting into more pieces, was slower), and a
 // piece pays a fixed start-up and merge cost, so the choice splits only when
-// there are fewer than 128 (batch, kv head) pairs, into about 128 workgroups
+// there are fewer than 128 workgroups per piece, into about 128 workgroups
 // with at least 32 tiles (8 per wave) each.
+//
+// With more than 32 query rows per kv head, each 32-row group is its own
+// workgroup; the groups of one (batch, kv head) are placed 8 workgroup ids
+// apart, which puts them on one XCD (ids are dealt to the 8 XCDs in turn), so
+// the second read of the same K and V tiles finds them in that XCD's L2.
 inline DecodePlan make_decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int kv_split) {
   DecodePlan dp{};
   const int ntiles = (Sk + 31) / 32;
-  const long long cols = (long long)B * Hkv;
+  dp.rgroups = (int)(((long long)(Hq / Hkv) * Sq + 31) / 32);
+  const long long bh = (long long)B * Hkv;
+  const long long ucols = dp.rgroups > 1 ? ((bh + 7) / 8) * 8 * dp.rgroups : bh;
+  if (ucols > 0x7fffffffll) {
+    dp.grid = -1;
+    return dp;
+  }
+  dp.ucols = (int)ucols;
+  const long long cols = bh * dp.rgroups;
   long long pieces = 1;
   if (kv_split == 0) {
     if (cols < 128) pieces = (128 + cols - 1) / cols;
@@ -326,7 +355,7 @@ inline DecodePlan make_decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d
   if (pieces > ntiles) pieces = ntiles;
   dp.piece_tiles = (int)((ntiles + pieces - 1) / pieces);
   dp.pieces = (ntiles + dp.piece_tiles - 1) / dp.piece_tiles;
-  dp.grid = cols * dp.pieces;
+  dp.grid = ucols * dp.pieces;
   if (dp.pieces > 1) {
     const size_t rows = (size_t)B * Sq * Hq;
     dp.lse_offset = ((size_t)dp.pieces * rows * d * 4 + 255) & ~(size_t)255;

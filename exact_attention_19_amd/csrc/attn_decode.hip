@@ -1,6 +1,6 @@
 // Decode-shaped attention forward for AMD Instinct MI355X (gfx950): a few new
-// query rows per sequence (g * Sq <= 32 rows per kv head, g = Hq / Hkv) over
-// a long K/V cache.
+// query rows per sequence (g * Sq <= 128 rows per kv head, g = Hq / Hkv)
+// over a long K/V cache.
 //
 // The MiniPaged-Qwen page (section 19) sets decode apart from prefill: the
 // query side has almost no parallelism and the work becomes reading the K/V
@@ -10,12 +10,14 @@
 // * All g * Sq query rows of one (batch, kv head) -- every query head of the
 //   GQA group and every new token -- are the 32 rows of ONE wave: row r is
 //   query head h0 + r / Sq, token r % Sq.  The prefill kernel would give each
-//   query head its own 32-row wave, mostly empty.
+//   query head its own 32-row wave, mostly empty.  More than 32 such rows
+//   are cut into 32-row groups, each a workgroup of its own over the same
+//   keys (placed on one XCD, so that the K/V tiles are read from HBM once).
 // * The DEC_WAVES (4) waves of a workgroup walk different 32-key tiles of the
 //   key range (tile w, w + 4, ...), each with its own softmax state, and the
-//   states are merged through LDS at the end (the online-softmax rescale).  A key range
-//   can further be cut into pieces over workgroups, merged by the merge
-//   kernel, when (batch, kv head) pairs are too few to fill the GPU.
+//   states are merged through LDS at the end (the online-softmax rescale).
+//   A key range can further be cut into pieces over workgroups, merged by
+//   the merge kernel, when (batch, kv head) pairs are too few to fill the GPU.
 // * The work is bound by reading K and V: K rows go straight from global
 //   memory into registers as the A operand of S^T = K Q^T (lane l loads key
 //   row sigma(l & 31)); V tiles go to LDS by buffer DMA for the transposed
@@ -53,13 +55,24 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const int ncol = p.B * p.Hkv;
-  const int col = blockIdx.x % ncol;
-  const int piece = blockIdx.x / ncol;
+  // workgroup -> (piece, batch, kv head, row group); with several row
+  // groups, those of one (batch, kv head) sit 8 ids apart (one XCD)
+  const int piece = blockIdx.x / p.ucols;
+  const int u = blockIdx.x % p.ucols;
+  int col = u, rg = 0;
+  if (p.rgroups > 1) {
+    const int chunk = 8 * p.rgroups;
+    col = (u / chunk) * 8 + u % 8;
+    rg = (u % chunk) / 8;
+    if (col >= p.B * p.Hkv) return;  // padding of the last chunk
+  }
   const int b = col / p.Hkv;
   const int kvh = col % p.Hkv;
   const int g = p.Hq / p.Hkv;
-  const int M = g * p.Sq;
+  // this workgroup's query rows: rows 32 rg .. 32 rg + M - 1 of the
+  // g * Sq rows of the kv head (row R is head kvh * g + R / Sq, token R % Sq)
+  const int r0g = 32 * rg;
+  const int M = min(32, g * p.Sq - r0g);
   // keys of this sequence (paged cache: its own length, at most Sk, which
   // the host keeps within the block table)
   int Sk = p.Sk;
@@ -68,8 +81,8 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
   // this lane's query row
   const int r = l32;
   const bool rok = r < M;
-  const int hq = kvh * g + (rok ? r / p.Sq : 0);
-  const int qi = rok ? r % p.Sq : 0;
+  const int hq = kvh * g + (rok ? (r0g + r) / p.Sq : 0);
+  const int qi = rok ? (r0g + r) % p.Sq : 0;
   i16x8 qf[KK];
   {
     const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)qi * p.q_ss + (int64_t)hq * p.q_sh;
@@ -342,8 +355,8 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
       const bool has = lr_s > 0.f;
       const float inv = has ? 1.f / lr_s : 0.f;
       const float lse = has ? (mmax + __builtin_amdgcn_logf(lf_s)) * LN2 : -INFINITY;
-      const int h = kvh * g + rr / p.Sq;
-      const int i = rr % p.Sq;
+      const int h = kvh * g + (r0g + rr) / p.Sq;
+      const int i = (r0g + rr) % p.Sq;
       uint16_t* orow = p.o + (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh;
       // a piece of a split key range writes its fp32 state normalised over
       // its keys instead

@@ -941,6 +941,8 @@ attn_status run_decode(const void* q, const void* k, const void* v, void* o, flo
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.piece_tiles = dp.piece_tiles;
+  a.rgroups = dp.rgroups;
+  a.ucols = dp.ucols;
   a.grid = dp.grid;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   if (pg != nullptr) {
@@ -1050,7 +1052,9 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
     // the decode kernel, unsplit: a workgroup per (batch, kv head) with all
     // g * Sq rows in one wave, DEC_WAVES waves over the keys
     const int g = Hq / Hkv;
-    const int vals_dec[10] = {B * Hkv, DEC_WAVES * 64, Sq, 32, g, 32,
+    const DecodePlan dp = make_decode_plan(B, Sq, Sk, Hq, Hkv, d, 1);
+    if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
+    const int vals_dec[10] = {(int)dp.grid, DEC_WAVES * 64, Sq, 32, g, 32,
                               DEC_WAVES * 2 * 32 * d * 2, 0, 0, 1};
     for (int i = 0; i < 10; ++i) vals[i] = vals_dec[i];
   }

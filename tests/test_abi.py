@@ -398,10 +398,44 @@ def test_decode_plan(cfg, kv_split):
         assert sp["keys_per_piece"] == 0 and ws == 0 and sp["merge_grid"] == 0
 
 
+@pytest.mark.parametrize("cfg", [
+    (32, 4, 8192, 64, 4, 128, 1, ATTN_DTYPE_BF16),   # 16 x 4 = 64 rows: 2 groups
+    (32, 8, 8192, 64, 4, 128, 1, ATTN_DTYPE_BF16),   # 128 rows: 4 groups
+    (3, 3, 5000, 32, 1, 64, 0, ATTN_DTYPE_F16),      # 96 rows: 3 groups
+    (1, 2, 32768, 64, 2, 128, 1, ATTN_DTYPE_BF16),   # 64 rows, one sequence
+])
+@pytest.mark.parametrize("kv_split", [0, 1, 5])
+def test_decode_plan_row_groups(cfg, kv_split):
+    """Up to 128 query rows per kv head with at most 8 tokens take the
+    decode kernel as 32-row groups, one workgroup each; the groups of one
+    (batch, kv head) sit 8 workgroup ids apart, so a piece spans
+    ceil(B Hkv / 8) * 8 * groups ids."""
+    _lib()
+    B, Sq, Sk, Hq, Hkv, d, causal, dt = cfg
+    rg = -(-(Hq // Hkv) * Sq // 32)
+    ucols = -(-B * Hkv // 8) * 8 * rg
+    plan = binding.attn_fwd_plan(*cfg)
+    assert plan["decode"] == 1 and plan["grid"] == ucols
+    sp = binding.attn_fwd_split_plan(*cfg, kv_split)
+    ntiles = -(-Sk // 32)
+    cols = B * Hkv * rg
+    if kv_split == 0:
+        pieces = -(-128 // cols) if cols < 128 else 1
+        pieces = min(pieces, max(ntiles // 32, 1))
+    else:
+        pieces = kv_split if kv_split > 1 else 1
+    pieces = min(pieces, ntiles)
+    per = -(-ntiles // pieces)
+    pieces = -(-ntiles // per)
+    assert sp["pieces"] == pieces and sp["grid"] == ucols * pieces
+
+
 def test_prefill_shapes_do_not_take_the_decode_kernel():
     _lib()
     for cfg in ((1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16),
-                (1, 9, 100, 32, 8, 128, 1, ATTN_DTYPE_BF16),     # 4 x 9 = 36 rows
+                (1, 9, 100, 32, 8, 128, 1, ATTN_DTYPE_BF16),     # 4 x 9 = 36 rows, Sq > 8
+                (1, 8, 100, 256, 8, 128, 1, ATTN_DTYPE_BF16),    # 32 x 8 = 256 rows
+                (1, 64, 4096, 1, 1, 128, 0, ATTN_DTYPE_F16),     # 64 rows but Sq 64
                 (1, 1, 1000, 8, 8, 96, 0, ATTN_DTYPE_BF16)):     # d = 96
         assert binding.attn_fwd_plan(*cfg)["decode"] == 0
 

@@ -1,5 +1,6 @@
 """GPU parity of the decode kernel (shapes whose query rows per kv head,
-Hq / Hkv * Sq, number at most 32, at d = 64 or 128), through the C ABI,
+Hq / Hkv * Sq, number at most 32, or at most 128 in 32-row groups when
+Sq <= 8, at d = 64 or 128), through the C ABI,
 against the fp64 oracle: every output element, whole and with the key range
 cut into pieces over workgroups, across GQA group sizes, token counts, causal
 offsets, ragged key lengths and strided inputs.  Tolerances as for the
@@ -36,6 +37,13 @@ def _cases():
         for dt in ("f16", "bf16"):
             for causal in (False, True):
                 out.append((16, 4, 5, 2000, d, dt, causal))
+    # more than 32 rows per kv head (Sq <= 8): 32-row groups, one workgroup
+    # each; the last group partly filled (96 = 3 x 32 + 0, 40 = 32 + 8, ...)
+    for (Hq, Hkv, Sq) in ((64, 4, 4), (32, 4, 8), (64, 2, 3), (40, 4, 4), (128, 8, 8)):
+        for Sk in (1, 33, 4099):
+            out.append((Hq, Hkv, Sq, Sk, 128, "bf16", True))
+    for d in (64, 128):
+        out.append((48, 2, 2, 1500, d, "f16", False))
     return out
 
 

@@ -73,7 +73,7 @@ def test_paged_head_sizes_dtypes_masks(d, dt, causal):
 
 @pytest.mark.parametrize("block_size", [16, 32])
 @pytest.mark.parametrize("Hq,Hkv,Sq", [(32, 8, 4), (8, 1, 4), (4, 4, 8), (1, 1, 32),
-                                       (12, 3, 3)])
+                                       (12, 3, 3), (64, 4, 4), (32, 2, 6)])
 def test_paged_group_sizes_and_tokens(Hq, Hkv, Sq, block_size):
     # lengths shorter than Sq: the first rows see no key (O = 0, LSE = -inf)
     _run(f"paged_g{Hq // Hkv}_sq{Sq}", [2, 1, 999, 32, 18], block_size, Hq=Hq, Hkv=Hkv, Sq=Sq,
