@@ -602,7 +602,8 @@ attn_status validate_bwd(const void* q, const void* k, const void* v, const void
     return ATTN_ERR_INVALID_ARG;
   if (((uintptr_t)lse) & 3u) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // (d = 256 would need 256 registers of dK/dV sums per wave alone)
+  if (d != 32 && d != 64 && d != 96 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)Sq + Sk >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)Hq * d * 2 * 64 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31))
@@ -630,11 +631,19 @@ hipError_t launch_bwd_t(const Plan& pl, const BwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int DT, int D>
+hipError_t launch_bwd_c(bool causal, const Plan& pl, const BwdParams& p, hipStream_t st) {
+  return causal ? launch_bwd_t<DT, D, true>(pl, p, st) : launch_bwd_t<DT, D, false>(pl, p, st);
+}
+
 template <int DT>
 hipError_t launch_bwd_d(int d, bool causal, const Plan& pl, const BwdParams& p, hipStream_t st) {
-  if (d == 128)
-    return causal ? launch_bwd_t<DT, 128, true>(pl, p, st) : launch_bwd_t<DT, 128, false>(pl, p, st);
-  return causal ? launch_bwd_t<DT, 64, true>(pl, p, st) : launch_bwd_t<DT, 64, false>(pl, p, st);
+  switch (d) {
+    case 32: return launch_bwd_c<DT, 32>(causal, pl, p, st);
+    case 64: return launch_bwd_c<DT, 64>(causal, pl, p, st);
+    case 96: return launch_bwd_c<DT, 96>(causal, pl, p, st);
+    default: return launch_bwd_c<DT, 128>(causal, pl, p, st);
+  }
 }
 
 }  // namespace

@@ -147,6 +147,13 @@ def _cases():
             Workload(f"bwd_causal_empty_rows_{dt}", 1, 4, 1, 333, 200, 64, dt, True, 0.2),
             Workload(f"bwd_gqa_nc_{dt}", 2, 8, 2, 190, 450, 128, dt, False, 1 / math.sqrt(128)),
         ]
+    # head sizes 32 and 96 (one and three 32-column blocks)
+    for d in (32, 96):
+        cases += [
+            Workload(f"bwd_d{d}_causal_off_bf16", 1, 8, 2, 200, 333, d, "bf16", True,
+                     1 / math.sqrt(d)),
+            Workload(f"bwd_d{d}_gqa_nc_f16", 2, 4, 1, 150, 270, d, "f16", False, 1 / math.sqrt(d)),
+        ]
     cases += [Workload("bwd_scale1_f16", 1, 4, 4, 300, 300, 128, "f16", True, 1.0),
               Workload("bwd_one_row_bf16", 2, 8, 4, 1, 700, 128, "bf16", True, 1 / math.sqrt(128)),
               Workload("bwd_one_key_bf16", 1, 4, 2, 100, 1, 64, "bf16", False, 0.3)]
