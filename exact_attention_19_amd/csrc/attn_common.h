@@ -288,8 +288,6 @@ Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
 using attn_detail::DecodeArgs;
 using attn_detail::launch_decode;
 
-// The decode kernel takes shapes whose query rows per kv head fit one wave
-// (g * Sq <= 32) at d = 64 or 128.
 // Waves per decode workgroup, each walking its own key tiles.  Measured on
 // MI355X: 4 (two workgroups per CU) stream K and V at 5.5 TB/s; 8 (one
 // workgroup of two waves per SIMD) were 1-5 % slower.
@@ -307,7 +305,7 @@ constexpr int DEC_MAX_SQ_GROUPED = 8;
 
 inline bool decode_eligible(int Sq, int Hq, int Hkv, int d) {
   const long long rows = (long long)(Hq / Hkv) * Sq;
-  if (d != 64 && d != 128) return false;
+  if (d != 32 && d != 64 && d != 96 && d != 128) return false;
   return rows <= 32 || (rows <= DEC_MAX_ROWS && Sq <= DEC_MAX_SQ_GROUPED);
 }
 

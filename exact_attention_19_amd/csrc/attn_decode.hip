@@ -315,10 +315,12 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
   const float lf_tot = T::LSE_FROM_FP32_SUM ? pair_sum(l_fp32) : lr_tot;
   __syncthreads();  // every wave is done with its V stages: reuse them
   // [wave][row][D] floats; the float4 at column c of row r sits at column
-  // c ^ 4 (r % 16), so that 16 rows written at one column, and one row read
-  // by 16 lanes, each fill all 64 banks once
+  // c ^ 4 (r % 16) (c ^ 4 (r % 8) when D is not a multiple of 64, so that
+  // the column stays inside the row), so that 16 rows written at one
+  // column, and one row read by 16 lanes, fill the 64 banks evenly
   float* mo = (float*)&lds_v[0][0][0];
-  auto mo_at = [&](int row, int c) { return mo + row * D + (c ^ ((row & 15) << 2)); };
+  constexpr int SWZ = D % 64 == 0 ? 15 : 7;
+  auto mo_at = [&](int row, int c) { return mo + row * D + (c ^ ((row & SWZ) << 2)); };
   if (hh == 0) {
     lds_m[wave][l32] = m_run;
     lds_lr[wave][l32] = lr_tot;
@@ -364,8 +366,9 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
                         ? nullptr
                         : p.part_o + ((((int64_t)piece * p.B + b) * p.Sq + i) * p.Hq + h) * D;
 #pragma unroll
-      for (int j = 0; j < D / 64; ++j) {
+      for (int j = 0; j < (D + 63) / 64; ++j) {
         const int c = 4 * l16 + 64 * j;
+        if (D % 64 != 0 && c >= D) continue;
         f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -413,9 +416,19 @@ hipError_t launch_decode_d(bool causal, const DecodeArgs& a, hipStream_t st) {
 
 __attribute__((visibility("hidden"))) hipError_t attn_detail::launch_decode(
     int dtype, int d, int causal, const DecodeArgs& a, hipStream_t st) {
-  if (dtype == ATTN_DTYPE_BF16)
-    return d == 128 ? launch_decode_d<ATTN_DTYPE_BF16, 128>(causal != 0, a, st)
-                    : launch_decode_d<ATTN_DTYPE_BF16, 64>(causal != 0, a, st);
-  return d == 128 ? launch_decode_d<ATTN_DTYPE_F16, 128>(causal != 0, a, st)
-                  : launch_decode_d<ATTN_DTYPE_F16, 64>(causal != 0, a, st);
+  const bool c = causal != 0;
+  if (dtype == ATTN_DTYPE_BF16) {
+    switch (d) {
+      case 32: return launch_decode_d<ATTN_DTYPE_BF16, 32>(c, a, st);
+      case 64: return launch_decode_d<ATTN_DTYPE_BF16, 64>(c, a, st);
+      case 96: return launch_decode_d<ATTN_DTYPE_BF16, 96>(c, a, st);
+      default: return launch_decode_d<ATTN_DTYPE_BF16, 128>(c, a, st);
+    }
+  }
+  switch (d) {
+    case 32: return launch_decode_d<ATTN_DTYPE_F16, 32>(c, a, st);
+    case 64: return launch_decode_d<ATTN_DTYPE_F16, 64>(c, a, st);
+    case 96: return launch_decode_d<ATTN_DTYPE_F16, 96>(c, a, st);
+    default: return launch_decode_d<ATTN_DTYPE_F16, 128>(c, a, st);
+  }
 }

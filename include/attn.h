@@ -108,7 +108,8 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
  *       overlapping the matrix products of the previous and next tiles) is
  *       used
  *   [9] 1 if the decode kernel is used: when the query rows of a kv head
- *       (Hq / Hkv * Sq) number at most 128 and d is 64 or 128, each group
+ *       (Hq / Hkv * Sq) number at most 32 (or 128 with Sq <= 8) and d is
+ *       32, 64, 96 or 128, each group
  *       of up to 32 of them shares one wave and the 4 waves of a workgroup
  *       split the keys (then [0] counts a workgroup per (batch, kv head,
  *       32-row group), [2] is Sq and [4] the GQA group size)
@@ -325,7 +326,8 @@ attn_status attn_bwd_workspace(int B, int Sq, int Hq, size_t* bytes);
  *   max_seqlen   the longest length to cover, 1 .. max_blocks * block_size;
  *                it sizes the key split (no device read of seqlens is made)
  *   B ... dtype  as for attn_fwd, restricted to the decode kernel's shapes:
- *                d = 64 or 128 and (Hq / Hkv) * Sq <= 128, else
+ *                d = 32, 64, 96 or 128 and (Hq / Hkv) * Sq <= 32 (or
+ *                <= 128 with Sq <= 8), else
  *                ATTN_ERR_UNSUPPORTED
  *   kv_split, workspace, workspace_bytes  as for attn_fwd_split, with the
  *                decode rule for kv_split = 0; the workspace size is

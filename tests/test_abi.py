@@ -371,7 +371,7 @@ def test_bwd_workspace_and_early_rejection():
 ])
 @pytest.mark.parametrize("kv_split", [0, 1, 3])
 def test_decode_plan(cfg, kv_split):
-    """Decode shapes (g * Sq <= 32, d 64 or 128) take the decode kernel: one
+    """Decode shapes (g * Sq <= 32, d 32 to 128) take the decode kernel: one
     workgroup per (batch, kv head) and key piece; automatic pieces only below
     128 (batch, kv head) pairs, about 128 workgroups of at least 32 tiles;
     the workspace holds one fp32 row state per piece and query row."""
@@ -438,7 +438,7 @@ def test_prefill_shapes_do_not_take_the_decode_kernel():
                 (1, 9, 100, 32, 8, 128, 1, ATTN_DTYPE_BF16),     # 4 x 9 = 36 rows, Sq > 8
                 (1, 8, 100, 256, 8, 128, 1, ATTN_DTYPE_BF16),    # 32 x 8 = 256 rows
                 (1, 64, 4096, 1, 1, 128, 0, ATTN_DTYPE_F16),     # 64 rows but Sq 64
-                (1, 1, 1000, 8, 8, 96, 0, ATTN_DTYPE_BF16)):     # d = 96
+                (1, 1, 1000, 8, 8, 256, 0, ATTN_DTYPE_BF16)):    # d = 256
         assert binding.attn_fwd_plan(*cfg)["decode"] == 0
 
 
@@ -476,9 +476,12 @@ def test_paged_decode_validation():
                  dict(block_size=8), dict(block_size=24), dict(block_size=0), dict(max_seqlen=0),
                  dict(max_seqlen=20 * 64 + 1), dict(scale=0.0), dict(causal=2)):
         assert _pcheck(**over) == ATTN_ERR_INVALID_ARG, over
-    # outside the decode kernel's shapes: (Hq / Hkv) * Sq > 32, d not 64/128
-    for over in (dict(Sq=9), dict(d=96), dict(d=256), dict(dtype=2)):
+    # outside the decode kernel's shapes: (Hq / Hkv) * Sq > 32 with Sq > 8,
+    # d not 32, 64, 96 or 128
+    for over in (dict(Sq=9), dict(d=80), dict(d=256), dict(dtype=2)):
         assert _pcheck(**over) == ATTN_ERR_UNSUPPORTED, over
+    for over in (dict(d=32), dict(d=96), dict(Sq=8)):
+        assert _pcheck(**over) == ATTN_OK, over
 
 
 @pytest.mark.parametrize("B,max_seqlen,kv_split", [(4, 1200, 0), (32, 8192, 0), (1, 32768, 0),

@@ -1,6 +1,6 @@
 """GPU parity of the decode kernel (shapes whose query rows per kv head,
 Hq / Hkv * Sq, number at most 32, or at most 128 in 32-row groups when
-Sq <= 8, at d = 64 or 128), through the C ABI,
+Sq <= 8, at d = 32, 64, 96 or 128), through the C ABI,
 against the fp64 oracle: every output element, whole and with the key range
 cut into pieces over workgroups, across GQA group sizes, token counts, causal
 offsets, ragged key lengths and strided inputs.  Tolerances as for the
@@ -44,6 +44,12 @@ def _cases():
             out.append((Hq, Hkv, Sq, Sk, 128, "bf16", True))
     for d in (64, 128):
         out.append((48, 2, 2, 1500, d, "f16", False))
+    # head sizes 32 and 96 (one and three 32-column blocks; the merge area's
+    # swizzle stays inside rows that are not a multiple of 64 columns)
+    for d in (32, 96):
+        for dt in ("f16", "bf16"):
+            out.append((32, 8, 2, 2049, d, dt, True))
+            out.append((64, 4, 4, 700, d, dt, False))
     return out
 
 
