@@ -19,7 +19,8 @@ ATTN_DTYPE_F16, ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1, 2
 EXPORTED = ("attn_fwd", "attn_fwd_check", "attn_fwd_plan", "attn_fwd_split",
             "attn_fwd_split_workspace", "attn_fwd_split_plan", "attn_fwd_strided",
             "attn_fwd_strided_check", "attn_merge", "attn_merge_check", "attn_bwd",
-            "attn_bwd_check", "attn_bwd_workspace", "attn_decode_paged",
+            "attn_bwd_check", "attn_bwd_workspace", "attn_fwd_causal_offset",
+            "attn_fwd_causal_offset_check", "attn_fwd_causal_offset_workspace", "attn_decode_paged",
             "attn_decode_paged_check", "attn_decode_paged_workspace", "attn_status_str",
             "attn_abi_version")
 
@@ -72,6 +73,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_merge.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i, vp]
     lib.attn_merge_check.restype = i
     lib.attn_merge_check.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i]
+    lo = ctypes.c_longlong
+    lib.attn_fwd_causal_offset.restype = i
+    lib.attn_fwd_causal_offset.argtypes = [vp] * 5 + [i] * 6 + [f, lo, i, vp, i, vp, sz, vp]
+    lib.attn_fwd_causal_offset_check.restype = i
+    lib.attn_fwd_causal_offset_check.argtypes = [vp] * 5 + [i] * 6 + [f, lo, i, vp]
+    lib.attn_fwd_causal_offset_workspace.restype = i
+    lib.attn_fwd_causal_offset_workspace.argtypes = [i] * 6 + [lo, i, i, ctypes.POINTER(sz)]
     lib.attn_decode_paged.restype = i
     lib.attn_decode_paged.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, i, vp, sz, vp]
     lib.attn_decode_paged_check.restype = i
@@ -313,6 +321,77 @@ def attn_fwd_strided(q, k, v, scale: float | None = None, causal: bool = False,
         int(kv_split), ws_ptr, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_strided")
+    return out, lse
+
+
+def attn_fwd_causal_offset_workspace(B, Sq, Sk, Hq, Hkv, d, causal_offset, dtype_code,
+                                     kv_split=0) -> int:
+    """Workspace bytes attn_fwd_causal_offset needs (0 when it does not split)."""
+    n = ctypes.c_size_t(0)
+    st = load_library().attn_fwd_causal_offset_workspace(B, Sq, Sk, Hq, Hkv, d, int(causal_offset),
+                                                         dtype_code, int(kv_split),
+                                                         ctypes.byref(n))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_causal_offset_workspace")
+    return int(n.value)
+
+
+def attn_fwd_causal_offset(q, k, v, causal_offset: int, scale: float | None = None,
+                           kv_split: int = 0, out=None, lse=None, return_lse: bool = True,
+                           workspace=None, stream=None):
+    """Causal attention with an explicit mask offset: query i sees key j iff
+    j <= i + causal_offset.  For keys [k0, k1) of a causal problem with Sk
+    keys in all, causal_offset = Sk - Sq - k0 (k, v may then be the slices
+    k[:, k0:k1], v[:, k0:k1] of the full tensors: any (b, s, h) strides with
+    a contiguous last dimension).  q, k, v in the (B, S, H, d) layout; out
+    dense unless given.  Returns (o, lse); rows that see no key get o = 0,
+    lse = -inf.  The shards' (o, lse) merge with attn_merge."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (batch, seq, heads, d_head)")
+    B, Sq, Hq, d = q.shape
+    Bk, Sk, Hkv, dk = k.shape
+    if tuple(v.shape) != (Bk, Sk, Hkv, dk) or Bk != B or dk != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}")
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v and out must share one dtype")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous")
+    if tuple(out.shape) != (B, Sq, Hq, d):
+        raise ValueError("out must have the shape of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq, Sq)):
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+    strides = []
+    for t in (q, k, v, out):
+        strides += [t.stride(0), t.stride(1), t.stride(2)]
+    if workspace is None:
+        need = attn_fwd_causal_offset_workspace(B, Sq, Sk, Hq, Hkv, d, causal_offset, code,
+                                                kv_split)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().attn_fwd_causal_offset(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, B, Sq, Sk, Hq, Hkv, d, float(scale),
+        int(causal_offset), code, _strides_arg(strides), int(kv_split), ws_ptr, ws_bytes,
+        ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_causal_offset")
     return out, lse
 
 

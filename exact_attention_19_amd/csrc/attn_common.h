@@ -29,6 +29,8 @@ struct DecodeArgs {
   int64_t v_sb, v_ss, v_sh;
   int64_t o_sb, o_ss, o_sh;
   int B, Sq, Sk, Hq, Hkv;
+  int off;           // causal: query i sees key j <= i + off (dense keys;
+                     // a paged sequence of length L uses L - Sq)
   int piece_tiles;   // 32-key tiles per piece
   int rgroups;       // 32-row groups per kv head: ceil(g * Sq / 32)
   int ucols;         // workgroups per piece: B * Hkv, or with several row

@@ -93,18 +93,22 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
       qf[kk] = __builtin_bit_cast(i16x8, x);
     }
   }
-  // keys this row sees: j < Sk, and j <= qi + Sk - Sq when causal
+  // keys this row sees: j < Sk, and j <= qi + off when causal (off = Sk - Sq
+  // for the last Sq positions of a sequence, or the caller's offset)
+  const int off = p.seqlens != nullptr ? Sk - p.Sq : p.off;
   int lim = Sk - 1;
-  if (CAUSAL) lim = min(lim, qi + Sk - p.Sq);
+  if (CAUSAL) lim = min(lim, qi + off);
   if (!rok) lim = -1;
 
   // the piece's tiles [t_lo, t_hi); this wave takes t_lo + wave, + NW, ...
   const int ntiles = (Sk + DBC - 1) / DBC;
   const int t_lo = piece * p.piece_tiles;
   const int t_hi = min(ntiles, t_lo + p.piece_tiles);
-  // last key seen by any row of the group (tiles past it are skipped)
-  // (bottom-right alignment: the last query row sees every key)
-  const int t_end = Sk > 0 ? min(t_hi, (Sk - 1) / DBC + 1) : 0;
+  // last key seen by any row (tiles past it are skipped): the last query
+  // row's limit when causal
+  int last_key = Sk - 1;
+  if (CAUSAL) last_key = min(last_key, p.Sq - 1 + off);
+  const int t_end = last_key >= 0 ? min(t_hi, last_key / DBC + 1) : 0;
 
   const bool paged = p.block_table != nullptr;
   const char* kbase =

@@ -755,8 +755,10 @@ struct SplitPlan {
   size_t ws_bytes;     // workspace bytes (0 = none)
 };
 
+// off: the causal offset (query i sees key j <= i + off), Sk - Sq unless
+// the caller gives another (a key shard of a longer sequence)
 SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
-                          int kv_split) {
+                          int kv_split, int off) {
   SplitPlan sp{};
   sp.base = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
   const Plan& pl = sp.base;
@@ -765,7 +767,6 @@ SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int cau
   sp.q_first = Sq;
   sp.grid = pl.grid;
   if (pl.grid <= 0 || kv_split == 1) return sp;
-  const int off = Sk - Sq;
   const int nmax = block_tiles((pl.qtiles - 1) * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0);
   int chunk;
   if (kv_split == 0) {
@@ -862,7 +863,7 @@ hipError_t launch_d(int d, bool causal, const Plan& pl, long long nwg, const Par
 
 Params fill_params(const Plan& pl, const void* q, const void* k, const void* v, void* o,
                    float* lse, int B, int Sq, int Sk, int Hq, int Hkv, float scale,
-                   const Strides& st) {
+                   const Strides& st, int off) {
   Params p{};
   p.q_sb = st.s[0], p.q_ss = st.s[1], p.q_sh = st.s[2];
   p.k_sb = st.s[3], p.k_ss = st.s[4], p.k_sh = st.s[5];
@@ -885,7 +886,7 @@ Params fill_params(const Plan& pl, const void* q, const void* k, const void* v, 
   p.qtiles = pl.qtiles;
   p.ncols = pl.ncols;
   p.xcd_cols = pl.xcd_cols;
-  p.off = Sk - Sq;
+  p.off = off;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.chunk = 0;
   p.q_split = Sq;
@@ -919,7 +920,7 @@ struct PagedKV {
 attn_status run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                        int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal,
                        int dtype, const Strides& st, int kv_split, void* workspace,
-                       size_t workspace_bytes, hipStream_t hs, const PagedKV* pg = nullptr) {
+                       size_t workspace_bytes, hipStream_t hs, const PagedKV* pg, int off) {
   const DecodePlan dp = make_decode_plan(B, Sq, Sk, Hq, Hkv, d, kv_split);
   if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   if (dp.pieces > 1 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
@@ -940,6 +941,7 @@ attn_status run_decode(const void* q, const void* k, const void* v, void* o, flo
   a.Sk = Sk;
   a.Hq = Hq;
   a.Hkv = Hkv;
+  a.off = off;
   a.piece_tiles = dp.piece_tiles;
   a.rgroups = dp.rgroups;
   a.ucols = dp.ucols;
@@ -980,16 +982,16 @@ attn_status run_decode(const void* q, const void* k, const void* v, void* o, flo
 attn_status run_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal,
                         int dtype, const Strides& st, int kv_split, void* workspace,
-                        size_t workspace_bytes, hipStream_t hs) {
+                        size_t workspace_bytes, hipStream_t hs, int off) {
   if (decode_eligible(Sq, Hq, Hkv, d))
     return run_decode(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype, st, kv_split,
-                      workspace, workspace_bytes, hs);
-  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split);
+                      workspace, workspace_bytes, hs, nullptr, off);
+  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, off);
   if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   if (sp.chunk > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
                        workspace_bytes < sp.ws_bytes))
     return ATTN_ERR_INVALID_ARG;
-  Params p = fill_params(sp.base, q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, scale, st);
+  Params p = fill_params(sp.base, q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, scale, st, off);
   if (sp.chunk == 0) {
     hipError_t e = launch_attn(dtype, d, causal, sp.base, sp.grid, p, hs);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -1017,7 +1019,7 @@ attn_status run_forward(const void* q, const void* k, const void* v, void* o, fl
   mp.rows_wg = sp.base.rows_wg;
   mp.chunk = sp.chunk;
   mp.Sk = Sk;
-  mp.off = Sk - Sq;
+  mp.off = off;
   mp.causal = causal;
   e = launch_merge_any(ATTN_DTYPE_F32, dtype, d, sp.merge_grid, mp, hs);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -1068,7 +1070,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
   attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
   if (st != ATTN_OK) return st;
   return run_forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype,
-                     dense_strides(Sq, Sk, Hq, Hkv, d), 1, nullptr, 0, (hipStream_t)stream);
+                     dense_strides(Sq, Sk, Hq, Hkv, d), 1, nullptr, 0, (hipStream_t)stream, Sk - Sq);
 }
 
 attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
@@ -1088,7 +1090,7 @@ attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, i
     for (int i = 0; i < n && i < 5; ++i) out[i] = vals[i];
     return ATTN_OK;
   }
-  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split);
+  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, Sk - Sq);
   if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   const int vals[5] = {(int)sp.grid, sp.npieces, sp.chunk * BC, sp.q_first,
                        (int)sp.merge_grid};
@@ -1104,7 +1106,7 @@ attn_status attn_fwd_split_workspace(int B, int Sq, int Sk, int Hq, int Hkv, int
   if (st != ATTN_OK) return st;
   *bytes = decode_eligible(Sq, Hq, Hkv, d)
                ? make_decode_plan(B, Sq, Sk, Hq, Hkv, d, kv_split).ws_bytes
-               : make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split).ws_bytes;
+               : make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, Sk - Sq).ws_bytes;
   return ATTN_OK;
 }
 
@@ -1117,7 +1119,7 @@ attn_status attn_fwd_split(const void* q, const void* k, const void* v, void* o,
   if (kv_split < 0) return ATTN_ERR_INVALID_ARG;
   return run_forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype,
                      dense_strides(Sq, Sk, Hq, Hkv, d), kv_split, workspace, workspace_bytes,
-                     (hipStream_t)stream);
+                     (hipStream_t)stream, Sk - Sq);
 }
 
 attn_status attn_fwd_strided_check(const void* q, const void* k, const void* v, void* o,
@@ -1140,7 +1142,53 @@ attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* 
   Strides sv;
   for (int i = 0; i < 12; ++i) sv.s[i] = strides[i];
   return run_forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype, sv, kv_split,
-                     workspace, workspace_bytes, (hipStream_t)stream);
+                     workspace, workspace_bytes, (hipStream_t)stream, Sk - Sq);
+}
+
+attn_status attn_fwd_causal_offset_check(const void* q, const void* k, const void* v, void* o,
+                                         float* lse, int B, int Sq, int Sk, int Hq, int Hkv,
+                                         int d, float scale, long long causal_offset, int dtype,
+                                         const long long* strides) {
+  attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, 1, dtype);
+  if (st != ATTN_OK) return st;
+  if (causal_offset <= -(1ll << 30) || causal_offset >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
+  return strides != nullptr ? validate_strides((const int64_t*)strides) : ATTN_OK;
+}
+
+attn_status attn_fwd_causal_offset_workspace(int B, int Sq, int Sk, int Hq, int Hkv, int d,
+                                             long long causal_offset, int dtype, int kv_split,
+                                             size_t* bytes) {
+  if (bytes == nullptr || kv_split < 0) return ATTN_ERR_INVALID_ARG;
+  int out[1];
+  attn_status st = attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, 1, dtype, out, 1);
+  if (st != ATTN_OK) return st;
+  if (causal_offset <= -(1ll << 30) || causal_offset >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
+  if (decode_eligible(Sq, Hq, Hkv, d)) {
+    const DecodePlan dp = make_decode_plan(B, Sq, Sk, Hq, Hkv, d, kv_split);
+    if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
+    *bytes = dp.ws_bytes;
+    return ATTN_OK;
+  }
+  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, 1, kv_split, (int)causal_offset);
+  if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
+  *bytes = sp.ws_bytes;
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_causal_offset(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int d,
+                                   float scale, long long causal_offset, int dtype,
+                                   const long long* strides, int kv_split, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  attn_status st = attn_fwd_causal_offset_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale,
+                                                causal_offset, dtype, strides);
+  if (st != ATTN_OK) return st;
+  if (kv_split < 0) return ATTN_ERR_INVALID_ARG;
+  Strides sv = dense_strides(Sq, Sk, Hq, Hkv, d);
+  if (strides != nullptr)
+    for (int i = 0; i < 12; ++i) sv.s[i] = strides[i];
+  return run_forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, 1, dtype, sv, kv_split,
+                     workspace, workspace_bytes, (hipStream_t)stream, (int)causal_offset);
 }
 
 attn_status attn_merge_check(const void* o_parts, const float* lse_parts, int n_parts,
@@ -1243,7 +1291,8 @@ attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_
   sv.s[6] = 0, sv.s[7] = (int64_t)Hkv * d, sv.s[8] = d;
   const PagedKV pg{block_table, seqlens, num_blocks, block_size, max_blocks};
   return run_decode(q, k_cache, v_cache, o, lse, B, Sq, max_seqlen, Hq, Hkv, d, scale, causal,
-                    dtype, sv, kv_split, workspace, workspace_bytes, (hipStream_t)stream, &pg);
+                    dtype, sv, kv_split, workspace, workspace_bytes, (hipStream_t)stream, &pg,
+                    max_seqlen - Sq);
 }
 
 const char* attn_status_str(int status) {

@@ -193,6 +193,44 @@ attn_status attn_fwd_strided_check(const void* q, const void* k, const void* v,
                                    const long long* strides);
 
 /*
+ * attn_fwd_causal_offset -- causal attention with the mask's offset given
+ * explicitly: query i sees key j iff j <= i + causal_offset (attn_fwd's
+ * causal mode is causal_offset = Sk - Sq).  This is what a shard of the keys
+ * of a longer causal problem needs (context parallelism): for keys
+ * [k0, k0 + Sk) of a problem with Sk_total keys, causal_offset =
+ * Sk_total - Sq - k0, and the shards' outputs and LSEs merge into the full
+ * attention with attn_merge (the pages' online-softmax rescale applied to
+ * whole parts; "FlashAttention personal implementation notes", section
+ * "Online Softmax").  Rows that see no key of the shard get O = 0 and
+ * LSE = -inf, which the merge weighs 0.
+ *
+ *   causal_offset  -2^30 < causal_offset < 2^30
+ *   strides        NULL (dense (B, S, H, d)) or as for attn_fwd_strided
+ *   the rest       as for attn_fwd_split; the workspace size is
+ *                  attn_fwd_causal_offset_workspace's
+ */
+attn_status attn_fwd_causal_offset(const void* q, const void* k, const void* v,
+                                   void* o, float* lse, int B, int Sq, int Sk,
+                                   int Hq, int Hkv, int d, float scale,
+                                   long long causal_offset, int dtype,
+                                   const long long* strides, int kv_split,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+attn_status attn_fwd_causal_offset_check(const void* q, const void* k,
+                                         const void* v, void* o, float* lse,
+                                         int B, int Sq, int Sk, int Hq, int Hkv,
+                                         int d, float scale,
+                                         long long causal_offset, int dtype,
+                                         const long long* strides);
+
+attn_status attn_fwd_causal_offset_workspace(int B, int Sq, int Sk, int Hq,
+                                             int Hkv, int d,
+                                             long long causal_offset,
+                                             int dtype, int kv_split,
+                                             size_t* bytes);
+
+/*
  * attn_fwd_split_workspace -- bytes of workspace attn_fwd_split needs for
  * these arguments (0 when it would not split), without any device call.
  * Returns the status attn_fwd_split's validation of the sizes would return.

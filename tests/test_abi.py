@@ -513,3 +513,33 @@ def test_paged_decode_rejects_before_any_device_call():
     assert lib.attn_decode_paged(*p, *a, 0, 0x200000, need - 4, None) == ATTN_ERR_INVALID_ARG
     assert lib.attn_decode_paged(*p, *a, 0, 0x200010, need, None) == ATTN_ERR_INVALID_ARG
     assert lib.attn_decode_paged(*p, *vals, -1, None, 0, None) == ATTN_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------- causal offset
+
+def test_causal_offset_validation_and_workspace():
+    lib = _lib()
+    p = [A + 0x1000 * i for i in range(5)]
+    args = (*p, 2, 100, 120, 8, 2, 128, ctypes.c_float(0.125))
+    assert lib.attn_fwd_causal_offset_check(*args, 20, ATTN_DTYPE_BF16, None) == ATTN_OK
+    assert lib.attn_fwd_causal_offset_check(*args, -5000, ATTN_DTYPE_BF16, None) == ATTN_OK
+    for off in (1 << 30, -(1 << 30), 1 << 40):
+        assert lib.attn_fwd_causal_offset_check(*args, off, ATTN_DTYPE_BF16,
+                                                None) == ATTN_ERR_INVALID_ARG, off
+    bad = binding._strides_arg([8] * 11 + [3])
+    assert lib.attn_fwd_causal_offset_check(*args, 20, ATTN_DTYPE_BF16,
+                                            bad) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_causal_offset_check(*args, 20, 5, None) == ATTN_ERR_UNSUPPORTED
+    # with the offset Sk - Sq the workspace is attn_fwd_split's (causal)
+    for cfg in ((1, 1280, 1536, 16, 16, 128), (2, 1024, 1024, 16, 16, 128),
+                (1, 1, 32768, 32, 8, 128)):
+        B, Sq, Sk, Hq, Hkv, d = cfg
+        for ks in (0, 1, 4):
+            assert binding.attn_fwd_causal_offset_workspace(
+                B, Sq, Sk, Hq, Hkv, d, Sk - Sq, ATTN_DTYPE_F16, ks) == \
+                binding.attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, 1, ATTN_DTYPE_F16, ks)
+    # a shard whose keys no row sees needs no split
+    assert binding.attn_fwd_causal_offset_workspace(1, 1280, 1536, 16, 16, 128, -2000,
+                                                    ATTN_DTYPE_F16, 0) == 0
+    with pytest.raises(binding.AttnError):
+        binding.attn_fwd_causal_offset_workspace(1, 100, 100, 8, 2, 128, 0, ATTN_DTYPE_F16, -1)
