@@ -105,6 +105,10 @@ WORKLOADS = {
         Workload("gqa8_causal_outlier_bf16_b1_hq32_hkv4_s16384_d128", 1, 32, 4,
                  16384, 16384, 128, "bf16", True, 1.0 / math.sqrt(128),
                  "outlier"),
+        # the MiniPaged-Qwen page's Qwen3-0.6B attention heads (Hq 16, Hkv 8,
+        # group 2, d 128) on 4K-token prompts, 4 sequences
+        Workload("gqa2_causal_bf16_b4_hq16_hkv8_s4096_d128", 4, 16, 8, 4096, 4096, 128, "bf16",
+                 True, 1.0 / math.sqrt(128)),
         # decode: the 8K GQA heads, one new token for each of 32 sequences
         Workload("decode_gqa4_bf16_b32_hq32_hkv8_sq1_sk8192_d128", 32, 32, 8, 1,
                  8192, 128, "bf16", True, 1.0 / math.sqrt(128)),

@@ -176,7 +176,8 @@ def _sample_rows(w: Workload, per_head: int, seed: int):
 
 
 @pytest.mark.parametrize("name", ["gqa4_causal_bf16_b1_hq32_hkv8_s8192_d128",
-                                  "gqa8_causal_outlier_bf16_b1_hq32_hkv4_s16384_d128"])
+                                  "gqa8_causal_outlier_bf16_b1_hq32_hkv4_s16384_d128",
+                                  "gqa2_causal_bf16_b4_hq16_hkv8_s4096_d128"])
 def test_full_size_gqa_sampled_rows(name):
     w = WORKLOADS[name]
     q, k, v = make_inputs(w, seed=0)
