@@ -387,6 +387,9 @@ def main():
             # the event pair then times both
             "launches_per_step": 3 if args.backward else (2 if split["keys_per_piece"] > 0 else 1),
             "kernel_avg_us": round(kern_avg_s * 1e6, 2),
+            # the algorithmic bytes over the kernel time, whatever the bound
+            "algorithmic_gbs": round(((bwd_bytes(w) if args.backward else w.algorithmic_bytes())
+                                      / kern_avg_s / 1e9), 1),
             "kernel_min_us": round(kern_min_s * 1e6, 2),
             "kernel_median_us": round(kern_med_s * 1e6, 2),
             "flops_per_launch": flops,
