@@ -6,13 +6,14 @@ over workgroups and merges them (small grids); ``attn_fwd_strided`` takes
 strided views (e.g. the (B, H, S, d) layout); ``attn_merge`` combines
 partial states over disjoint key subsets; ``attn_bwd`` gives dQ, dK, dV;
 ``attn_decode_paged`` runs decode attention over a paged K/V cache;
-``attn_fwd_causal_offset`` takes the causal mask's offset explicitly (a key
-shard of a longer causal problem).  The
+``attn_fwd_causal_offset`` and ``attn_bwd_causal_offset`` take the causal
+mask's offset explicitly (a key shard of a longer causal problem).  The
 library is loaded on first use; if it has not been built, that call raises
 ImportError (there is no fallback path).
 """
 from .binding import (  # noqa: F401
-    AttnError, attn_abi_version, attn_bwd, attn_bwd_check, attn_bwd_workspace,
+    AttnError, attn_abi_version, attn_bwd, attn_bwd_causal_offset,
+    attn_bwd_causal_offset_check, attn_bwd_check, attn_bwd_workspace,
     attn_decode_paged, attn_decode_paged_check, attn_decode_paged_workspace, attn_fwd,
     attn_fwd_causal_offset, attn_fwd_causal_offset_workspace,
     attn_fwd_check, attn_fwd_plan, attn_fwd_split, attn_fwd_split_plan,

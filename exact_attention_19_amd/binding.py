@@ -19,7 +19,8 @@ ATTN_DTYPE_F16, ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1, 2
 EXPORTED = ("attn_fwd", "attn_fwd_check", "attn_fwd_plan", "attn_fwd_split",
             "attn_fwd_split_workspace", "attn_fwd_split_plan", "attn_fwd_strided",
             "attn_fwd_strided_check", "attn_merge", "attn_merge_check", "attn_bwd",
-            "attn_bwd_check", "attn_bwd_workspace", "attn_fwd_causal_offset",
+            "attn_bwd_check", "attn_bwd_workspace", "attn_bwd_causal_offset",
+            "attn_bwd_causal_offset_check", "attn_fwd_causal_offset",
             "attn_fwd_causal_offset_check", "attn_fwd_causal_offset_workspace", "attn_decode_paged",
             "attn_decode_paged_check", "attn_decode_paged_workspace", "attn_status_str",
             "attn_abi_version")
@@ -80,6 +81,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_causal_offset_check.argtypes = [vp] * 5 + [i] * 6 + [f, lo, i, vp]
     lib.attn_fwd_causal_offset_workspace.restype = i
     lib.attn_fwd_causal_offset_workspace.argtypes = [i] * 6 + [lo, i, i, ctypes.POINTER(sz)]
+    lib.attn_bwd_causal_offset.restype = i
+    lib.attn_bwd_causal_offset.argtypes = [vp] * 9 + [i] * 6 + [f, lo, i, vp, sz, vp]
+    lib.attn_bwd_causal_offset_check.restype = i
+    lib.attn_bwd_causal_offset_check.argtypes = [vp] * 9 + [i] * 6 + [f, lo, i]
     lib.attn_decode_paged.restype = i
     lib.attn_decode_paged.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, i, vp, sz, vp]
     lib.attn_decode_paged_check.restype = i
@@ -451,13 +456,16 @@ def attn_bwd_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, 
                                              float(scale), int(causal), dtype_code))
 
 
-def attn_bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False,
-             dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Gradients (dq, dk, dv) of sum(dout * o) for o, lse = attn_fwd(q, k, v).
+def attn_bwd_causal_offset_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                                 dv_ptr, B, Sq, Sk, Hq, Hkv, d, scale, causal_offset,
+                                 dtype_code) -> int:
+    """attn_bwd_causal_offset's validation on raw addresses; returns the status code."""
+    return int(load_library().attn_bwd_causal_offset_check(
+        q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, B, Sq, Sk, Hq, Hkv,
+        d, float(scale), ctypes.c_longlong(int(causal_offset)), dtype_code))
 
-    q, o, dout: (B, Sq, Hq, d); k, v: (B, Sk, Hkv, d); one dtype (fp16/bf16),
-    dense; lse: (B, Hq, Sq) fp32 from attn_fwd.  Outputs are allocated when
-    not given; ``workspace`` (uint8, attn_bwd_workspace bytes) likewise."""
+
+def _bwd_args(q, k, v, o, lse, dout, scale, dq, dk, dv, workspace, stream):
     import torch
     B, Sq, Sk, Hq, Hkv, d, code = _check_qkv(q, k, v)
     for name, t in (("o", o), ("dout", dout)):
@@ -479,15 +487,42 @@ def attn_bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = F
                                 device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = load_library().attn_bwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Sq, Sk, Hq, Hkv, d, float(scale),
-        int(bool(causal)), code, workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream.cuda_stream))
+    head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            B, Sq, Sk, Hq, Hkv, d, float(scale))
+    tail = (code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(stream.cuda_stream))
+    return head, tail, (dq, dk, dv)
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * o) for o, lse = attn_fwd(q, k, v).
+
+    q, o, dout: (B, Sq, Hq, d); k, v: (B, Sk, Hkv, d); one dtype (fp16/bf16),
+    dense; lse: (B, Hq, Sq) fp32 from attn_fwd.  Outputs are allocated when
+    not given; ``workspace`` (uint8, attn_bwd_workspace bytes) likewise."""
+    head, tail, out = _bwd_args(q, k, v, o, lse, dout, scale, dq, dk, dv, workspace, stream)
+    st = load_library().attn_bwd(*head, int(bool(causal)), *tail)
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
-    return dq, dk, dv
+    return out
 
+
+def attn_bwd_causal_offset(q, k, v, o, lse, dout, causal_offset: int,
+                           scale: float | None = None, dq=None, dk=None, dv=None,
+                           workspace=None, stream=None):
+    """Backward of one causal key shard: query i sees key j of k/v iff
+    j <= i + causal_offset.  o and lse are the FULL problem's (the merged
+    forward over all shards); the returned dk, dv are this shard's exact
+    gradients and dq is its part of the full dQ (the parts of all shards sum
+    to it).  Arguments otherwise as for attn_bwd."""
+    head, tail, out = _bwd_args(q, k, v, o, lse, dout, scale, dq, dk, dv, workspace, stream)
+    st = load_library().attn_bwd_causal_offset(*head, ctypes.c_longlong(int(causal_offset)),
+                                               *tail)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_causal_offset")
+    return out
 
 def attn_decode_paged_check(q_ptr, k_ptr, v_ptr, table_ptr, lens_ptr, o_ptr, lse_ptr, B, Sq,
                             Hq, Hkv, d, num_blocks, block_size, max_blocks, max_seqlen, scale,

@@ -665,13 +665,16 @@ attn_status attn_bwd_workspace(int B, int Sq, int Hq, size_t* bytes) {
   return ATTN_OK;
 }
 
-attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                     const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
-                     int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal, int dtype,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  attn_status st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Sk, Hq, Hkv, d, scale,
-                                causal, dtype);
-  if (st != ATTN_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// The three launches for causal offset `off` (query i sees key j <= i + off;
+// Sk - Sq for attn_bwd), after validation.
+attn_status run_bwd(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                    int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream, int off) {
   const size_t need = bwd_workspace_bytes(B, Sq, Hq);
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
     return ATTN_ERR_INVALID_ARG;
@@ -700,13 +703,52 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   p.qtiles = pl.qtiles;
   p.ncols = pl.ncols;
   p.xcd_cols = pl.xcd_cols;
-  p.off = Sk - Sq;
+  p.off = off;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = dtype == ATTN_DTYPE_BF16 ? launch_bwd_d<ATTN_DTYPE_BF16>(d, causal != 0, pl, p, hs)
                                           : launch_bwd_d<ATTN_DTYPE_F16>(d, causal != 0, pl, p, hs);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                     int Sq, int Sk, int Hq, int Hkv, int d, float scale, int causal, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Sk, Hq, Hkv, d, scale,
+                                causal, dtype);
+  if (st != ATTN_OK) return st;
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype,
+                 workspace, workspace_bytes, stream, Sk - Sq);
+}
+
+attn_status attn_bwd_causal_offset_check(const void* q, const void* k, const void* v,
+                                         const void* o, const float* lse, const void* dout,
+                                         void* dq, void* dk, void* dv, int B, int Sq, int Sk,
+                                         int Hq, int Hkv, int d, float scale,
+                                         long long causal_offset, int dtype) {
+  attn_status st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Sk, Hq, Hkv, d, scale,
+                                1, dtype);
+  if (st != ATTN_OK) return st;
+  if (causal_offset <= -(1ll << 30) || causal_offset >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_causal_offset(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dout, void* dq, void* dk,
+                                   void* dv, int B, int Sq, int Sk, int Hq, int Hkv, int d,
+                                   float scale, long long causal_offset, int dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = attn_bwd_causal_offset_check(q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Sk, Hq,
+                                                Hkv, d, scale, causal_offset, dtype);
+  if (st != ATTN_OK) return st;
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Sk, Hq, Hkv, d, scale, 1, dtype,
+                 workspace, workspace_bytes, stream, (int)causal_offset);
 }
 
 }  // extern "C"

@@ -330,6 +330,36 @@ attn_status attn_bwd_check(const void* q, const void* k, const void* v,
                            int Hq, int Hkv, int d, float scale, int causal,
                            int dtype);
 
+/*
+ * attn_bwd_causal_offset -- attn_bwd for causal attention with an explicit
+ * mask offset (query i sees key j iff j <= i + causal_offset), as
+ * attn_fwd_causal_offset computes it: the backward of one key shard of a
+ * longer causal problem.  Given the full problem's O and LSE (the merged
+ * forward) and dO, it returns exactly the shard's dK and dV, and its part
+ * of dQ (the sum over the shard's keys; the parts of all shards add up to
+ * dQ, which the caller sums, in fp32 for accuracy).
+ *
+ *   o, lse           the full problem's output and LSE (not the shard's)
+ *   causal_offset    -2^30 < causal_offset < 2^30
+ *   the rest         as for attn_bwd (dk, dv: the shard's Sk keys)
+ */
+attn_status attn_bwd_causal_offset(const void* q, const void* k, const void* v,
+                                   const void* o, const float* lse,
+                                   const void* dout, void* dq, void* dk,
+                                   void* dv, int B, int Sq, int Sk, int Hq,
+                                   int Hkv, int d, float scale,
+                                   long long causal_offset, int dtype,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+attn_status attn_bwd_causal_offset_check(const void* q, const void* k,
+                                         const void* v, const void* o,
+                                         const float* lse, const void* dout,
+                                         void* dq, void* dk, void* dv, int B,
+                                         int Sq, int Sk, int Hq, int Hkv, int d,
+                                         float scale, long long causal_offset,
+                                         int dtype);
+
 /* Workspace bytes attn_bwd needs for B * Hq * Sq query rows (no device call). */
 attn_status attn_bwd_workspace(int B, int Sq, int Hq, size_t* bytes);
 

@@ -543,3 +543,27 @@ def test_causal_offset_validation_and_workspace():
                                                     ATTN_DTYPE_F16, 0) == 0
     with pytest.raises(binding.AttnError):
         binding.attn_fwd_causal_offset_workspace(1, 100, 100, 8, 2, 128, 0, ATTN_DTYPE_F16, -1)
+
+
+def test_bwd_causal_offset_validation():
+    lib = _lib()
+    p = [A + 0x1000 * i for i in range(9)]
+    vals = (2, 100, 120, 8, 2, 128, 0.125)
+    for off in (20, -5000, 4000, 0):
+        assert binding.attn_bwd_causal_offset_check(*p, *vals, off, ATTN_DTYPE_BF16) == ATTN_OK
+    for off in (1 << 30, -(1 << 30), 1 << 40):
+        assert binding.attn_bwd_causal_offset_check(*p, *vals, off,
+                                                    ATTN_DTYPE_BF16) == ATTN_ERR_INVALID_ARG
+    # the checks of attn_bwd apply too
+    q = list(p)
+    q[3] = None
+    assert binding.attn_bwd_causal_offset_check(*q, *vals, 0, ATTN_DTYPE_F16) \
+        == ATTN_ERR_INVALID_ARG
+    assert binding.attn_bwd_causal_offset_check(*p, 2, 100, 120, 8, 2, 80, 0.125, 0,
+                                                ATTN_DTYPE_F16) == ATTN_ERR_UNSUPPORTED
+    assert binding.attn_bwd_causal_offset_check(*p, *vals, 0, 2) == ATTN_ERR_UNSUPPORTED
+    need = binding.attn_bwd_workspace(2, 100, 8)
+    args = (*p, 2, 100, 120, 8, 2, 128, ctypes.c_float(0.125), ctypes.c_longlong(7),
+            ATTN_DTYPE_BF16)
+    assert lib.attn_bwd_causal_offset(*args, None, need, None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_bwd_causal_offset(*args, 0x200000, need - 4, None) == ATTN_ERR_INVALID_ARG

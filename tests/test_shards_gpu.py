@@ -6,6 +6,11 @@ is the full causal attention (the single-device half of key sharding).
 Prefill and decode shapes, with and without the key split; offsets that
 leave every key visible or none.  Tolerances as for the forward, plus the
 extra rounding of 16-bit shard outputs in the merged result.
+
+attn_bwd_causal_offset, the backward of a shard given the full problem's O
+and LSE: its dK, dV are the slices of the oracle's full-problem gradients,
+and the sum of the shards' dQ parts is the full dQ, within the backward's
+derived bounds (plus the 16-bit rounding of each dQ part).
 """
 import math
 
@@ -97,3 +102,65 @@ def test_offsets_past_both_ends(Sq, Hq, Hkv):
     assert torch.allclose(o_all.float(), o_nc.float(), atol=2e-3, rtol=0)
     assert torch.allclose(l_all, l_nc, atol=1e-4, rtol=0)
     assert torch.all(o_none == 0) and torch.all(torch.isneginf(l_none))
+
+
+def _bwd_full(w, seed):
+    from exact_attention_19_amd import attn_fwd
+    q, k, v = make_inputs(w, seed=seed)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(seed + 1)).to(q.dtype)
+    o, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=True)
+    return q, k, v, do, o, lse
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,d,dt,cuts", [
+    (1, 8, 2, 300, 1000, 128, "bf16", [0, 250, 640, 1000]),
+    (2, 4, 4, 257, 257, 64, "f16", [0, 100, 257]),        # rows 0-99 see none of shard 2
+    (1, 4, 1, 333, 200, 96, "bf16", [0, 64, 200]),        # rows with no key at all
+    (2, 8, 4, 1, 700, 128, "bf16", [0, 300, 699, 700]),
+])
+def test_backward_key_shards(B, Hq, Hkv, Sq, Sk, d, dt, cuts):
+    from exact_attention_19_amd import attn_bwd_causal_offset
+    from oracle import attn_bwd_oracle
+    from test_bwd_gpu import TINY, U, error_bounds
+    w = _w(B, Hq, Hkv, Sq, Sk, d, dt)
+    q, k, v, do, o, lse = _bwd_full(w, seed=Sq + Sk + d)
+    qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    rq, rk, rv = attn_bwd_oracle(q, k, v, do, w.scale, True)
+    bq, bk, bv = error_bounds(q, k, v, do, o.cpu(), lse.cpu(), w.scale, True, dt)
+    u = U[dt]
+    dq_sum = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    dq_mag = torch.zeros_like(dq_sum)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        off = Sk - Sq - a
+        _say(f"[gpu] attn_bwd_causal_offset {w.name} keys [{a}, {b}) offset {off}")
+        dq, dk, dv = attn_bwd_causal_offset(qg, kg[:, a:b].contiguous(), vg[:, a:b].contiguous(),
+                                            o, lse, dog, off, scale=w.scale)
+        torch.cuda.synchronize()
+        for name, got, ref, bound in (("dk", dk, rk[:, a:b], bk[:, a:b]),
+                                      ("dv", dv, rv[:, a:b], bv[:, a:b])):
+            gd = got.double().cpu().numpy()
+            allowed = 2.0 * (bound + u * np.abs(ref)) + 0.5 * TINY[dt]
+            diff = np.abs(gd - ref)
+            assert np.isfinite(gd).all() and np.all(diff <= allowed), \
+                f"{name} [{a}, {b}): max|d| {diff.max():.3e}, worst use {(diff / allowed).max():.2f}"
+        dq_sum += dq.float()
+        dq_mag += dq.float().abs()
+    gd = dq_sum.double().cpu().numpy()
+    # each part was rounded to 16 bit once more than the single-call dQ
+    allowed = 2.0 * (bq + u * np.abs(rq)) + u * dq_mag.double().cpu().numpy() \
+        + len(cuts) * 0.5 * TINY[dt]
+    diff = np.abs(gd - rq)
+    assert np.all(diff <= allowed), \
+        f"dq: max|d| {diff.max():.3e}, worst use {(diff / allowed).max():.2f}"
+
+
+def test_backward_offset_sk_minus_sq_is_attn_bwd():
+    from exact_attention_19_amd import attn_bwd, attn_bwd_causal_offset
+    w = _w(1, 8, 2, 200, 333, 128, "bf16")
+    q, k, v, do, o, lse = _bwd_full(w, seed=8)
+    qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    a = attn_bwd(qg, kg, vg, o, lse, dog, scale=w.scale, causal=True)
+    b = attn_bwd_causal_offset(qg, kg, vg, o, lse, dog, 333 - 200, scale=w.scale)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
