@@ -567,3 +567,20 @@ def test_bwd_causal_offset_validation():
             ATTN_DTYPE_BF16)
     assert lib.attn_bwd_causal_offset(*args, None, need, None) == ATTN_ERR_INVALID_ARG
     assert lib.attn_bwd_causal_offset(*args, 0x200000, need - 4, None) == ATTN_ERR_INVALID_ARG
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """load_library() before `import torch` must not map a second HIP runtime
+    (torch's bundled one beside /opt/rocm's): the process would crash."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from exact_attention_19_amd import binding\n"
+            "binding.load_library()\n"
+            "import torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         timeout=600, cwd="/tmp")
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
