@@ -180,6 +180,24 @@ def test_bwd_gqa_head_layout_at_1536():
     _check(w, *_run(w))
 
 
+@pytest.mark.timeout(900)
+def test_bwd_full_size_kv_group():
+    """The 8K GQA workload at full size, in the launch configuration that
+    bench.py --backward times (all 32 query heads, 8 kv heads).  The
+    gradients of kv group 0 (query heads 0-3, kv head 0) depend only on that
+    group's tensors, so the oracle run on the group alone is their exact
+    reference: every element of dq[:, :, 0:4], dk[:, :, 0] and dv[:, :, 0]."""
+    w = WORKLOADS["gqa4_causal_bf16_b1_hq32_hkv8_s8192_d128"]
+    q, k, v, do, o, lse, dq, dk, dv = _run(w)
+    g = w.Hq // w.Hkv
+    sub = w.with_(name="bwd_gqa4_s8192_group0", Hq=g, Hkv=1)
+    _say(f"[cpu] oracle on kv group 0 of {w.name} (about half a minute)")
+    hq = lambda t: t[:, :, :g].contiguous()
+    hk = lambda t: t[:, :, :1].contiguous()
+    _check(sub, hq(q), hk(k), hk(v), hq(do), hq(o), lse[:, :g].contiguous(), hq(dq), hk(dk),
+           hk(dv))
+
+
 def test_bwd_deterministic():
     from exact_attention_19_amd import attn_bwd, attn_fwd
     w = Workload("bwd_det", 1, 8, 2, 333, 517, 128, "bf16", True, 0.1)
