@@ -660,20 +660,54 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
     if (n == 1) return;  // a block that was not split wrote O itself
   }
   const int64_t lrow = ((int64_t)b * p.Hq + hq) * p.sq_rows + ii;
+  // one pass over the pieces, MB at a time: the loads of a batch are all in
+  // flight together (a decode row can have 16 or more pieces, and few rows
+  // give the kernel few waves to hide a round trip per piece), and the
+  // running max M rescales the sums when a batch raises it.  MB follows the
+  // piece count (2, 4 or 8) so that short merges load no empty slots.
   float M = -INFINITY;
-  for (int q = 0; q < n; ++q) M = fmaxf(M, p.parts_lse[(int64_t)q * p.rows + lrow]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
-  if (M > -INFINITY) {
-    for (int q = 0; q < n; ++q) {
-      const float w =
-          __builtin_amdgcn_exp2f((p.parts_lse[(int64_t)q * p.rows + lrow] - M) * LOG2E);
-      const f32x4 x = load_part4<PDT>(p.parts, ((int64_t)q * p.rows + r) * D + c);
-      W += w;
+  auto merge = [&](auto mb) {
+    constexpr int MB = decltype(mb)::value;
+    for (int q0 = 0; q0 < n; q0 += MB) {
+      float l[MB];
+      f32x4 x[MB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, x[e], acc[e]);
+      for (int e = 0; e < MB; ++e) {
+        const int q = q0 + e;
+        l[e] = -INFINITY;
+        x[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (q < n) {
+          l[e] = p.parts_lse[(int64_t)q * p.rows + lrow];
+          x[e] = load_part4<PDT>(p.parts, ((int64_t)q * p.rows + r) * D + c);
+        }
+      }
+      float m = M;
+#pragma unroll
+      for (int e = 0; e < MB; ++e) m = fmaxf(m, l[e]);
+      if (m > -INFINITY) {
+        const float a = __builtin_amdgcn_exp2f((M - m) * LOG2E);  // 0 while M = -inf
+        W *= a;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] *= a;
+#pragma unroll
+        for (int e = 0; e < MB; ++e) {
+          const float w = __builtin_amdgcn_exp2f((l[e] - m) * LOG2E);
+          W += w;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(w, x[e][k], acc[k]);
+        }
+        M = m;
+      }
     }
-  }
+  };
+  if (n <= 2)
+    merge(std::integral_constant<int, 2>{});
+  else if (n <= 4)
+    merge(std::integral_constant<int, 4>{});
+  else
+    merge(std::integral_constant<int, 8>{});
   const float inv = W > 0.f ? 1.f / W : 0.f;
   f32x8 y;
 #pragma unroll
