@@ -323,10 +323,13 @@ struct DecodePlan {
 // Pieces per (batch, kv head): kv_split 1 = none; k > 1 = k; 0 = the
 // library's choice.  Measured on MI355X: one decode workgroup per CU already
 // streams K and V at the chip's practical rate (5.5 TB/s with 256 of them; a
-// second workgroup per CU, or cutting into more pieces, was slower), and a
-// piece pays a fixed start-up and merge cost, so the choice splits only when
-// there are fewer than 128 workgroups per piece, into about 128 workgroups
-// with at least 32 tiles (8 per wave) each.
+// second workgroup per CU was slower), and each piece adds to the merge, so
+// the choice splits only when there are fewer than 256 workgroups, into
+// about 256 workgroups with at least 8 tiles (256 keys) each.  128
+// workgroups left half the CUs idle: 32K keys of one sequence took 35.5 us
+// in 16 pieces and 30.4 us in 32, 16 sequences of 8K 148 us unsplit and
+// 107 us in 2 pieces, and short sequences gain down to about 8 tiles per
+// piece (4K keys: 14.6 us in 8 pieces, 12.0 us in 16).
 //
 // With more than 32 query rows per kv head, each 32-row group is its own
 // workgroup; the groups of one (batch, kv head) are placed 8 workgroup ids
@@ -346,8 +349,8 @@ inline DecodePlan make_decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d
   const long long cols = bh * dp.rgroups;
   long long pieces = 1;
   if (kv_split == 0) {
-    if (cols < 128) pieces = (128 + cols - 1) / cols;
-    const long long most = ntiles / 32 > 1 ? ntiles / 32 : 1;
+    if (cols < 256) pieces = (256 + cols - 1) / cols;
+    const long long most = ntiles / 8 > 1 ? ntiles / 8 : 1;
     if (pieces > most) pieces = most;
   } else if (kv_split > 1) {
     pieces = kv_split;

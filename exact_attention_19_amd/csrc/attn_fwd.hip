@@ -664,7 +664,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
   // flight together (a decode row can have 16 or more pieces, and few rows
   // give the kernel few waves to hide a round trip per piece), and the
   // running max M rescales the sums when a batch raises it.  MB follows the
-  // piece count (2, 4 or 8) so that short merges load no empty slots.
+  // piece count (2, 4, 8 or 16) so that short merges load no empty slots.
   float M = -INFINITY;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
@@ -706,8 +706,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
     merge(std::integral_constant<int, 2>{});
   else if (n <= 4)
     merge(std::integral_constant<int, 4>{});
-  else
+  else if (n <= 8)
     merge(std::integral_constant<int, 8>{});
+  else
+    merge(std::integral_constant<int, 16>{});
   const float inv = W > 0.f ? 1.f / W : 0.f;
   f32x8 y;
 #pragma unroll

@@ -373,7 +373,7 @@ def test_bwd_workspace_and_early_rejection():
 def test_decode_plan(cfg, kv_split):
     """Decode shapes (g * Sq <= 32, d 32 to 128) take the decode kernel: one
     workgroup per (batch, kv head) and key piece; automatic pieces only below
-    128 (batch, kv head) pairs, about 128 workgroups of at least 32 tiles;
+    256 (batch, kv head) pairs, about 256 workgroups of at least 8 tiles;
     the workspace holds one fp32 row state per piece and query row."""
     _lib()
     B, Sq, Sk, Hq, Hkv, d, causal, dt = cfg
@@ -384,8 +384,8 @@ def test_decode_plan(cfg, kv_split):
     ntiles = -(-Sk // 32)
     cols = B * Hkv
     if kv_split == 0:
-        pieces = -(-128 // cols) if cols < 128 else 1
-        pieces = min(pieces, max(ntiles // 32, 1))
+        pieces = -(-256 // cols) if cols < 256 else 1
+        pieces = min(pieces, max(ntiles // 8, 1))
     else:
         pieces = kv_split if kv_split > 1 else 1
     pieces = min(pieces, ntiles)
@@ -422,8 +422,8 @@ def test_decode_plan_row_groups(cfg, kv_split):
     ntiles = -(-Sk // 32)
     cols = B * Hkv * rg
     if kv_split == 0:
-        pieces = -(-128 // cols) if cols < 128 else 1
-        pieces = min(pieces, max(ntiles // 32, 1))
+        pieces = -(-256 // cols) if cols < 256 else 1
+        pieces = min(pieces, max(ntiles // 8, 1))
     else:
         pieces = kv_split if kv_split > 1 else 1
     pieces = min(pieces, ntiles)
