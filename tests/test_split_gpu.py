@@ -243,6 +243,35 @@ def test_merge_empty_parts_and_rows():
     assert np.abs(lg[fin] - lse_ref[fin]).max() <= 1e-5
 
 
+@pytest.mark.parametrize("P", [1, 2, 3, 7, 9, 16, 17, 37])
+def test_merge_many_parts(P):
+    """Part counts on both sides of the merge's batch sizes (2, 4, 8, 16),
+    with LSEs growing by part (each batch raises the running max, so the sums
+    are rescaled), the first parts empty for some rows (the max starts at
+    -inf), and rows no part saw, against the fp64 oracle merge."""
+    from exact_attention_19_amd import attn_merge
+    B, Sq, Hq, d = 1, 24, 2, 128
+    r = np.random.default_rng(100 + P)
+    op = r.standard_normal((P, B, Sq, Hq, d)).astype(np.float32)
+    lp = (np.arange(P, dtype=np.float32)[:, None, None, None] * 1.5
+          + r.standard_normal((P, B, Hq, Sq)).astype(np.float32))
+    lp[: P // 2, :, :, 5:10] = -np.inf     # rows 5..9: the first half of the parts saw nothing
+    op[: P // 2, :, 5:10] = 0.0
+    lp[:, :, :, :3] = -np.inf              # rows 0..2: no part saw anything
+    op[:, :, :3] = 0.0
+    o_ref, lse_ref = merge_partials_oracle(op.astype(np.float64), lp.astype(np.float64))
+    _say(f"[gpu] attn_merge P={P} d={d}")
+    o, lse = attn_merge(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda(),
+                        dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    og, lg = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert np.all(og[:, :3] == 0) and np.all(np.isneginf(lg[:, :, :3]))
+    assert np.all(np.abs(og - o_ref) <= half_ulp(o_ref, "bf16") + 1e-5), np.abs(og - o_ref).max()
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lg), fin)
+    assert np.abs(lg[fin] - lse_ref[fin]).max() <= 1e-5 * (1 + np.abs(lse_ref[fin]).max())
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_key_shards_merged_equal_full_attention(dt):
     """Key-sharded attention on one device: attn_fwd on each key shard (no
