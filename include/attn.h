@@ -337,7 +337,10 @@ attn_status attn_bwd_check(const void* q, const void* k, const void* v,
  * longer causal problem.  Given the full problem's O and LSE (the merged
  * forward) and dO, it returns exactly the shard's dK and dV, and its part
  * of dQ (the sum over the shard's keys; the parts of all shards add up to
- * dQ, which the caller sums, in fp32 for accuracy).
+ * dQ, which the caller sums, in fp32 for accuracy).  This holds because the
+ * recomputation above needs, besides the shard's keys, only the row
+ * quantities LSE_i and D_i = dO_i . O_i of the full problem (the same reason
+ * the forward returns the LSE: "CuTe DSL example", docstring).
  *
  *   o, lse           the full problem's output and LSE (not the shard's)
  *   causal_offset    -2^30 < causal_offset < 2^30
