@@ -183,23 +183,52 @@ def _check_qkv(q, k, v):
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
+        _on_device(name, t, q.device)
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous (batch, seq, heads, d_head)")
     return B, Sq, Sk, Hq, Hkv, d, code
 
 
+def _on_device(name, t, device):
+    """A caller-given buffer the kernels write or read: a tensor on the GPU
+    that holds q (a host tensor or one on another GPU would take a device
+    address the kernel cannot use)."""
+    if not hasattr(t, "is_cuda") or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, q on {device}")
+
+
+def _check_lse(lse, B, Hq, Sq, device):
+    import torch
+    if lse is None:
+        return
+    _on_device("lse", lse, device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+
+
+def _check_workspace(workspace, device):
+    if workspace is None:
+        return
+    _on_device("workspace", workspace, device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
+
+
 def _outputs(q, out, lse, return_lse):
+    """out: (allocated here when None) a contiguous tensor with q's shape,
+    dtype and device; lse: fp32 (B, Hq, Sq) on the same device, or None."""
     import torch
     B, Sq, Hq, _ = q.shape
     if out is None:
         out = torch.empty_like(q)
+    _on_device("out", out, q.device)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {q.dtype} tensor of shape {tuple(q.shape)}")
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                            or tuple(lse.shape) != (B, Hq, Sq)):
-        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+    _check_lse(lse, B, Hq, Sq, q.device)
     return out, lse
 
 
@@ -242,6 +271,7 @@ def attn_fwd_split(q, k, v, scale: float | None = None, causal: bool = False,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse, return_lse)
+    _check_workspace(workspace, q.device)
     if workspace is None:  # (a given workspace is size-checked by the library)
         need = attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, causal, code, kv_split)
         if need > 0:
@@ -302,17 +332,15 @@ def attn_fwd_strided(q, k, v, scale: float | None = None, causal: bool = False,
     for name, t in (("q", qv), ("k", kv_), ("v", vv), ("out", ov)):
         if t.dtype != q.dtype:
             raise TypeError("q, k, v and out must share one dtype")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
+        _on_device(name, t, q.device)
         if t.stride(3) != 1:
             raise ValueError(f"{name}: the head dimension must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                            or tuple(lse.shape) != (B, Hq, Sq)):
-        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+    _check_lse(lse, B, Hq, Sq, q.device)
+    _check_workspace(workspace, q.device)
     strides = []
     for t in (qv, kv_, vv, ov):
         strides += [t.stride(0), t.stride(1), t.stride(2)]
@@ -370,8 +398,7 @@ def attn_fwd_causal_offset(q, k, v, causal_offset: int, scale: float | None = No
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         if t.dtype != q.dtype:
             raise TypeError("q, k, v and out must share one dtype")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
+        _on_device(name, t, q.device)
         if t.stride(3) != 1:
             raise ValueError(f"{name}: the head dimension must be contiguous")
     if tuple(out.shape) != (B, Sq, Hq, d):
@@ -380,9 +407,8 @@ def attn_fwd_causal_offset(q, k, v, causal_offset: int, scale: float | None = No
         scale = 1.0 / math.sqrt(d)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                            or tuple(lse.shape) != (B, Hq, Sq)):
-        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+    _check_lse(lse, B, Hq, Sq, q.device)
+    _check_workspace(workspace, q.device)
     strides = []
     for t in (q, k, v, out):
         strides += [t.stride(0), t.stride(1), t.stride(2)]
@@ -421,18 +447,21 @@ def attn_merge(o_parts, lse_parts, dtype=None, out=None, lse=None,
     if tuple(lse_parts.shape) != (P, B, Hq, Sq) or lse_parts.dtype != torch.float32:
         raise ValueError("lse_parts must be a float32 (P, B, Hq, Sq) tensor")
     for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts)):
-        if not t.is_cuda or not t.is_contiguous():
+        _on_device(name, t, o_parts.device)
+        if not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     pcode = _dtype_code(o_parts, allow_f32=True)
     if dtype is None:
         dtype = torch.bfloat16 if o_parts.dtype == torch.float32 else o_parts.dtype
     if out is None:
         out = torch.empty((B, Sq, Hq, d), dtype=dtype, device=o_parts.device)
+    _on_device("out", out, o_parts.device)
     ocode = _dtype_code(out)
     if tuple(out.shape) != (B, Sq, Hq, d) or not out.is_contiguous():
         raise ValueError("out must be a contiguous (B, Sq, Hq, d) tensor")
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=o_parts.device)
+    _check_lse(lse, B, Hq, Sq, o_parts.device)
     if stream is None:
         stream = torch.cuda.current_stream(o_parts.device)
     st = load_library().attn_merge(
@@ -474,19 +503,22 @@ def _bwd_args(q, k, v, o, lse, dout, scale, dq, dk, dv, workspace, stream):
     import torch
     B, Sq, Sk, Hq, Hkv, d, code = _check_qkv(q, k, v)
     for name, t in (("o", o), ("dout", dout)):
-        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_cuda \
-                or not t.is_contiguous():
+        _on_device(name, t, q.device)
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor like q")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor")
+    if lse is None:
+        raise ValueError("lse (the forward's, fp32 (B, Hq, Sq)) is required")
+    _check_lse(lse, B, Hq, Sq, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _on_device(name, t, q.device)
         if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous tensor shaped like its input")
+    _check_workspace(workspace, q.device)
     if workspace is None:
         workspace = torch.empty(attn_bwd_workspace(B, Sq, Hq), dtype=torch.uint8,
                                 device=q.device)
@@ -578,8 +610,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seqlens, scale: float | 
         raise ValueError("block_table must be (B, max_blocks) and seqlens (B,)")
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("block_table", block_table), ("seqlens", seqlens)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
+        _on_device(name, t, q.device)
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     max_blocks = block_table.shape[1]
@@ -588,6 +619,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seqlens, scale: float | 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse, return_lse)
+    _check_workspace(workspace, q.device)
     if workspace is None:
         need = attn_decode_paged_workspace(B, Sq, Hq, Hkv, d, int(max_seqlen), kv_split)
         if need > 0:

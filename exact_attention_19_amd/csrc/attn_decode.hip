@@ -169,8 +169,10 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
       const int64_t base = (h2 == 0 || !own) ? tr.r0 : tr.r1;
       const int rr = own ? min(row, last - 16 * h2) : last;
       const uint32_t off = (uint32_t)rr * rbv + (uint32_t)chunk * 16;
+      // the descriptor spans the 16 rows' bytes, 15 strides + one row of D
+      // elements (a stride below D, or 0, still reads whole rows)
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vbase + base * (int64_t)rbv), 0, (int)(16 * rbv), 0x00020000);
+          (void*)(vbase + base * (int64_t)rbv), 0, (int)(15 * rbv + D * 2), 0x00020000);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(

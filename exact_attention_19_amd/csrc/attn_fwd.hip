@@ -264,8 +264,11 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
   // global load to LDS would also do, but the compiler then assumes it may
   // count on the LDS counter and waits for every outstanding LDS read at
   // each dependency.)  Rows past Sk in the ragged last tile re-read row
-  // Sk - 1 (their keys are masked).  Host validation keeps BC * (row stride)
-  // below 2^31.
+  // Sk - 1 (their keys are masked).  The descriptor spans the bytes the
+  // tile's rows occupy, (BC - 1) * (row stride) + one row of D elements, so
+  // a row stride below D (overlapping or broadcast K/V views, stride 0
+  // included) still reads every row whole.  Host validation keeps BC * (row
+  // stride) below 2^31.
   const uint32_t ld_off_k = (uint32_t)ld_row * rbk + (uint32_t)ld_col * 2;
   const uint32_t ld_off_v = (uint32_t)ld_row * rbv + (uint32_t)ld_col * 2;
   auto issue_rows = [&](const char* slice, uint32_t row_bytes, uint32_t ld_off, int n,
@@ -276,7 +279,8 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
       off = (uint32_t)(min(n * BC + ld_row, p.Sk - 1) - n * BC) * row_bytes + (uint32_t)ld_col * 2;
     // raw buffer, 32-bit data format (word 3 of the descriptor)
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)(BC * row_bytes), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)((BC - 1) * row_bytes + D * 2),
+                                          0x00020000);
 #pragma unroll
     for (int u = 0; u < CPT; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_PTR(void))(buf + (u * NW + wave) * 1024),
@@ -761,13 +765,41 @@ Strides dense_strides(int Sq, int Sk, int Hq, int Hkv, int d) {
   return Strides{{q[0], q[1], q[2], k[0], k[1], k[2], k[0], k[1], k[2], q[0], q[1], q[2]}};
 }
 
-// Strides: non-negative multiples of 8 elements (16-byte aligned rows), and a
-// K or V tile (64 key rows) within 2^31 bytes of its first row.
-attn_status validate_strides(const int64_t* st) {
+// The rows of an output view (sizes n[3], element strides s[3], rows of d
+// contiguous elements) are pairwise disjoint: taking the dimensions of more
+// than one index by increasing stride, each stride reaches past everything
+// the smaller ones span.  (Sufficient, not necessary: a view that fails it
+// may still be disjoint, but every dense or sliced layout passes.)
+bool rows_disjoint(const int64_t* n, const int64_t* s, int64_t d) {
+  int idx[3] = {0, 1, 2};
+  for (int a = 0; a < 3; ++a)
+    for (int b = a + 1; b < 3; ++b)
+      if (s[idx[b]] < s[idx[a]]) {
+        const int t = idx[a];
+        idx[a] = idx[b];
+        idx[b] = t;
+      }
+  int64_t extent = d;  // elements spanned by the dimensions taken so far
+  for (int a = 0; a < 3; ++a) {
+    const int i = idx[a];
+    if (n[i] <= 1) continue;
+    if (s[i] < extent) return false;
+    extent += s[i] * (n[i] - 1);
+  }
+  return true;
+}
+
+// Strides: non-negative multiples of 8 elements (16-byte aligned rows), a K
+// or V tile (64 key rows) within 2^31 bytes of its first row, and output rows
+// that do not overlap (two rows written to one address would race).  q, k
+// and v are only read: any strides, 0 (a broadcast) included.
+attn_status validate_strides(const int64_t* st, int B, int Sq, int Hq, int d) {
   if (st == nullptr) return ATTN_ERR_INVALID_ARG;
   for (int i = 0; i < 12; ++i)
     if (st[i] < 0 || (st[i] & 7) != 0) return ATTN_ERR_INVALID_ARG;
   if (st[4] * 2 * 64 >= (1ll << 31) || st[7] * 2 * 64 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  const int64_t n_o[3] = {B, Sq, Hq};
+  if (!rows_disjoint(n_o, st + 9, d)) return ATTN_ERR_INVALID_ARG;
   return ATTN_OK;
 }
 
@@ -1164,7 +1196,7 @@ attn_status attn_fwd_strided_check(const void* q, const void* k, const void* v, 
                                    const long long* strides) {
   attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
   if (st != ATTN_OK) return st;
-  return validate_strides((const int64_t*)strides);
+  return validate_strides((const int64_t*)strides, B, Sq, Hq, d);
 }
 
 attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1188,7 +1220,7 @@ attn_status attn_fwd_causal_offset_check(const void* q, const void* k, const voi
   attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, 1, dtype);
   if (st != ATTN_OK) return st;
   if (causal_offset <= -(1ll << 30) || causal_offset >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
-  return strides != nullptr ? validate_strides((const int64_t*)strides) : ATTN_OK;
+  return strides != nullptr ? validate_strides((const int64_t*)strides, B, Sq, Hq, d) : ATTN_OK;
 }
 
 attn_status attn_fwd_causal_offset_workspace(int B, int Sq, int Sk, int Hq, int Hkv, int d,

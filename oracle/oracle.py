@@ -55,6 +55,16 @@ def _load():
     return _lib
 
 
+def default_threads() -> int:
+    """Threads for the oracle: the CPUs this process may run on, at most 16
+    (a GPU machine gives one GPU's jobs a 16-CPU share whatever it reports)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _as_f64(x) -> np.ndarray:
     """Widen a numpy array or a CPU torch tensor (any float dtype) to a
     contiguous fp64 numpy array.  Widening fp16/bf16/fp32 to fp64 is exact."""
@@ -83,7 +93,7 @@ def attn_fwd_oracle(q, k, v, scale: float, causal: bool, rows=None,
     if vd.shape != kd.shape or Bk != B or dk != d:
         raise ValueError("shape mismatch between q, k, v")
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = default_threads()
     dp = ctypes.POINTER(ctypes.c_double)
     if rows is None:
         o = np.empty((B, Sq, Hq, d), np.float64)
@@ -213,7 +223,7 @@ def attn_bwd_oracle(q, k, v, dout, scale: float, causal: bool, nthreads: int | N
     if vd.shape != kd.shape or Bk != B or dk_ != d or dod.shape != qd.shape:
         raise ValueError("shape mismatch between q, k, v, dout")
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = default_threads()
     dq = np.empty_like(qd)
     dk = np.empty_like(kd)
     dv = np.empty_like(vd)

@@ -286,7 +286,19 @@ def test_strided_validation():
     W = (Hq + 2 * Hkv) * d
     packed = [Sq * W, W, d, Sq * W, W, d, Sq * W, W, d] + good[9:]
     assert binding.attn_fwd_strided_check(*args, packed) == ATTN_OK
-    assert binding.attn_fwd_strided_check(*args, [0] * 12) == ATTN_OK  # broadcast reads
+    # q, k, v are only read: zero strides broadcast one row (the K/V tile
+    # descriptors span (rows - 1) strides + one row, so stride 0 reads whole rows)
+    assert binding.attn_fwd_strided_check(*args, [0] * 9 + good[9:]) == ATTN_OK
+    # output rows must not overlap: zero or too-small o strides race
+    for o_st in ([0, 0, 0], [Sq * Hq * d, 0, d], [Sq * Hq * d, Hq * d, 0],
+                 [Sq * Hq * d, Hq * d, d - 8], [8, Hq * d, d], [Sq * Hq * d, d, d]):
+        assert binding.attn_fwd_strided_check(*args, good[:9] + o_st) == ATTN_ERR_INVALID_ARG, o_st
+    # a dimension of size 1 may take any stride; gaps between rows are fine
+    one = (A, A + 0x1000, A + 0x2000, A + 0x3000, A + 0x4000, 1, Sq, Sk, 1, 1, d,
+           0.125, 1, ATTN_DTYPE_BF16)
+    assert binding.attn_fwd_strided_check(*one, [0, d, 0] * 4) == ATTN_OK
+    assert binding.attn_fwd_strided_check(*args, good[:9] + [Sq * Hq * 2 * d, Hq * 2 * d, 2 * d]) \
+        == ATTN_OK
     for i in range(12):
         for bad in (-8, 4, 1):
             st = list(good)
@@ -584,3 +596,18 @@ def test_one_hip_runtime_whatever_the_import_order():
                          timeout=600, cwd="/tmp")
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+def test_binding_checks_reject_host_buffers():
+    """The binding's buffer checks, on host tensors (no GPU needed): a host
+    output, LSE or workspace is refused before any library call."""
+    import torch
+    dev = torch.device("cuda:0")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding._on_device("out", torch.empty(4), dev)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding._check_lse(torch.empty((1, 2, 3), dtype=torch.float32), 1, 2, 3, dev)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding._check_workspace(torch.empty(16, dtype=torch.uint8), dev)
+    binding._check_lse(None, 1, 2, 3, dev)
+    binding._check_workspace(None, dev)

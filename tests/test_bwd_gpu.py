@@ -1,14 +1,25 @@
 """GPU parity of the backward pass (attn_bwd, through the C ABI) against the
 fp64 oracle's gradients.
 
+Inputs.  The backward consumes the forward's O and LSE.  The parity cases
+feed it the oracle's O (rounded to the 16-bit type) and LSE (rounded to
+fp32), so they test the backward kernels alone and their bound does not
+depend on how accurate the GPU forward happens to be.  The composed cases
+(GPU forward, then GPU backward, as a training step runs them) take the
+forward's stated tolerances instead: |dLSE| <= 1e-3 and |dO| <= 2e-3 (fp16)
+or 1e-2 (bf16) per element.
+
 Bound.  No page fixes a precision for gradients, so each element's bound is
 derived from the arithmetic (and written out below): with u the unit
 roundoff of the 16-bit type (2^-8 bf16, 2^-11 fp16),
-  P       is recomputed in fp32 from the forward's LSE: relative error
-          e_P = |dLSE| + 2^-20 (the measured LSE error of the same forward
-          call, plus exp2 and fp32 rounding);
-  D_i     = dO_i . O_i uses the forward's 16-bit O: |dD_i| =
-          |dO_i . (O_gpu - O)| + d 2^-24 |dO_i| . |O_i|;
+  P       is recomputed in fp32 from the given LSE: relative error
+          e_P = e_LSE + 2^-20 (the error of the LSE handed in -- its fp32
+          rounding, or the forward's tolerance -- plus exp2 and fp32
+          rounding);
+  D_i     = dO_i . O_i uses the given 16-bit O: |dD_i| = e_D,i +
+          d 2^-24 |dO_i| . |O_i|, with e_D,i = |dO_i . (O_given - O)| for
+          the rounded oracle O, or tol_O sum_c |dO_ic| for a forward within
+          its tolerance;
   dS_ij   = P (dP - D), rounded to 16 bit once: |d dS| <= e_P |dS| +
           P |dD_i| + P d 2^-24 |dO_i| . |v_j| + u |dS| + t/2, with t the
           smallest spacing of the format (2^-24 for fp16, whose subnormals
@@ -29,7 +40,7 @@ import torch
 
 from oracle import attn_bwd_oracle, attn_fwd_oracle
 from exact_attention_19_amd.workloads import WORKLOADS, Workload, make_inputs
-from parity_common import _say
+from parity_common import TOL_LSE, TOL_O, _say
 
 pytestmark = pytest.mark.gpu
 
@@ -50,12 +61,15 @@ def _f64(t):
     return t.detach().to("cpu").to(torch.float64)
 
 
-def error_bounds(q, k, v, do, o_gpu, lse_gpu, scale, causal, dt):
+def error_bounds(q, k, v, do, o_in, lse_in, scale, causal, dt, stated=False):
     """Elementwise bounds (dq, dk, dv) as derived in the module docstring,
-    from fp64 quantities computed here with torch on the CPU."""
+    from fp64 quantities computed here with torch on the CPU.  o_in, lse_in:
+    the O and LSE the backward was given.  stated=False: they are the
+    oracle's, rounded, and their error is that rounding; stated=True: they
+    come from the GPU forward, and only its stated tolerances are assumed."""
     u = U[dt]
     acc = 2.0 ** -24
-    qd, kd, vd, dod, og = (_f64(t) for t in (q, k, v, do, o_gpu))
+    qd, kd, vd, dod, og = (_f64(t) for t in (q, k, v, do, o_in))
     B, Sq, Hq, d = qd.shape
     Sk, Hkv = kd.shape[1], kd.shape[2]
     g = Hq // Hkv
@@ -77,14 +91,21 @@ def error_bounds(q, k, v, do, o_gpu, lse_gpu, scale, causal, dt):
                           torch.full_like(z[..., 0], float("-inf")))
     o = torch.matmul(p, vh)
     dp = torch.matmul(doh, vh.transpose(-1, -2))
-    dD = (doh * (og.permute(0, 2, 1, 3) - o)).sum(-1).abs() \
-        + d * acc * (doh.abs() * o.abs()).sum(-1)
+    if stated:
+        e_d = TOL_O[dt] * doh.abs().sum(-1)
+    else:
+        e_d = (doh * (og.permute(0, 2, 1, 3) - o)).sum(-1).abs()
+    dD = e_d + d * acc * (doh.abs() * o.abs()).sum(-1)
     D = (p * dp).sum(-1)
     ds = p * (dp - D[..., None])
     fin = torch.isfinite(lse_ref)
-    lg = _f64(lse_gpu)
-    dl = (lg[fin] - lse_ref[fin]).abs().max().item() if fin.any() else 0.0
-    e_p = dl + 2.0 ** -20
+    if stated:
+        dl = TOL_LSE
+    else:
+        lg = _f64(lse_in)
+        dl = (lg[fin] - lse_ref[fin]).abs().max().item() if fin.any() else 0.0
+    # a relative error e^dl - 1 of P, about dl
+    e_p = math.expm1(dl) + 2.0 ** -20
     dds = e_p * ds.abs() + p * dD[..., None] \
         + p * d * acc * torch.matmul(doh.abs(), vh.abs().transpose(-1, -2)) + u * ds.abs()
     # rounding to 16 bit: relative u, or half the smallest spacing where the
@@ -102,23 +123,35 @@ def error_bounds(q, k, v, do, o_gpu, lse_gpu, scale, causal, dt):
     return bq.numpy(), bk.numpy(), bv.numpy()
 
 
-def _run(w: Workload, seed=0, dout_scale=1.0):
+def oracle_forward(q, k, v, w):
+    """The oracle's O rounded to the input type (RNE) and LSE rounded to fp32:
+    the forward outputs the backward consumes, free of any GPU error."""
+    o_ref, lse_ref = attn_fwd_oracle(q, k, v, w.scale, w.causal)
+    return torch.from_numpy(o_ref).to(q.dtype), torch.from_numpy(lse_ref).to(torch.float32)
+
+
+def _run(w: Workload, seed=0, dout_scale=1.0, fwd="oracle"):
+    """fwd="oracle": the backward gets the oracle's O and LSE; fwd="gpu": the
+    GPU forward's (the composed training step)."""
     from exact_attention_19_amd import attn_bwd, attn_fwd
     q, k, v = make_inputs(w, seed=seed)
     gen = torch.Generator().manual_seed(seed + 1000)
     do = (dout_scale * torch.randn(q.shape, generator=gen)).to(q.dtype)
     qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     _say(f"[gpu] attn_bwd {w.name} B={w.B} Sq={w.Sq} Sk={w.Sk} Hq={w.Hq} Hkv={w.Hkv} "
-         f"d={w.d} {w.dtype} causal={w.causal}")
-    o, lse = attn_fwd(qg, kg, vg, scale=w.scale, causal=w.causal)
+         f"d={w.d} {w.dtype} causal={w.causal} forward from the {fwd}")
+    if fwd == "oracle":
+        o, lse = (t.cuda() for t in oracle_forward(q, k, v, w))
+    else:
+        o, lse = attn_fwd(qg, kg, vg, scale=w.scale, causal=w.causal)
     dq, dk, dv = attn_bwd(qg, kg, vg, o, lse, dog, scale=w.scale, causal=w.causal)
     torch.cuda.synchronize()
     return q, k, v, do, o.cpu(), lse.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
 
 
-def _check(w, q, k, v, do, o, lse, dq, dk, dv):
+def _check(w, q, k, v, do, o, lse, dq, dk, dv, stated=False):
     rq, rk, rv = attn_bwd_oracle(q, k, v, do, w.scale, w.causal)
-    bq, bk, bv = error_bounds(q, k, v, do, o, lse, w.scale, w.causal, w.dtype)
+    bq, bk, bv = error_bounds(q, k, v, do, o, lse, w.scale, w.causal, w.dtype, stated=stated)
     u = U[w.dtype]
     worst = {}
     for name, got, ref, bound in (("dq", dq, rq, bq), ("dk", dk, rk, bk), ("dv", dv, rv, bv)):
@@ -165,6 +198,15 @@ def test_bwd_parity(w):
     _check(w, *_run(w))
 
 
+@pytest.mark.parametrize("w", [c for c in _cases() if c.name in (
+    "bwd_causal_off_bf16", "bwd_causal_empty_rows_f16", "bwd_gqa_nc_bf16", "bwd_scale1_f16")],
+    ids=lambda w: w.name)
+def test_bwd_after_gpu_forward(w):
+    """The training step as run: GPU forward, then GPU backward on its O and
+    LSE, bounded with the forward's stated tolerances only."""
+    _check(w, *_run(w, fwd="gpu"), stated=True)
+
+
 def test_bwd_1k_causal_workload():
     """The 2 x 1024 causal fp16 MHA workload, every gradient element."""
     w = WORKLOADS["mha_causal_f16_b2_h16_s1024_d128"]
@@ -187,15 +229,28 @@ def test_bwd_full_size_kv_group():
     gradients of kv group 0 (query heads 0-3, kv head 0) depend only on that
     group's tensors, so the oracle run on the group alone is their exact
     reference: every element of dq[:, :, 0:4], dk[:, :, 0] and dv[:, :, 0]."""
+    from exact_attention_19_amd import attn_bwd, attn_fwd
     w = WORKLOADS["gqa4_causal_bf16_b1_hq32_hkv8_s8192_d128"]
-    q, k, v, do, o, lse, dq, dk, dv = _run(w)
     g = w.Hq // w.Hkv
     sub = w.with_(name="bwd_gqa4_s8192_group0", Hq=g, Hkv=1)
-    _say(f"[cpu] oracle on kv group 0 of {w.name} (about half a minute)")
+    q, k, v = make_inputs(w, seed=0)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(1000)).to(q.dtype)
     hq = lambda t: t[:, :, :g].contiguous()
     hk = lambda t: t[:, :, :1].contiguous()
-    _check(sub, hq(q), hk(k), hk(v), hq(do), hq(o), lse[:, :g].contiguous(), hq(dq), hk(dk),
-           hk(dv))
+    # group 0's O and LSE from the oracle (on the group alone); the other
+    # groups' from the GPU forward (they do not enter group 0's gradients)
+    _say(f"[cpu] oracle forward of kv group 0 of {w.name}")
+    o0, lse0 = oracle_forward(hq(q), hk(k), hk(v), sub)
+    qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    _say(f"[gpu] attn_fwd + attn_bwd {w.name}")
+    o, lse = attn_fwd(qg, kg, vg, scale=w.scale, causal=w.causal)
+    o[:, :, :g] = o0.cuda()
+    lse[:, :g] = lse0.cuda()
+    dq, dk, dv = attn_bwd(qg, kg, vg, o, lse, dog, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    _say(f"[cpu] oracle backward of kv group 0 of {w.name} (about half a minute)")
+    _check(sub, hq(q), hk(k), hk(v), hq(do), o0, lse0, hq(dq), hk(dk), hk(dv))
 
 
 def test_bwd_deterministic():

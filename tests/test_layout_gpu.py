@@ -140,3 +140,94 @@ def test_merge_head_sizes():
     torch.cuda.synchronize()
     assert np.abs(o.double().cpu().numpy() - o_ref).max() <= 2e-3
     assert np.abs(lse.double().cpu().numpy() - lse_ref).max() <= 1e-4
+
+
+@pytest.mark.parametrize("kv_split", [1, 3])
+@pytest.mark.parametrize("Sq,Sk,causal,dt", [(200, 333, True, "bf16"), (129, 64, False, "f16"),
+                                             (77, 1000, True, "f16")])
+def test_kv_broadcast_along_seq(Sq, Sk, causal, dt, kv_split):
+    """k and v expanded along the key axis (row stride 0): every key is the
+    same row, read whole through the tile descriptors."""
+    from exact_attention_19_amd import attn_fwd_strided
+    w = _w(f"kv_bcast_{Sq}_{Sk}", 2, 8, 2, Sq, Sk, 128, dt, causal)
+    q, k, v = make_inputs(w, seed=Sq + 3 * Sk)
+    k1, v1 = k[:, :1], v[:, :1]
+    kx, vx = k1.cuda().expand(-1, Sk, -1, -1), v1.cuda().expand(-1, Sk, -1, -1)
+    assert kx.stride(1) == 0
+    _say(f"[gpu] attn_fwd_strided K/V broadcast along S {w.name} kv_split={kv_split}")
+    o, lse = attn_fwd_strided(q.cuda(), kx, vx, scale=w.scale, causal=causal, kv_split=kv_split)
+    torch.cuda.synchronize()
+    kd, vd = k1.expand(-1, Sk, -1, -1).contiguous(), v1.expand(-1, Sk, -1, -1).contiguous()
+    _check_full(w, q, kd, vd, o.cpu(), lse.cpu(), strict=False)
+
+
+def test_kv_overlapping_rows():
+    """k and v views whose rows overlap (row stride 64 elements < d = 128):
+    key j is elements [64 j, 64 j + 128) of one flat buffer."""
+    from exact_attention_19_amd import attn_fwd_strided
+    B, Sq, Sk, Hq, Hkv, d = 1, 150, 300, 4, 1, 128
+    w = _w("kv_overlap", B, Hq, Hkv, Sq, Sk, d, "bf16", True)
+    q, _, _ = make_inputs(w, seed=21)
+    g = torch.Generator().manual_seed(22)
+    flat_k = torch.randn(64 * (Sk + 1), generator=g).to(torch.bfloat16)
+    flat_v = torch.randn(64 * (Sk + 1), generator=g).to(torch.bfloat16)
+    fk, fv = flat_k.cuda(), flat_v.cuda()
+    kx = fk.as_strided((B, Sk, Hkv, d), (0, 64, 0, 1))
+    vx = fv.as_strided((B, Sk, Hkv, d), (0, 64, 0, 1))
+    _say("[gpu] attn_fwd_strided overlapping K/V rows")
+    o, lse = attn_fwd_strided(q.cuda(), kx, vx, scale=w.scale, causal=True, kv_split=1)
+    torch.cuda.synchronize()
+    kd = flat_k.as_strided((B, Sk, Hkv, d), (0, 64, 0, 1)).contiguous()
+    vd = flat_v.as_strided((B, Sk, Hkv, d), (0, 64, 0, 1)).contiguous()
+    _check_full(w, q, kd, vd, o.cpu(), lse.cpu(), strict=False)
+
+
+def test_binding_rejects_bad_buffers_before_any_launch():
+    """Caller-given outputs and workspaces of the wrong shape, dtype, layout
+    or device raise before the library is called."""
+    from exact_attention_19_amd import (attn_bwd, attn_decode_paged, attn_fwd, attn_fwd_split,
+                                        attn_fwd_strided, attn_merge)
+    w = _w("bad_bufs", 1, 4, 2, 64, 64, 64, "bf16", True)
+    q, k, v = (t.cuda() for t in make_inputs(w, seed=1))
+    lse_ok = torch.empty((1, 4, 64), dtype=torch.float32, device="cuda")
+    bad_outs = [torch.empty(1, 64, 4, 32, dtype=torch.bfloat16, device="cuda"),   # shape
+                torch.empty_like(q, dtype=torch.float16),                           # dtype
+                torch.empty(1, 64, 4, 128, dtype=torch.bfloat16, device="cuda")[..., :64],
+                torch.empty(q.shape, dtype=torch.bfloat16)]                         # host
+    for out in bad_outs:
+        for fn in (attn_fwd, attn_fwd_split):
+            with pytest.raises(ValueError):
+                fn(q, k, v, causal=True, out=out)
+    for lse in (torch.empty((1, 4, 64), dtype=torch.float32),                       # host
+                torch.empty((1, 4, 63), dtype=torch.float32, device="cuda")):
+        with pytest.raises(ValueError):
+            attn_fwd(q, k, v, causal=True, lse=lse)
+        with pytest.raises(ValueError):
+            attn_fwd_strided(q, k, v, causal=True, lse=lse)
+    with pytest.raises(ValueError):
+        attn_fwd_split(q, k, v, causal=True, kv_split=2,
+                       workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    o, lse = attn_fwd(q, k, v, causal=True)
+    do = torch.randn_like(q)
+    for name in ("dq", "dk", "dv"):
+        with pytest.raises(ValueError):
+            attn_bwd(q, k, v, o, lse, do, causal=True, **{name: torch.empty(k.shape if name != "dq"
+                                                                            else q.shape,
+                                                                            dtype=q.dtype)})
+    with pytest.raises(ValueError):
+        attn_bwd(q, k, v, o, lse.cpu(), do, causal=True)
+    with pytest.raises(ValueError):
+        attn_bwd(q, k, v, o, lse, do, causal=True, workspace=torch.empty(4096, dtype=torch.uint8))
+    parts = torch.zeros((2, 1, 64, 4, 64), dtype=torch.float32, device="cuda")
+    plse = torch.zeros((2, 1, 4, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        attn_merge(parts, plse, out=torch.empty((1, 64, 4, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        attn_merge(parts, plse, lse=torch.empty((1, 4, 64), dtype=torch.float32))
+    qd = q[:, :1].contiguous()
+    pool = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16, device="cuda")
+    table = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    lens = torch.full((1,), 64, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        attn_decode_paged(qd, pool, pool, table, lens, out=torch.empty(qd.shape, dtype=qd.dtype))
+    torch.cuda.synchronize()

@@ -104,11 +104,17 @@ def test_offsets_past_both_ends(Sq, Hq, Hkv):
     assert torch.all(o_none == 0) and torch.all(torch.isneginf(l_none))
 
 
-def _bwd_full(w, seed):
+def _bwd_full(w, seed, fwd="oracle"):
+    """Inputs, dO and the full problem's O and LSE on the GPU: the oracle's
+    (rounded to the 16-bit type and fp32) or, fwd="gpu", the GPU forward's."""
     from exact_attention_19_amd import attn_fwd
+    from test_bwd_gpu import oracle_forward
     q, k, v = make_inputs(w, seed=seed)
     do = torch.randn(q.shape, generator=torch.Generator().manual_seed(seed + 1)).to(q.dtype)
-    o, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=True)
+    if fwd == "oracle":
+        o, lse = (t.cuda() for t in oracle_forward(q, k, v, w))
+    else:
+        o, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=True)
     return q, k, v, do, o, lse
 
 
