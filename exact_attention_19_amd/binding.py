@@ -15,8 +15,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
+ATTN_ERR_SCRATCH = 4
 ATTN_DTYPE_F16, ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1, 2
 EXPORTED = ("attn_fwd", "attn_fwd_check", "attn_fwd_plan", "attn_fwd_split",
+            "attn_fwd_split_noalloc",
             "attn_fwd_split_workspace", "attn_fwd_split_plan", "attn_fwd_strided",
             "attn_fwd_strided_check", "attn_merge", "attn_merge_check", "attn_bwd",
             "attn_bwd_check", "attn_bwd_workspace", "attn_bwd_causal_offset",
@@ -59,6 +61,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.attn_fwd_split.restype = i
     lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.attn_fwd_split_noalloc.restype = i
+    lib.attn_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
     lib.attn_fwd_split_workspace.restype = i
     lib.attn_fwd_split_workspace.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.attn_fwd_split_plan.restype = i
@@ -287,6 +291,33 @@ def attn_fwd_split(q, k, v, scale: float | None = None, causal: bool = False,
         ws_ptr, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_split")
+    return out, lse
+
+
+def attn_fwd_split_noalloc(q, k, v, scale: float | None = None, causal: bool = False,
+                           kv_split: int = 0, out=None, lse=None, stream=None):
+    """attn_fwd_split with the key split's partial states in the library's
+    static per-GPU scratch (no workspace, nothing allocated by the library).
+    ``out`` and ``lse`` must be given (allocating them is the caller's
+    business).  Calls whose kernels overlap on one GPU race on the scratch;
+    calls on one stream are safe.  Raises AttnError (ATTN_ERR_SCRATCH) when
+    the split needs more than the scratch holds."""
+    import torch
+    B, Sq, Sk, Hq, Hkv, d, code = _check_qkv(q, k, v)
+    if out is None:
+        raise ValueError("attn_fwd_split_noalloc writes into a caller-given out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse, False)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().attn_fwd_split_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None,
+        B, Sq, Sk, Hq, Hkv, d, float(scale), int(bool(causal)), code, int(kv_split),
+        ctypes.c_void_p(stream.cuda_stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_split_noalloc")
     return out, lse
 
 

@@ -60,6 +60,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "attn.h"
@@ -1093,9 +1094,70 @@ attn_status run_forward(const void* q, const void* k, const void* v, void* o, fl
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+// ------------------------------------------------------------ static scratch
+//
+// attn_fwd_split_noalloc keeps the key split's partial states in this
+// library-owned device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  Host code
+// never uses the array's name as a device address: at the first call on a
+// device, with that device current, hipGetSymbolAddress gives that device's
+// address, which is kept per device and passed to the kernels.
+constexpr size_t kScratchBytes = ATTN_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device that runs `stream` (the current device
+// for the null stream), looked up once per device.
+attn_status scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return ATTN_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_LAUNCH;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || ptr == nullptr) return ATTN_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+attn_status attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int d,
+                                   float scale, int causal, int dtype, int kv_split,
+                                   void* stream) {
+  attn_status st = attn_fwd_check(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype);
+  if (st != ATTN_OK) return st;
+  if (kv_split < 0) return ATTN_ERR_INVALID_ARG;
+  size_t need = 0;
+  st = attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, causal, dtype, kv_split, &need);
+  if (st != ATTN_OK) return st;
+  if (need > kScratchBytes) return ATTN_ERR_SCRATCH;  // before any device call
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_stream((hipStream_t)stream, &ws);
+    if (st != ATTN_OK) return st;
+  }
+  return run_forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype,
+                     dense_strides(Sq, Sk, Hq, Hkv, d), kv_split, ws, need, (hipStream_t)stream,
+                     Sk - Sq);
+}
 
 attn_status attn_fwd_check(const void* q, const void* k, const void* v, void* o,
                            float* lse, int B, int Sq, int Sk, int Hq, int Hkv,
@@ -1369,6 +1431,8 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "unsupported head size or dtype";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_SCRATCH:
+      return "the key split needs more than the library's static scratch (16 MiB)";
     default: return "unknown status";
   }
 }

@@ -55,13 +55,15 @@ typedef enum {
                                index space too large */
   ATTN_ERR_UNSUPPORTED = 2, /* d, dtype or (paged decode) shape outside the
                                built set */
-  ATTN_ERR_LAUNCH = 3       /* HIP reported an error for the launch */
+  ATTN_ERR_LAUNCH = 3,      /* HIP reported an error for the launch */
+  ATTN_ERR_SCRATCH = 4      /* attn_fwd_split_noalloc: the key split would
+                               need more than ATTN_SCRATCH_BYTES */
 } attn_status;
 
 /* F32 is accepted only for the partial outputs passed to attn_merge. */
 typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1, ATTN_DTYPE_F32 = 2 } attn_dtype;
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /*
  * attn_fwd -- fused attention forward.
@@ -160,6 +162,39 @@ attn_status attn_fwd_split(const void* q, const void* k, const void* v, void* o,
                            size_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_split_noalloc -- attn_fwd_split without a caller workspace and
+ * without any allocation, for callers that cannot allocate device memory
+ * during the call: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * The key split's partial states go to a static device array of
+ * ATTN_SCRATCH_BYTES that the library holds on each GPU it runs on, until
+ * the process ends.  Its address on a device is looked up (not allocated)
+ * at the first call that runs on that device.  The call allocates nothing
+ * and calls no hipMalloc or hipFree.
+ *
+ *   q ... dtype, kv_split, stream  as for attn_fwd_split; the kernels run on
+ *          the device of `stream` (the current device for NULL)
+ *
+ * Every call on one GPU shares that GPU's array: two calls whose kernels
+ * overlap on one GPU (different streams with no ordering between them)
+ * race and give wrong results.  Calls on one stream are ordered and safe.
+ * Nothing in the array needs clearing: each call's merge reads only what
+ * the same call wrote.
+ *
+ * Returns ATTN_ERR_SCRATCH, before any device call, when the split would
+ * need more than ATTN_SCRATCH_BYTES (attn_fwd_split_workspace gives the
+ * need; kv_split = 1, or a coarser split, needs less or none); else as
+ * attn_fwd_split.
+ */
+#define ATTN_SCRATCH_BYTES ((size_t)16 << 20)
+attn_status attn_fwd_split_noalloc(const void* q, const void* k, const void* v,
+                                   void* o, float* lse, int B, int Sq, int Sk,
+                                   int Hq, int Hkv, int d, float scale,
+                                   int causal, int dtype, int kv_split,
+                                   void* stream);
+
+/*
  * attn_fwd_strided -- attn_fwd_split on tensors with arbitrary row strides:
  * any (batch, seq, head) layout with d contiguous, e.g. the (B, H, S, d)
  * layout of the personal-notes and cuTile pages, or q, k, v sliced out of
@@ -170,8 +205,13 @@ attn_status attn_fwd_split(const void* q, const void* k, const void* v, void* o,
  *            v: batch, seq, head;  o: batch, seq, head.
  *            Element (b, s, h, c) of q is at q + b*qs_b + s*qs_s + h*qs_h + c.
  *            Each stride must be >= 0 and a multiple of 8 (16-byte aligned
- *            rows), and 64 * (k and v seq stride) * 2 < 2^31.  The rows of o
- *            must not overlap each other or the inputs (not checked).
+ *            rows), and 64 * (k and v seq stride) * 2 < 2^31.  q, k and v
+ *            are only read: any strides (0 broadcasts one row).  The rows of
+ *            o must not overlap each other: a layout in which they might
+ *            (checked by taking the dimensions by increasing stride, each
+ *            reaching past all the smaller ones span) is rejected with
+ *            ATTN_ERR_INVALID_ARG.  o must not overlap the inputs (not
+ *            checked).
  *   lse      as for attn_fwd: contiguous fp32 (B, Hq, Sq) or NULL
  *   kv_split, workspace, workspace_bytes  as for attn_fwd_split (the
  *            workspace size does not depend on the strides)

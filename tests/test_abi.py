@@ -611,3 +611,23 @@ def test_binding_checks_reject_host_buffers():
         binding._check_workspace(torch.empty(16, dtype=torch.uint8), dev)
     binding._check_lse(None, 1, 2, 3, dev)
     binding._check_workspace(None, dev)
+
+
+def test_noalloc_refuses_a_split_beyond_the_scratch_before_any_device_call():
+    lib = _lib()
+    m = re.search(r"#define\s+ATTN_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)",
+                  open(HEADER).read())
+    cap = int(m.group(1)) << int(m.group(2))
+    shape = (4, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16)
+    assert binding.attn_fwd_split_workspace(*shape, kv_split=8) > cap
+    rc = lib.attn_fwd_split_noalloc(A, A, A, A, None, *shape[:6], ctypes.c_float(0.1), 1,
+                                    ATTN_DTYPE_BF16, 8, None)
+    assert rc == binding.ATTN_ERR_SCRATCH
+    assert "scratch" in binding.attn_status_str(rc)
+    # the usual argument checks come first
+    assert lib.attn_fwd_split_noalloc(A, A, A, A, None, 4, 8192, 8192, 32, 7, 128,
+                                      ctypes.c_float(0.1), 1, ATTN_DTYPE_BF16, 8,
+                                      None) == ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_split_noalloc(A, A, A, A, None, 1, 64, 64, 4, 4, 64,
+                                      ctypes.c_float(0.1), 1, ATTN_DTYPE_BF16, -1,
+                                      None) == ATTN_ERR_INVALID_ARG
