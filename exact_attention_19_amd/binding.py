@@ -12,7 +12,9 @@ import math
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libattn.so")
+# ATTN_LIBRARY names another build of the same sources (the host-side
+# sanitizer build used by the CPU checks)
+LIB_PATH = os.environ.get("ATTN_LIBRARY") or os.path.join(PKG, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
 ATTN_ERR_SCRATCH = 4

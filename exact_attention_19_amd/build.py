@@ -26,25 +26,68 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libattn.so")
 
 
-def build_command(out: str) -> list[str]:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, *SOURCES, "-o", out]
+# Host-side sanitizer build (CPU checks only): AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host half of every source (argument
+# validation, launch plans, workspace sizes); the gfx950 device code is built
+# as usual.  The result goes to SANITIZE_LIB, never over LIB.
+SANITIZE_DIR = os.path.join(ROOT, "_build", "sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, "libattn.so")
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=undefined",
+                       "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source into libattn.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = build_command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed to build libattn.so")
-    os.replace(tmp, LIB)
-    return LIB
+def build_command(out: str, src: str | None = None, sanitize: bool = False) -> list[str]:
+    """hipcc for one source (-c, to an object) or, src None, all of them into a
+    shared library."""
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE]
+    if sanitize:
+        cmd += HOST_SANITIZE_FLAGS
+    if src is not None:
+        return cmd + ["-c", src, "-o", out]
+    return cmd + ["-shared", *SOURCES, "-o", out]
+
+
+def build_library(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every HIP source into libattn.so (always recompiles).  The
+    sources are compiled in parallel, then linked."""
+    lib = SANITIZE_LIB if sanitize else LIB
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
+    tmp = lib + ".tmp"
+    objs = [tmp + "." + os.path.basename(s) + ".o" for s in SOURCES]
+    procs = []
+    for s, o in zip(SOURCES, objs):
+        cmd = build_command(o, s, sanitize)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                      text=True))
+    failed = False
+    for p in procs:
+        out, err = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(out + err)
+            failed = True
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed to compile libattn.so")
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        if sanitize:
+            link[1:1] = HOST_SANITIZE_FLAGS
+        if verbose:
+            print(" ".join(link), flush=True)
+        r = subprocess.run(link, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed to link libattn.so")
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build_library(verbose=True))
+    print(build_library(verbose=True, sanitize="--sanitize" in sys.argv))

@@ -14,7 +14,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
-_LIB = os.path.join(_HERE, "libattn_oracle.so")
+# ATTN_ORACLE_LIBRARY names another build of the same source (the sanitizer
+# build below) for the test run that checks it.
+_LIB = os.environ.get("ATTN_ORACLE_LIBRARY") or os.path.join(_HERE, "libattn_oracle.so")
+_SANITIZE_LIB = os.path.join(os.path.dirname(_HERE), "_build", "sanitize", "libattn_oracle.so")
 _lib = None
 
 
@@ -22,16 +25,26 @@ def oracle_lib_path() -> str:
     return _LIB
 
 
-def build_oracle(force: bool = True) -> str:
+def build_oracle(force: bool = True, sanitize: bool = False) -> str:
     """Compile attn_oracle.c into libattn_oracle.so with gcc (-O2, no fast-math:
-    the oracle keeps IEEE fp64 semantics)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(
-            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
-             "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+    the oracle keeps IEEE fp64 semantics).  sanitize=True: a separate build
+    with AddressSanitizer and UndefinedBehaviorSanitizer, compiled by the
+    ROCm clang so that it shares one sanitizer runtime with the HIP library's
+    host-side sanitizer build in the process that tests both."""
+    lib = _SANITIZE_LIB if sanitize else _LIB
+    if force or not os.path.exists(lib):
+        os.makedirs(os.path.dirname(lib), exist_ok=True)
+        tmp = lib + ".tmp"
+        if sanitize:
+            cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c99", "-fPIC", "-shared",
+                   "-pthread", "-ffp-contract=off", "-fsanitize=address,undefined",
+                   "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+        else:
+            cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+                   "-fno-fast-math", "-ffp-contract=off"]
+        subprocess.check_call(cmd + [_SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
