@@ -29,6 +29,7 @@ struct DecodeArgs {
   int64_t v_sb, v_ss, v_sh;
   int64_t o_sb, o_ss, o_sh;
   int B, Sq, Sk, Hq, Hkv;
+  int d;             // head size; the kernel is built for D >= d (padded)
   int off;           // causal: query i sees key j <= i + off (dense keys;
                      // a paged sequence of length L uses L - Sq)
   int piece_tiles;   // 32-key tiles per piece
@@ -72,6 +73,26 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BC = 64;              // keys per K/V tile
 constexpr float LN2 = 0.693147180559945309417f;
+
+// ------------------------------------------------------------ head sizes
+// Any head size d that is a multiple of 8 from 8 to 256 runs on the kernels
+// built for the next size up in this list (the CuTe DSL example pads its
+// head size up to a multiple of 32 the same way): the tile layout, the MFMA
+// steps and the LDS buffers take the padded size D, the columns past d are
+// loaded as zeros (Q, K, V) and never stored (O).
+inline bool head_size_ok(int d) { return d >= 8 && d <= 256 && d % 8 == 0; }
+inline int padded_head(int d) {
+  return d <= 32 ? 32 : d <= 64 ? 64 : d <= 96 ? 96 : d <= 128 ? 128 : d <= 192 ? 192 : 256;
+}
+// The 32-column blocks below every head size that runs on the kernel built
+// for D (d > the next smaller built size): loads of blocks from this one on
+// must check their columns against d.
+constexpr int full_col_blocks(int D) {
+  return D == 32 ? 0 : D == 64 ? 1 : D == 96 ? 2 : D == 128 ? 3 : D == 192 ? 4 : 6;
+}
+// A buffer-load offset past any record count the host allows (< 2^31): the
+// load returns zeros, which is how the padded columns of a tile are filled.
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
 
 // ---------------------------------------------------------------- dtypes
 template <int DT>
@@ -283,7 +304,7 @@ Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
   pl.xcd_cols = (pl.ncols % 8 == 0) ? pl.ncols / 8 : 0;
   const long long grid = qt * pl.ncols;
   pl.grid = (grid > 0x7fffffffll || pl.qtiles < 0) ? -1 : (int)grid;
-  pl.lds_bytes = 4 * BC * d * 2;
+  pl.lds_bytes = 4 * BC * padded_head(d) * 2;
   return pl;
 }
 
@@ -306,8 +327,8 @@ constexpr int DEC_MAX_ROWS = 128;
 constexpr int DEC_MAX_SQ_GROUPED = 8;
 
 inline bool decode_eligible(int Sq, int Hq, int Hkv, int d) {
+  (void)d;  // every head size (padded up to a built one)
   const long long rows = (long long)(Hq / Hkv) * Sq;
-  if (d != 32 && d != 64 && d != 96 && d != 128) return false;
   return rows <= 32 || (rows <= DEC_MAX_ROWS && Sq <= DEC_MAX_SQ_GROUPED);
 }
 
@@ -361,7 +382,7 @@ inline DecodePlan make_decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d
   dp.grid = ucols * dp.pieces;
   if (dp.pieces > 1) {
     const size_t rows = (size_t)B * Sq * Hq;
-    dp.lse_offset = ((size_t)dp.pieces * rows * d * 4 + 255) & ~(size_t)255;
+    dp.lse_offset = ((size_t)dp.pieces * rows * padded_head(d) * 4 + 255) & ~(size_t)255;
     dp.ws_bytes = dp.lse_offset + (size_t)dp.pieces * rows * 4;
   }
   if (dp.grid > 0x7fffffffll) dp.grid = -1;

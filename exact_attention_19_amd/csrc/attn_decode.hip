@@ -36,7 +36,8 @@ constexpr int DBC = 32;                    // keys per tile
 constexpr float DEC_RESCALE_TAU = 8.0f;    // lazy max update, as the prefill kernel
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(DEC_WAVES * 64, D > 128 ? 1 : 8 / DEC_WAVES) void attn_decode_kernel(
+    DecodeArgs p) {
   using T = Ty<DT>;
   constexpr int CB = D / 32;
   constexpr int KK = D / 16;
@@ -88,8 +89,8 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
     const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)qi * p.q_ss + (int64_t)hq * p.q_sh;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (rok) x = *(const u32x4*)(qrow + kk * 16 + hh * 8);
+      u32x4 x = {0u, 0u, 0u, 0u};  // columns past d stay zero
+      if (rok && kk * 16 + hh * 8 < p.d) x = *(const u32x4*)(qrow + kk * 16 + hh * 8);
       qf[kk] = __builtin_bit_cast(i16x8, x);
     }
   }
@@ -150,13 +151,19 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
     const int64_t row = (kidx >= 16 ? tr.r1 : tr.r0) + (kidx & 15);
     const uint16_t* krow = (const uint16_t*)(kbase + row * (int64_t)rbk);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      kf[kk] = __builtin_bit_cast(i16x8, *(const u32x4*)(krow + kk * 16 + hh * 8));
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};  // columns past d: zeros, not read
+      if (kk * 16 + hh * 8 < p.d) x = *(const u32x4*)(krow + kk * 16 + hh * 8);
+      kf[kk] = __builtin_bit_cast(i16x8, x);
+    }
   };
   // V tile n -> this wave's LDS stage: column-blocked, 32 rows x 64 bytes per
   // block, chunk c of row r at slot c ^ ((r >> 2) & 3); round u covers block
   // u >> 1, rows 16 (u & 1) + lane / 4
   // (rows past Sk re-read the last key's row, whose values are finite)
+  // (chunks past d, in the column blocks from full_col_blocks(D) on, load
+  // zeros: an offset past the descriptor's end)
+  constexpr int FULL = full_col_blocks(D);
   auto load_v = [&](int n, const TileRows& tr, LDS_PTR(char) buf) {
     const int row = lane >> 2;
     const int chunk = (lane & 3) ^ ((row >> 2) & 3);
@@ -172,11 +179,13 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
       // the descriptor spans the 16 rows' bytes, 15 strides + one row of D
       // elements (a stride below D, or 0, still reads whole rows)
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vbase + base * (int64_t)rbv), 0, (int)(15 * rbv + D * 2), 0x00020000);
+          (void*)(vbase + base * (int64_t)rbv), 0, (int)(15 * rbv + p.d * 2), 0x00020000);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (LDS_PTR(void))(buf + cb * VBLK + h2 * 1024), 16, off, 64 * cb, 0, 0);
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint32_t o = cb < FULL || 32 * cb + chunk * 8 < p.d ? off : OOB_OFFSET;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_PTR(void))(buf + cb * VBLK + h2 * 1024),
+                                                 16, o, 64 * cb, 0, 0);
+      }
     }
   };
   // transposed V fragment (A operand of O^T += V^T P^T): rows 16t + 8hh ..
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 8 / DEC_WAVES) void attn_decode_ker
 #pragma unroll
       for (int j = 0; j < (D + 63) / 64; ++j) {
         const int c = 4 * l16 + 64 * j;
-        if (D % 64 != 0 && c >= D) continue;
+        if (c >= p.d) continue;  // columns past d (and past D) are not written
         f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -424,17 +433,21 @@ __attribute__((visibility("hidden"))) hipError_t attn_detail::launch_decode(
     int dtype, int d, int causal, const DecodeArgs& a, hipStream_t st) {
   const bool c = causal != 0;
   if (dtype == ATTN_DTYPE_BF16) {
-    switch (d) {
+    switch (padded_head(d)) {
       case 32: return launch_decode_d<ATTN_DTYPE_BF16, 32>(c, a, st);
       case 64: return launch_decode_d<ATTN_DTYPE_BF16, 64>(c, a, st);
       case 96: return launch_decode_d<ATTN_DTYPE_BF16, 96>(c, a, st);
-      default: return launch_decode_d<ATTN_DTYPE_BF16, 128>(c, a, st);
+      case 128: return launch_decode_d<ATTN_DTYPE_BF16, 128>(c, a, st);
+      case 192: return launch_decode_d<ATTN_DTYPE_BF16, 192>(c, a, st);
+      default: return launch_decode_d<ATTN_DTYPE_BF16, 256>(c, a, st);
     }
   }
-  switch (d) {
+  switch (padded_head(d)) {
     case 32: return launch_decode_d<ATTN_DTYPE_F16, 32>(c, a, st);
     case 64: return launch_decode_d<ATTN_DTYPE_F16, 64>(c, a, st);
     case 96: return launch_decode_d<ATTN_DTYPE_F16, 96>(c, a, st);
-    default: return launch_decode_d<ATTN_DTYPE_F16, 128>(c, a, st);
+    case 128: return launch_decode_d<ATTN_DTYPE_F16, 128>(c, a, st);
+    case 192: return launch_decode_d<ATTN_DTYPE_F16, 192>(c, a, st);
+    default: return launch_decode_d<ATTN_DTYPE_F16, 256>(c, a, st);
   }
 }

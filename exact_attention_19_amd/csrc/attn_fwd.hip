@@ -84,6 +84,8 @@ struct Params {
   int64_t v_sb, v_ss, v_sh;
   int64_t o_sb, o_ss, o_sh;
   int B, Sq, Sk, Hq, Hkv;
+  int d;         // head size: the kernel is built for D >= d, columns past d
+                 // read as zeros and are not written
   int group;     // Hq / Hkv
   int gh;        // query heads per workgroup (divides group and the wave count)
   int hsub;      // group / gh
@@ -272,6 +274,10 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
   // stride) below 2^31.
   const uint32_t ld_off_k = (uint32_t)ld_row * rbk + (uint32_t)ld_col * 2;
   const uint32_t ld_off_v = (uint32_t)ld_row * rbv + (uint32_t)ld_col * 2;
+  // The column rounds from full_col_blocks(D) on may hold columns that a
+  // padded head size lacks: those lanes load from past the descriptor's end,
+  // which fills zeros.
+  constexpr int FULL = full_col_blocks(D);
   auto issue_rows = [&](const char* slice, uint32_t row_bytes, uint32_t ld_off, int n,
                         LDS_PTR(char) buf) {
     const char* tile = slice + (int64_t)n * BC * row_bytes;
@@ -280,12 +286,14 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
       off = (uint32_t)(min(n * BC + ld_row, p.Sk - 1) - n * BC) * row_bytes + (uint32_t)ld_col * 2;
     // raw buffer, 32-bit data format (word 3 of the descriptor)
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)((BC - 1) * row_bytes + D * 2),
+        __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)((BC - 1) * row_bytes + p.d * 2),
                                           0x00020000);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u)
+    for (int u = 0; u < CPT; ++u) {
+      const uint32_t o = u < FULL || 32 * u + ld_col < p.d ? off : OOB_OFFSET;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_PTR(void))(buf + (u * NW + wave) * 1024),
-                                               16, off, 64 * u, 0, 0);
+                                               16, o, 64 * u, 0, 0);
+    }
   };
 
   // ---- Q fragments, kept in registers
@@ -297,8 +305,8 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
         p.q + (int64_t)b * p.q_sb + (int64_t)(ok ? qi : 0) * p.q_ss + (int64_t)hq * p.q_sh;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (ok) x = *(const u32x4*)(qrow + kk * 16 + hh * 8);
+      u32x4 x = {0u, 0u, 0u, 0u};  // columns past d stay zero
+      if (ok && kk * 16 + hh * 8 < p.d) x = *(const u32x4*)(qrow + kk * 16 + hh * 8);
       qf[kk] = __builtin_bit_cast(i16x8, x);
     }
   }
@@ -559,7 +567,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
           f32x4 x;
 #pragma unroll
           for (int r = 0; r < 4; ++r) x[r] = acc_o[cb][4 * g + r] * inv;
-          *(f32x4*)(prow + cb * 32 + 8 * g + 4 * hh) = x;
+          if (cb * 32 + 8 * g + 4 * hh < p.d) *(f32x4*)(prow + cb * 32 + 8 * g + 4 * hh) = x;
         }
       if (hh == 0) {
         const float lse = has ? (m_run + __builtin_amdgcn_logf(l_lse)) * LN2 : -INFINITY;
@@ -580,7 +588,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
           const i16x8 y = T::cvt(x);
           const u32x2 w = {(unsigned)(uint16_t)y[0] | ((unsigned)(uint16_t)y[1] << 16),
                            (unsigned)(uint16_t)y[2] | ((unsigned)(uint16_t)y[3] << 16)};
-          *(u32x2*)(orow + cb * 32 + 8 * g + 4 * hh) = w;
+          if (cb * 32 + 8 * g + 4 * hh < p.d) *(u32x2*)(orow + cb * 32 + 8 * g + 4 * hh) = w;
         }
       if (p.lse != nullptr && hh == 0) {
         const float lse = has ? (m_run + __builtin_amdgcn_logf(l_lse)) * LN2 : -INFINITY;
@@ -605,12 +613,15 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
 // threads per row), so the reads of a part row and the write of O are
 // contiguous across the row's threads.
 struct MergeParams {
-  const void* parts;      // part p, row r: parts + (p * rows + r) * D elements
+  const void* parts;      // part p, row r: parts + (p * rows + r) * pstride elements
   const float* parts_lse; // part p, (b, h, i): + p * rows + (b * Hq + h) * sq_rows + i - q_first
   uint16_t* o;            // (B, Sq, Hq, D) through the strides below
   int64_t o_sb, o_ss, o_sh;
   float* lse;             // (B, Hq, Sq) or null
   int B, Sq, Hq;
+  int d;        // head size (columns written); the kernel is built for D >= d
+  int pstride;  // elements per part row: D for a key split's workspace, d for
+                // attn_merge's dense parts
   int n_parts;  // parts per row; 0 = the piece count of a key split (below)
   int q_first;  // first merged query row; rows are (b, q_first.. Sq-1, h)
   int sq_rows;  // Sq - q_first
@@ -653,6 +664,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
   const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   if (r >= p.rows) return;
   const int c = (threadIdx.x % TPR) * 4;
+  const bool col_ok = c < p.d;  // columns past a padded head size: no loads, no store
   const int hq = (int)(r % p.Hq);
   const int64_t t = r / p.Hq;
   const int ii = (int)(t % p.sq_rows);
@@ -685,7 +697,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
         x[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
         if (q < n) {
           l[e] = p.parts_lse[(int64_t)q * p.rows + lrow];
-          x[e] = load_part4<PDT>(p.parts, ((int64_t)q * p.rows + r) * D + c);
+          if (col_ok) x[e] = load_part4<PDT>(p.parts, ((int64_t)q * p.rows + r) * p.pstride + c);
         }
       }
       float m = M;
@@ -725,7 +737,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
   const i16x8 h = Ty<ODT>::cvt(y);
   const u32x2 w2 = {(unsigned)(uint16_t)h[0] | ((unsigned)(uint16_t)h[1] << 16),
                     (unsigned)(uint16_t)h[2] | ((unsigned)(uint16_t)h[3] << 16)};
-  *(u32x2*)(p.o + (int64_t)b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)hq * p.o_sh + c) = w2;
+  if (col_ok)
+    *(u32x2*)(p.o + (int64_t)b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)hq * p.o_sh + c) = w2;
   if (p.lse != nullptr && c == 0)
     p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] =
         W > 0.f ? M + __builtin_amdgcn_logf(W) * LN2 : -INFINITY;
@@ -744,7 +757,7 @@ attn_status validate(const void* q, const void* k, const void* v, void* o,
     return ATTN_ERR_INVALID_ARG;
   if (((uintptr_t)lse) & 3u) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!head_size_ok(d)) return ATTN_ERR_UNSUPPORTED;
   // index-space limits: positions and per-tensor row counts stay in int32
   // arithmetic inside the kernel; element offsets are 64-bit.
   if ((int64_t)Sq + Sk >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
@@ -870,10 +883,11 @@ SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int cau
   sp.q_first = qt0 * pl.rows_wg;
   sp.grid = (long long)sp.npieces * pl.qtiles * pl.ncols;
   sp.merge_rows = (long long)B * (Sq - sp.q_first) * Hq;
-  const int rpb = 256 / (d / 4);
+  const int D = padded_head(d);
+  const int rpb = 256 / (D / 4);
   sp.merge_grid = (sp.merge_rows + rpb - 1) / rpb;
   const size_t parts = (size_t)sp.npieces * (size_t)sp.merge_rows;
-  sp.lse_offset = ((parts * (size_t)d * 4) + 255) & ~(size_t)255;
+  sp.lse_offset = ((parts * (size_t)D * 4) + 255) & ~(size_t)255;
   sp.ws_bytes = sp.lse_offset + parts * 4;
   if (sp.grid > 0x7fffffffll || sp.merge_grid > 0x7fffffffll) sp.grid = -1;
   return sp;
@@ -882,11 +896,12 @@ SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int cau
 template <int PDT, int ODT>
 hipError_t launch_merge(int d, long long grid, const MergeParams& mp, hipStream_t st) {
   const dim3 g((unsigned)grid), b(256);
-  switch (d) {
+  switch (padded_head(d)) {
     case 32: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 32>), g, b, 0, st, mp); break;
     case 64: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 64>), g, b, 0, st, mp); break;
     case 96: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 96>), g, b, 0, st, mp); break;
     case 128: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 128>), g, b, 0, st, mp); break;
+    case 192: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 192>), g, b, 0, st, mp); break;
     default: hipLaunchKernelGGL((attn_merge_kernel<PDT, ODT, 256>), g, b, 0, st, mp); break;
   }
   return hipGetLastError();
@@ -921,17 +936,18 @@ hipError_t launch_c(bool causal, const Plan& pl, long long nwg, const Params& p,
 template <int DT>
 hipError_t launch_d(int d, bool causal, const Plan& pl, long long nwg, const Params& p,
                     hipStream_t st) {
-  switch (d) {
+  switch (padded_head(d)) {
     case 32: return launch_c<DT, 32>(causal, pl, nwg, p, st);
     case 64: return launch_c<DT, 64>(causal, pl, nwg, p, st);
     case 96: return launch_c<DT, 96>(causal, pl, nwg, p, st);
     case 128: return launch_c<DT, 128>(causal, pl, nwg, p, st);
+    case 192: return launch_c<DT, 192>(causal, pl, nwg, p, st);
     default: return launch_c<DT, 256>(causal, pl, nwg, p, st);
   }
 }
 
 Params fill_params(const Plan& pl, const void* q, const void* k, const void* v, void* o,
-                   float* lse, int B, int Sq, int Sk, int Hq, int Hkv, float scale,
+                   float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int d, float scale,
                    const Strides& st, int off) {
   Params p{};
   p.q_sb = st.s[0], p.q_ss = st.s[1], p.q_sh = st.s[2];
@@ -948,6 +964,7 @@ Params fill_params(const Plan& pl, const void* q, const void* k, const void* v, 
   p.Sk = Sk;
   p.Hq = Hq;
   p.Hkv = Hkv;
+  p.d = d;
   p.group = Hq / Hkv;
   p.gh = pl.gh;
   p.hsub = p.group / pl.gh;
@@ -1010,6 +1027,7 @@ attn_status run_decode(const void* q, const void* k, const void* v, void* o, flo
   a.Sk = Sk;
   a.Hq = Hq;
   a.Hkv = Hkv;
+  a.d = d;
   a.off = off;
   a.piece_tiles = dp.piece_tiles;
   a.rgroups = dp.rgroups;
@@ -1039,11 +1057,13 @@ attn_status run_decode(const void* q, const void* k, const void* v, void* o, flo
   mp.B = B;
   mp.Sq = Sq;
   mp.Hq = Hq;
+  mp.d = d;
+  mp.pstride = padded_head(d);
   mp.n_parts = dp.pieces;
   mp.q_first = 0;
   mp.sq_rows = Sq;
   mp.rows = (long long)B * Sq * Hq;
-  const int rpb = 256 / (d / 4);
+  const int rpb = 256 / (padded_head(d) / 4);
   e = launch_merge_any(ATTN_DTYPE_F32, dtype, d, (mp.rows + rpb - 1) / rpb, mp, hs);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -1060,7 +1080,7 @@ attn_status run_forward(const void* q, const void* k, const void* v, void* o, fl
   if (sp.chunk > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
                        workspace_bytes < sp.ws_bytes))
     return ATTN_ERR_INVALID_ARG;
-  Params p = fill_params(sp.base, q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, scale, st, off);
+  Params p = fill_params(sp.base, q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, st, off);
   if (sp.chunk == 0) {
     hipError_t e = launch_attn(dtype, d, causal, sp.base, sp.grid, p, hs);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -1081,6 +1101,8 @@ attn_status run_forward(const void* q, const void* k, const void* v, void* o, fl
   mp.B = B;
   mp.Sq = Sq;
   mp.Hq = Hq;
+  mp.d = d;
+  mp.pstride = padded_head(d);
   mp.n_parts = 0;
   mp.q_first = sp.q_first;
   mp.sq_rows = Sq - sp.q_first;
@@ -1187,7 +1209,7 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
     const DecodePlan dp = make_decode_plan(B, Sq, Sk, Hq, Hkv, d, 1);
     if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
     const int vals_dec[10] = {(int)dp.grid, DEC_WAVES * 64, Sq, 32, g, 32,
-                              DEC_WAVES * 2 * 32 * d * 2, 0, 0, 1};
+                              DEC_WAVES * 2 * 32 * padded_head(d) * 2, 0, 0, 1};
     for (int i = 0; i < 10; ++i) vals[i] = vals_dec[i];
   }
   for (int i = 0; i < n && i < 10; ++i) out[i] = vals[i];
@@ -1213,7 +1235,7 @@ attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, i
     const DecodePlan dp = make_decode_plan(B, Sq, Sk, Hq, Hkv, d, kv_split);
     if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
     const long long mrows = (long long)B * Sq * Hq;
-    const int rpb = 256 / (d / 4);
+    const int rpb = 256 / (padded_head(d) / 4);
     const int vals[5] = {(int)dp.grid, dp.pieces, dp.pieces > 1 ? dp.piece_tiles * 32 : 0,
                          dp.pieces > 1 ? 0 : Sq,
                          dp.pieces > 1 ? (int)((mrows + rpb - 1) / rpb) : 0};
@@ -1330,7 +1352,7 @@ attn_status attn_merge_check(const void* o_parts, const float* lse_parts, int n_
       parts_dtype != ATTN_DTYPE_BF16)
     return ATTN_ERR_UNSUPPORTED;
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!head_size_ok(d)) return ATTN_ERR_UNSUPPORTED;
   const uintptr_t need = parts_dtype == ATTN_DTYPE_F32 ? 15u : 7u;
   if (((uintptr_t)o_parts & need) || ((uintptr_t)o & 7u) || ((uintptr_t)lse_parts & 3u) ||
       ((uintptr_t)lse & 3u))
@@ -1355,11 +1377,13 @@ attn_status attn_merge(const void* o_parts, const float* lse_parts, int n_parts,
   mp.B = B;
   mp.Sq = Sq;
   mp.Hq = Hq;
+  mp.d = d;
+  mp.pstride = d;
   mp.n_parts = n_parts;
   mp.q_first = 0;
   mp.sq_rows = Sq;
   mp.rows = (long long)B * Sq * Hq;
-  const int rpb = 256 / (d / 4);
+  const int rpb = 256 / (padded_head(d) / 4);
   const long long grid = (mp.rows + rpb - 1) / rpb;
   hipError_t e = launch_merge_any(parts_dtype, dtype, d, grid, mp, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -1383,7 +1407,7 @@ attn_status attn_decode_paged_check(const void* q, const void* k_cache, const vo
   if (((uintptr_t)block_table | (uintptr_t)seqlens | (uintptr_t)lse) & 3u)
     return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (!decode_eligible(Sq, Hq, Hkv, d)) return ATTN_ERR_UNSUPPORTED;
+  if (!head_size_ok(d) || !decode_eligible(Sq, Hq, Hkv, d)) return ATTN_ERR_UNSUPPORTED;
   // index space: query rows (merge), block-table entries, pool elements
   if ((long long)B * Sq * Hq >= (1ll << 31) || (long long)B * max_blocks >= (1ll << 31) ||
       (long long)num_blocks * block_size >= (1ll << 31) ||
@@ -1397,7 +1421,7 @@ attn_status attn_decode_paged_workspace(int B, int Sq, int Hq, int Hkv, int d, i
   if (bytes == nullptr || kv_split < 0 || B < 1 || Sq < 1 || Hkv < 1 || Hq < 1 ||
       Hq % Hkv != 0 || max_seqlen < 1)
     return ATTN_ERR_INVALID_ARG;
-  if (!decode_eligible(Sq, Hq, Hkv, d)) return ATTN_ERR_UNSUPPORTED;
+  if (!head_size_ok(d) || !decode_eligible(Sq, Hq, Hkv, d)) return ATTN_ERR_UNSUPPORTED;
   const DecodePlan dp = make_decode_plan(B, Sq, max_seqlen, Hq, Hkv, d, kv_split);
   if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   *bytes = dp.ws_bytes;

@@ -73,7 +73,11 @@ typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1, ATTN_DTYPE_F32 = 2 } att
  *   o      device pointer, (B, Sq, Hq, d), 16-byte aligned; written
  *   lse    device pointer to B*Hq*Sq floats, 4-byte aligned, or NULL to skip
  *   B, Sq, Sk, Hq, Hkv, d   sizes, all >= 1; Hq must be a multiple of Hkv;
- *          d must be 32, 64, 96, 128 or 256
+ *          d must be a multiple of 8 from 8 to 256; sizes other than 32,
+ *          64, 96, 128, 192 and 256 run on the kernel of the next of these
+ *          (the CuTe DSL Ampere FlashAttention-2 example's head-size
+ *          padding, "__init__" and "can_implement"): the columns past d are
+ *          loaded as zeros and never written
  *   scale  multiplier of the scores, finite and > 0 (1/sqrt(d) is usual)
  *   causal 0 = no mask, 1 = bottom-right causal mask
  *   dtype  an attn_dtype value
@@ -110,8 +114,7 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
  *       overlapping the matrix products of the previous and next tiles) is
  *       used
  *   [9] 1 if the decode kernel is used: when the query rows of a kv head
- *       (Hq / Hkv * Sq) number at most 32 (or 128 with Sq <= 8) and d is
- *       32, 64, 96 or 128, each group
+ *       (Hq / Hkv * Sq) number at most 32 (or 128 with Sq <= 8), each group
  *       of up to 32 of them shares one wave and the 4 waves of a workgroup
  *       split the keys (then [0] counts a workgroup per (batch, kv head,
  *       32-row group), [2] is Sq and [4] the GQA group size)
@@ -312,7 +315,7 @@ attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
  *               natural-log LSE of each part, as attn_fwd returns it; 4-byte
  *               aligned
  *   n_parts     >= 1
- *   B, Sq, Hq, d  sizes (d = 32, 64, 96, 128 or 256)
+ *   B, Sq, Hq, d  sizes (d a multiple of 8 from 8 to 256)
  *   o           device pointer, (B, Sq, Hq, d) of dtype (F16 or BF16),
  *               8-byte aligned; written (must not overlap the inputs)
  *   lse         B * Hq * Sq floats, or NULL to skip
@@ -437,8 +440,7 @@ attn_status attn_bwd_workspace(int B, int Sq, int Hq, size_t* bytes);
  *   max_seqlen   the longest length to cover, 1 .. max_blocks * block_size;
  *                it sizes the key split (no device read of seqlens is made)
  *   B ... dtype  as for attn_fwd, restricted to the decode kernel's shapes:
- *                d = 32, 64, 96 or 128 and (Hq / Hkv) * Sq <= 32 (or
- *                <= 128 with Sq <= 8), else
+ *                (Hq / Hkv) * Sq <= 32 (or <= 128 with Sq <= 8), else
  *                ATTN_ERR_UNSUPPORTED
  *   kv_split, workspace, workspace_bytes  as for attn_fwd_split, with the
  *                decode rule for kv_split = 0; the workspace size is

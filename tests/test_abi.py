@@ -94,11 +94,26 @@ def test_invalid_arguments(over):
     assert _check(**over) == ATTN_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("over", [dict(d=80), dict(d=512), dict(d=16), dict(d=48),
+@pytest.mark.parametrize("over", [dict(d=4), dict(d=12), dict(d=84), dict(d=264), dict(d=512),
                                   dict(dtype=2), dict(dtype=-1)])
 def test_unsupported(over):
     _lib()
     assert _check(**over) == ATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("d", [8, 16, 40, 48, 72, 80, 104, 136, 160, 192, 200, 248])
+def test_padded_head_sizes_pass_validation(d):
+    """Any multiple of 8 up to 256 runs on the next built size (32, 64, 96,
+    128, 192, 256), whose LDS tiles the plan reports."""
+    _lib()
+    assert _check(d=d) == ATTN_OK
+    D = next(x for x in (32, 64, 96, 128, 192, 256) if x >= d)
+    plan = binding.attn_fwd_plan(2, 1000, 1000, 8, 2, d, 1, ATTN_DTYPE_BF16)
+    assert plan["lds_bytes"] == 4 * 64 * D * 2
+    # the split path's workspace holds rows of the padded size
+    n = binding.attn_fwd_split_workspace(1, 300, 2000, 8, 2, d, 1, ATTN_DTYPE_BF16, kv_split=4)
+    m = binding.attn_fwd_split_workspace(1, 300, 2000, 8, 2, D, 1, ATTN_DTYPE_BF16, kv_split=4)
+    assert n == m > 0
 
 
 def test_attn_fwd_rejects_before_any_device_call():
@@ -108,7 +123,7 @@ def test_attn_fwd_rejects_before_any_device_call():
     st = lib.attn_fwd(A, A, A, A, None, 1, 8, 8, 4, 3, 64, ctypes.c_float(1.0), 0,
                       ATTN_DTYPE_F16, None)
     assert st == ATTN_ERR_INVALID_ARG
-    st = lib.attn_fwd(A, A, A, A, None, 1, 8, 8, 4, 4, 80, ctypes.c_float(1.0), 0,
+    st = lib.attn_fwd(A, A, A, A, None, 1, 8, 8, 4, 4, 84, ctypes.c_float(1.0), 0,
                       ATTN_DTYPE_F16, None)
     assert st == ATTN_ERR_UNSUPPORTED
 
@@ -258,7 +273,7 @@ def test_merge_validation():
                  dict(B=0), dict(Sq=0), dict(Hq=0), dict(o_parts=A + 8), dict(o=A + 4),
                  dict(lse=A + 2), dict(lse_parts=A + 2), dict(B=1 << 20, Sq=1 << 12)):
         assert _mcheck(**over) == ATTN_ERR_INVALID_ARG, over
-    for over in (dict(d=80), dict(parts_dtype=7), dict(dtype=binding.ATTN_DTYPE_F32)):
+    for over in (dict(d=84), dict(d=264), dict(parts_dtype=7), dict(dtype=binding.ATTN_DTYPE_F32)):
         assert _mcheck(**over) == ATTN_ERR_UNSUPPORTED, over
     lib = _lib()
     assert lib.attn_merge(A, A, 0, 2, 1, 8, 2, 64, A, None, 0, None) == ATTN_ERR_INVALID_ARG
@@ -449,9 +464,12 @@ def test_prefill_shapes_do_not_take_the_decode_kernel():
     for cfg in ((1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16),
                 (1, 9, 100, 32, 8, 128, 1, ATTN_DTYPE_BF16),     # 4 x 9 = 36 rows, Sq > 8
                 (1, 8, 100, 256, 8, 128, 1, ATTN_DTYPE_BF16),    # 32 x 8 = 256 rows
-                (1, 64, 4096, 1, 1, 128, 0, ATTN_DTYPE_F16),     # 64 rows but Sq 64
-                (1, 1, 1000, 8, 8, 256, 0, ATTN_DTYPE_BF16)):    # d = 256
+                (1, 64, 4096, 1, 1, 128, 0, ATTN_DTYPE_F16)):    # 64 rows but Sq 64
         assert binding.attn_fwd_plan(*cfg)["decode"] == 0
+    # every head size takes the decode kernel when the rows fit (d = 256 and
+    # padded sizes included)
+    for d in (256, 200, 40):
+        assert binding.attn_fwd_plan(1, 1, 1000, 8, 8, d, 0, ATTN_DTYPE_BF16)["decode"] == 1
 
 
 # ------------------------------------------------------------- paged decode
@@ -489,10 +507,10 @@ def test_paged_decode_validation():
                  dict(max_seqlen=20 * 64 + 1), dict(scale=0.0), dict(causal=2)):
         assert _pcheck(**over) == ATTN_ERR_INVALID_ARG, over
     # outside the decode kernel's shapes: (Hq / Hkv) * Sq > 32 with Sq > 8,
-    # d not 32, 64, 96 or 128
-    for over in (dict(Sq=9), dict(d=80), dict(d=256), dict(dtype=2)):
+    # d not a multiple of 8 up to 256
+    for over in (dict(Sq=9), dict(d=84), dict(d=264), dict(dtype=2)):
         assert _pcheck(**over) == ATTN_ERR_UNSUPPORTED, over
-    for over in (dict(d=32), dict(d=96), dict(Sq=8)):
+    for over in (dict(d=32), dict(d=96), dict(d=80), dict(d=256), dict(d=200), dict(Sq=8)):
         assert _pcheck(**over) == ATTN_OK, over
 
 

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from exact_attention_19_amd.workloads import Workload, make_inputs
-from parity_common import _check_full, _say
+from parity_common import _check_full, _say, half_ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -231,3 +231,120 @@ def test_binding_rejects_bad_buffers_before_any_launch():
     with pytest.raises(ValueError):
         attn_decode_paged(qd, pool, pool, table, lens, out=torch.empty(qd.shape, dtype=qd.dtype))
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ padded head sizes
+#
+# Head sizes that are multiples of 8 but not of 32 (and 160, 192, 200) run on
+# the kernel of the next built size (32, 64, 96, 128, 192, 256): the columns
+# past d load as zeros and are not stored.
+
+PADDED = (8, 40, 80, 104, 160, 192, 200)
+
+
+def _padded_cases():
+    cases = []
+    for d in PADDED:
+        for dt in ("f16", "bf16"):
+            cases.append((d, dt, 2, 333, 517, True, 8, 2))     # causal, offset, GQA 4
+            cases.append((d, dt, 1, 200, 130, True, 4, 4))     # rows with no key
+        cases.append((d, "bf16", 1, 129, 300, False, 6, 3))
+        cases.append((d, "f16", 1, 1, 700, True, 8, 1))        # decode kernel
+    return cases
+
+
+@pytest.mark.parametrize("d,dt,B,Sq,Sk,causal,Hq,Hkv", _padded_cases())
+def test_padded_head_sizes(d, dt, B, Sq, Sk, causal, Hq, Hkv):
+    from exact_attention_19_amd import attn_fwd
+    w = _w(f"pad{d}_{dt}_{Sq}_{Sk}", B, Hq, Hkv, Sq, Sk, d, dt, causal)
+    q, k, v = make_inputs(w, seed=3 * d + Sq)
+    _say(f"[gpu] attn_fwd padded head size {d} {w.name} causal={causal}")
+    # outputs start as NaN: every element of o must be written, none past d
+    o = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    o, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=causal, out=o)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+
+
+@pytest.mark.parametrize("d", [40, 80, 136, 160, 168, 200, 248])
+def test_padded_head_sizes_split_and_strided(d):
+    """The key split (partial states of the padded size, merged into d
+    columns) and strided views whose rows are d long inside wider rows: the
+    columns past d of the wider rows are NaN and must never be read."""
+    from exact_attention_19_amd import attn_fwd_split, attn_fwd_strided
+    w = _w(f"pad{d}_split", 1, 8, 2, 300, 2000, d, "bf16", True)
+    q, k, v = make_inputs(w, seed=d + 1)
+    _say(f"[gpu] attn_fwd_split padded head size {d}")
+    o, lse = attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=True, kv_split=5)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+    wide = 256 + 64
+    def embed(t):
+        x = torch.full(t.shape[:3] + (wide,), float("nan"), dtype=t.dtype)
+        x[..., :d] = t
+        return x.cuda()[..., :d]
+    qs, ks, vs = embed(q), embed(k), embed(v)
+    assert qs.stride(2) == wide
+    _say(f"[gpu] attn_fwd_strided padded head size {d} in rows of {wide}")
+    o2, lse2 = attn_fwd_strided(qs, ks, vs, scale=w.scale, causal=True, kv_split=0)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o2.cpu(), lse2.cpu(), strict=False)
+
+
+@pytest.mark.parametrize("d", [40, 200, 256])
+def test_padded_and_large_head_sizes_paged_decode(d):
+    from exact_attention_19_amd import attn_decode_paged
+    from exact_attention_19_amd.workloads import make_paged_cache
+    from oracle import attn_decode_paged_oracle
+    w = _w(f"paged_d{d}", 3, 16, 4, 2, 1000, d, "bf16", True)
+    q, k, v = make_inputs(w, seed=d)
+    lens = [1000, 517, 33]
+    kp, vp, table, seqlens = make_paged_cache(k, v, lens, 64, seed=1)
+    _say(f"[gpu] attn_decode_paged head size {d}")
+    o, lse = attn_decode_paged(q.cuda(), kp.cuda(), vp.cuda(), table.cuda(), seqlens.cuda(),
+                               scale=w.scale, causal=True, max_seqlen=1000)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attn_decode_paged_oracle(q, kp, vp, table, seqlens, w.scale, True, 1000)
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False, ref=(o_ref, lse_ref))
+
+
+def test_merge_padded_head_size():
+    """attn_merge at d = 40 (parts with rows of 40 floats) against numpy fp64."""
+    from exact_attention_19_amd import attn_merge
+    from oracle import merge_partials_oracle
+    r = np.random.default_rng(13)
+    P, B, Sq, Hq, d = 4, 2, 29, 3, 40
+    op = r.standard_normal((P, B, Sq, Hq, d)).astype(np.float32)
+    lp = (2 * r.standard_normal((P, B, Hq, Sq))).astype(np.float32)
+    o_ref, lse_ref = merge_partials_oracle(op.astype(np.float64), lp.astype(np.float64))
+    o, lse = attn_merge(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda(),
+                        dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    # the merge is fp32: the error is the rounding of O to bf16 (half an ulp)
+    # plus fp32 arithmetic
+    diff = np.abs(o.double().cpu().numpy() - o_ref)
+    assert np.all(diff <= half_ulp(o_ref, "bf16") + 1e-5 * (1 + np.abs(o_ref)))
+    assert np.abs(lse.double().cpu().numpy() - lse_ref).max() <= 1e-4
+
+
+@pytest.mark.parametrize("d", [8, 40, 136, 200])
+def test_padded_head_sizes_decode_strided(d):
+    """The decode kernel (one query row per head) on rows of d inside wider
+    NaN-filled rows: no column past d may be read."""
+    from exact_attention_19_amd import attn_fwd_plan, attn_fwd_strided
+    from exact_attention_19_amd.binding import ATTN_DTYPE_BF16
+    w = _w(f"pad{d}_decode_strided", 2, 16, 4, 1, 900, d, "bf16", True)
+    assert attn_fwd_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, d, 1, ATTN_DTYPE_BF16)["decode"] == 1
+    q, k, v = make_inputs(w, seed=d + 5)
+    wide = 264
+    def embed(t):
+        x = torch.full(t.shape[:3] + (wide,), float("nan"), dtype=t.dtype)
+        x[..., :d] = t
+        return x.cuda()[..., :d]
+    for kv_split in (1, 0):
+        _say(f"[gpu] attn_fwd_strided decode kernel, head size {d} in rows of {wide}, "
+             f"kv_split={kv_split}")
+        o, lse = attn_fwd_strided(embed(q), embed(k), embed(v), scale=w.scale, causal=True,
+                                  kv_split=kv_split)
+        torch.cuda.synchronize()
+        _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
