@@ -279,6 +279,8 @@ __device__ __forceinline__ void load_tile(const char* slice, uint32_t row_bytes,
 // ------------------------------------------------------------ launch plan
 struct Plan {
   int nw, qb, gh, rows_wg, qtiles, ncols, xcd_cols, grid, lds_bytes, pipelined;
+  int xcd_qsplit;  // > 0: XCDs sharing one (batch, kv head), each taking every
+                   // xcd_qsplit-th query block of all its head subsets
 };
 
 bool sizes_ok(int B, int Sq, int Sk, int Hq, int Hkv) {
@@ -302,6 +304,18 @@ Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
   const long long qt = (Sq + pl.rows_wg - 1) / pl.rows_wg;
   pl.qtiles = qt > 0x7fffffffll ? -1 : (int)qt;
   pl.xcd_cols = (pl.ncols % 8 == 0) ? pl.ncols / 8 : 0;
+  // Fewer (batch, kv head) pairs than XCDs, each split into head subsets: the
+  // subsets of a pair go to one XCD (they read the same K/V tiles at the same
+  // time, so the second read hits that XCD's L2), and the pair's query blocks
+  // are dealt to 8 / (B * Hkv) XCDs.
+  pl.xcd_qsplit = 0;
+  {
+    const int bh = B * Hkv;
+    if (hsub > 1 && bh < 8 && 8 % bh == 0 && qt % (8 / bh) == 0) {
+      pl.xcd_qsplit = 8 / bh;
+      pl.xcd_cols = 0;
+    }
+  }
   const long long grid = qt * pl.ncols;
   pl.grid = (grid > 0x7fffffffll || pl.qtiles < 0) ? -1 : (int)grid;
   pl.lds_bytes = 4 * BC * padded_head(d) * 2;

@@ -93,6 +93,7 @@ struct Params {
   int qtiles;    // ceil(Sq / rows_wg)
   int ncols;     // B * Hkv * hsub
   int xcd_cols;  // columns per XCD when the grid is XCD-ordered, else 0
+  int xcd_qsplit;  // > 0: XCDs per (batch, kv head) (query blocks dealt out)
   int off;       // Sk - Sq
   float scale_log2;  // scale * log2(e)
   // key split: K/V tiles per piece (even; 0 = no split).  A row block with
@@ -168,7 +169,15 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
   {
     const int L = blockIdx.x;
     int u;
-    if (p.xcd_cols > 0) {
+    if (p.xcd_qsplit > 0) {
+      // XCD x: (batch, kv head) x / xcd_qsplit, every head subset, query
+      // blocks x % xcd_qsplit, + xcd_qsplit, ... heaviest first (no key split)
+      const int xcd = L & 7;
+      const int k = L >> 3;
+      const int hs0 = k % p.hsub;
+      u = (k / p.hsub) * p.xcd_qsplit + xcd % p.xcd_qsplit;
+      col = (xcd / p.xcd_qsplit) * p.hsub + hs0;
+    } else if (p.xcd_cols > 0) {
       const int xcd = L & 7;
       const int k = L >> 3;
       u = k / p.xcd_cols;
@@ -972,6 +981,7 @@ Params fill_params(const Plan& pl, const void* q, const void* k, const void* v, 
   p.qtiles = pl.qtiles;
   p.ncols = pl.ncols;
   p.xcd_cols = pl.xcd_cols;
+  p.xcd_qsplit = pl.xcd_qsplit;
   p.off = off;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.chunk = 0;
@@ -1086,6 +1096,10 @@ attn_status run_forward(const void* q, const void* k, const void* v, void* o, fl
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
   }
   p.chunk = sp.chunk;
+  if (p.xcd_qsplit > 0) {  // pieces follow the column-major order
+    p.xcd_qsplit = 0;
+    p.xcd_cols = (p.ncols % 8 == 0) ? p.ncols / 8 : 0;
+  }
   p.q_split = sp.q_first;
   p.sq_split = Sq - sp.q_first;
   p.part_o = (float*)workspace;
@@ -1201,7 +1215,7 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
   if (st != ATTN_OK) return st;
   const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
   int vals[10] = {pl.grid, pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
-                  pl.lds_bytes, pl.xcd_cols > 0 ? 1 : 0, pl.pipelined, 0};
+                  pl.lds_bytes, pl.xcd_cols > 0 || pl.xcd_qsplit > 0 ? 1 : 0, pl.pipelined, 0};
   if (decode_eligible(Sq, Hq, Hkv, d)) {
     // the decode kernel, unsplit: a workgroup per (batch, kv head) with all
     // g * Sq rows in one wave, DEC_WAVES waves over the keys
