@@ -50,6 +50,8 @@ struct BwdParams {
   float* dvec;  // D_i, [B][Hq][Sq]
   float* l2;    // lse_i * log2(e), +inf for rows that see no key, [B][Hq][Sq]
   int B, Sq, Sk, Hq, Hkv;
+  int d;        // head size: rows hold d elements; the kernels are built for
+                // D >= d, columns past d read as zeros and are not written
   int group, gh, hsub, rows_wg, qtiles, ncols, xcd_cols;  // dq launch (forward plan)
   int off;      // Sk - Sq
   float scale, scale_log2;
@@ -68,9 +70,9 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
   const bool valid = row < rows;
   float acc = 0.f;
   if (valid) {
-    const uint16_t* orow = p.o + row * D;
-    const uint16_t* drow = p.dout + row * D;
-    for (int c = t; c < CH; c += 8) {
+    const uint16_t* orow = p.o + row * p.d;
+    const uint16_t* drow = p.dout + row * p.d;
+    for (int c = t; c < CH && 8 * c < p.d; c += 8) {
       const u32x4 a = *(const u32x4*)(orow + 8 * c);
       const u32x4 g = *(const u32x4*)(drow + 8 * c);
 #pragma unroll
@@ -152,9 +154,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
     n_full = min(n_full, lim > 0 ? lim / 64 : 0);
   }
 
-  const uint32_t rbkv = (uint32_t)p.Hkv * D * 2;
-  const char* kslice = (const char*)(p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
-  const char* vslice = (const char*)(p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
+  const uint32_t rbkv = (uint32_t)p.Hkv * p.d * 2;
+  const char* kslice = (const char*)(p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * p.d);
+  const char* vslice = (const char*)(p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * p.d);
 
   // this lane's query row: Q and dO fragments (B operands, d as k)
   const int qi = q0w + l32;
@@ -165,9 +167,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (ok) {
-        x = *(const u32x4*)(p.q + r * D + kk * 16 + hh * 8);
-        y = *(const u32x4*)(p.dout + r * D + kk * 16 + hh * 8);
+      if (ok && kk * 16 + hh * 8 < p.d) {  // columns past d stay zero
+        x = *(const u32x4*)(p.q + r * p.d + kk * 16 + hh * 8);
+        y = *(const u32x4*)(p.dout + r * p.d + kk * 16 + hh * 8);
       }
       qf[kk] = __builtin_bit_cast(i16x8, x);
       dof[kk] = __builtin_bit_cast(i16x8, y);
@@ -193,16 +195,16 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
   if (n_end > 0) {
-    load_tile<D>(kslice, rbkv, 0, p.Sk, kbuf(0), wave, lane);
-    load_tile<D>(vslice, rbkv, 0, p.Sk, vbuf(0), wave, lane);
+    load_tile<D>(kslice, rbkv, 0, p.Sk, p.d, kbuf(0), wave, lane);
+    load_tile<D>(vslice, rbkv, 0, p.Sk, p.d, vbuf(0), wave, lane);
     for (int j = 0; j < n_end; ++j) {
       // tile j has landed (this wave's loads) and every wave is done with
       // tile j - 1, whose buffers now take tile j + 1
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (j + 1 < n_end) {
-        load_tile<D>(kslice, rbkv, j + 1, p.Sk, kbuf(j + 1), wave, lane);
-        load_tile<D>(vslice, rbkv, j + 1, p.Sk, vbuf(j + 1), wave, lane);
+        load_tile<D>(kslice, rbkv, j + 1, p.Sk, p.d, kbuf(j + 1), wave, lane);
+        load_tile<D>(vslice, rbkv, j + 1, p.Sk, p.d, vbuf(j + 1), wave, lane);
       }
       LDS_PTR(char) const kt = kbuf(j);
       LDS_PTR(char) const vt = vbuf(j);
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
   }
 
   if (ok) {
-    uint16_t* row = p.dq + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D;
+    uint16_t* row = p.dq + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * p.d;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
         const i16x8 y = T::cvt(x);
         const u32x2 w = {(unsigned)(uint16_t)y[0] | ((unsigned)(uint16_t)y[1] << 16),
                          (unsigned)(uint16_t)y[2] | ((unsigned)(uint16_t)y[3] << 16)};
-        *(u32x2*)(row + cb * 32 + 8 * g + 4 * hh) = w;
+        if (cb * 32 + 8 * g + 4 * hh < p.d) *(u32x2*)(row + cb * 32 + 8 * g + 4 * hh) = w;
       }
   }
 }
@@ -344,14 +346,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   // K rows (waves 0-3) and V rows (waves 4-7) of the 128 keys into LDS, as
   // two 64-row tiles each; a tile wholly past Sk is zeroed instead
   {
-    const uint32_t rbk = (uint32_t)p.Hkv * D * 2;
+    const uint32_t rbk = (uint32_t)p.Hkv * p.d * 2;
     const char* slice =
-        (const char*)((qh == 0 ? p.k : p.v) + ((int64_t)b * p.Sk * p.Hkv + kvh) * D);
+        (const char*)((qh == 0 ? p.k : p.v) + ((int64_t)b * p.Sk * p.Hkv + kvh) * p.d);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       LDS_PTR(char) const dst = (LDS_PTR(char))(qh == 0 ? lds_k[i] : lds_v[i]);
       if (k0 + 64 * i < p.Sk) {
-        load_tile<D>(slice, rbk, 2 * kblk + i, p.Sk, dst, kg, lane);
+        load_tile<D>(slice, rbk, 2 * kblk + i, p.Sk, p.d, dst, kg, lane);
       } else {
         LDS_PTR(u32x4) z = (LDS_PTR(u32x4))dst;
         for (int e = kg * 64 + lane; e < TB / 16; e += 256) z[e] = (u32x4){0u, 0u, 0u, 0u};
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   }
   const int per_head = nqt > qt0 ? nqt - qt0 : 0;
   const int steps = per_head * p.group;
-  const uint32_t rbq = (uint32_t)p.Hq * D * 2;
+  const uint32_t rbq = (uint32_t)p.Hq * p.d * 2;
 
   // tile t: Q by waves 0-3, dO by waves 4-7, and the 64 rows' lse * log2(e)
   // (wave 0) and D (wave 4), rows clamped to Sq - 1 (rows past Sq are
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     const int h = kvh * p.group + nh;
     const int qt = qt0 + nq;
     const int64_t head0 = (int64_t)b * p.Sq * p.Hq + h;
-    load_tile<D>((const char*)((qh == 0 ? p.q : p.dout) + head0 * D), rbq, qt, p.Sq,
+    load_tile<D>((const char*)((qh == 0 ? p.q : p.dout) + head0 * p.d), rbq, qt, p.Sq, p.d,
                  qh == 0 ? qbuf(t) : obuf(t), kg, lane);
     if (kg == 0) {
       const float* src = (qh == 0 ? p.l2 : p.dvec) + ((int64_t)b * p.Hq + h) * p.Sq;
@@ -558,8 +560,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __syncthreads();
   if (qh == 0 && kok) {
     const int64_t r = ((int64_t)b * p.Sk + kj) * p.Hkv + kvh;
-    uint16_t* dkrow = p.dk + r * D;
-    uint16_t* dvrow = p.dv + r * D;
+    uint16_t* dkrow = p.dk + r * p.d;
+    uint16_t* dvrow = p.dv + r * p.d;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -581,8 +583,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
                           (unsigned)(uint16_t)xk[2] | ((unsigned)(uint16_t)xk[3] << 16)};
         const u32x2 wv = {(unsigned)(uint16_t)yv[0] | ((unsigned)(uint16_t)yv[1] << 16),
                           (unsigned)(uint16_t)yv[2] | ((unsigned)(uint16_t)yv[3] << 16)};
-        *(u32x2*)(dkrow + cb * 32 + 8 * g + 4 * hh) = wk;
-        *(u32x2*)(dvrow + cb * 32 + 8 * g + 4 * hh) = wv;
+        if (cb * 32 + 8 * g + 4 * hh < p.d) {
+          *(u32x2*)(dkrow + cb * 32 + 8 * g + 4 * hh) = wk;
+          *(u32x2*)(dvrow + cb * 32 + 8 * g + 4 * hh) = wv;
+        }
       }
   }
 }
@@ -602,8 +606,9 @@ attn_status validate_bwd(const void* q, const void* k, const void* v, const void
     return ATTN_ERR_INVALID_ARG;
   if (((uintptr_t)lse) & 3u) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
-  // (d = 256 would need 256 registers of dK/dV sums per wave alone)
-  if (d != 32 && d != 64 && d != 96 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // any multiple of 8 up to 128, padded to 32, 64, 96 or 128 (d above 128
+  // would need 256 registers of dK/dV sums per wave alone)
+  if (!head_size_ok(d) || d > 128) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)Sq + Sk >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)Hq * d * 2 * 64 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31))
@@ -638,7 +643,7 @@ hipError_t launch_bwd_c(bool causal, const Plan& pl, const BwdParams& p, hipStre
 
 template <int DT>
 hipError_t launch_bwd_d(int d, bool causal, const Plan& pl, const BwdParams& p, hipStream_t st) {
-  switch (d) {
+  switch (padded_head(d)) {
     case 32: return launch_bwd_c<DT, 32>(causal, pl, p, st);
     case 64: return launch_bwd_c<DT, 64>(causal, pl, p, st);
     case 96: return launch_bwd_c<DT, 96>(causal, pl, p, st);
@@ -696,6 +701,7 @@ attn_status run_bwd(const void* q, const void* k, const void* v, const void* o,
   p.Sk = Sk;
   p.Hq = Hq;
   p.Hkv = Hkv;
+  p.d = d;
   p.group = Hq / Hkv;
   p.gh = pl.gh;
   p.hsub = p.group / pl.gh;

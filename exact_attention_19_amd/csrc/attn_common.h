@@ -253,27 +253,32 @@ __device__ __forceinline__ i16x8 read_row_frag(LDS_PTR(char) tile, const uint32_
 }
 
 // Direct global -> LDS load of tile rows [64 n, 64 n + 64) of a row-strided
-// slice (row_bytes apart, d contiguous) by the 4 waves of a workgroup: round
-// u of a wave writes LDS bytes [(4u + wave) * 1024, +1024), i.e. column block
-// (4u + wave) / 4, rows 16 ((4u + wave) % 4) + lane / 4, slot lane % 4.  Rows
-// at or past nrows re-read row nrows - 1 (finite values; the caller masks
-// them).  MUBUF loads through a buffer descriptor of the tile (64 rows x
-// row_bytes, which the host keeps below 2^31).
+// slice (row_bytes apart, d <= D contiguous elements per row) by the 4 waves
+// of a workgroup: round u of a wave writes LDS bytes [(4u + wave) * 1024,
+// +1024), i.e. column block (4u + wave) / 4, rows 16 ((4u + wave) % 4) +
+// lane / 4, slot lane % 4.  Rows at or past nrows re-read row nrows - 1
+// (finite values; the caller masks them); columns at or past d are zeros
+// (their loads aim past the descriptor's end).  MUBUF loads through a buffer
+// descriptor of the tile's bytes (63 rows x row_bytes + one row, which the
+// host keeps below 2^31).
 template <int D>
 __device__ __forceinline__ void load_tile(const char* slice, uint32_t row_bytes, int n, int nrows,
-                                          LDS_PTR(char) buf, int wave, int lane) {
+                                          int d, LDS_PTR(char) buf, int wave, int lane) {
   constexpr int CB = D / 32;
+  constexpr int FULL = full_col_blocks(D);
   const int ld_row = 16 * wave + (lane >> 2);
   const int ld_chunk = (lane & 3) ^ ((ld_row >> 2) & 3);
   const int r = min(64 * n + ld_row, nrows - 1) - 64 * n;
   const uint32_t off = (uint32_t)r * row_bytes + (uint32_t)ld_chunk * 16;
   const char* tile = slice + (int64_t)n * 64 * row_bytes;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)(64 * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)tile, 0, (int)(63 * row_bytes + (uint32_t)d * 2), 0x00020000);
 #pragma unroll
-  for (int u = 0; u < CB; ++u)
+  for (int u = 0; u < CB; ++u) {
+    const uint32_t o = u < FULL || 32 * u + 8 * ld_chunk < d ? off : OOB_OFFSET;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_PTR(void))(buf + (u * 4 + wave) * 1024), 16,
-                                             off, 64 * u, 0, 0);
+                                             o, 64 * u, 0, 0);
+  }
 }
 
 // ------------------------------------------------------------ launch plan

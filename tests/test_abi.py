@@ -367,9 +367,9 @@ def test_bwd_validation():
             assert _bcheck(p) == ATTN_ERR_INVALID_ARG, i
     for over in (dict(Hq=7), dict(B=0), dict(Sk=0), dict(scale=0.0), dict(causal=3)):
         assert _bcheck(**over) == ATTN_ERR_INVALID_ARG, over
-    for over in (dict(d=80), dict(d=256), dict(dtype=2)):
+    for over in (dict(d=84), dict(d=136), dict(d=256), dict(dtype=2)):
         assert _bcheck(**over) == ATTN_ERR_UNSUPPORTED, over
-    for over in (dict(d=32), dict(d=96)):
+    for over in (dict(d=32), dict(d=96), dict(d=8), dict(d=40), dict(d=80), dict(d=120)):
         assert _bcheck(**over) == ATTN_OK, over
 
 
@@ -589,7 +589,7 @@ def test_bwd_causal_offset_validation():
     q[3] = None
     assert binding.attn_bwd_causal_offset_check(*q, *vals, 0, ATTN_DTYPE_F16) \
         == ATTN_ERR_INVALID_ARG
-    assert binding.attn_bwd_causal_offset_check(*p, 2, 100, 120, 8, 2, 80, 0.125, 0,
+    assert binding.attn_bwd_causal_offset_check(*p, 2, 100, 120, 8, 2, 84, 0.125, 0,
                                                 ATTN_DTYPE_F16) == ATTN_ERR_UNSUPPORTED
     assert binding.attn_bwd_causal_offset_check(*p, *vals, 0, 2) == ATTN_ERR_UNSUPPORTED
     need = binding.attn_bwd_workspace(2, 100, 8)
