@@ -150,12 +150,12 @@ def attn_fwd_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Sq, Sk, Hq, Hkv, d,
 
 def attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype_code, kv_split=0) -> dict:
     """The launches attn_fwd_split would make (no device call)."""
-    out = (ctypes.c_int * 5)()
+    out = (ctypes.c_int * 6)()
     st = load_library().attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), dtype_code,
-                                            int(kv_split), out, 5)
+                                            int(kv_split), out, 6)
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_split_plan")
-    keys = ("grid", "pieces", "keys_per_piece", "first_split_row", "merge_grid")
+    keys = ("grid", "pieces", "keys_per_piece", "first_split_row", "merge_grid", "threads")
     return dict(zip(keys, list(out)))
 
 

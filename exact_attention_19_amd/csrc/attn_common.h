@@ -286,6 +286,8 @@ struct Plan {
   int nw, qb, gh, rows_wg, qtiles, ncols, xcd_cols, grid, lds_bytes, pipelined;
   int xcd_qsplit;  // > 0: XCDs sharing one (batch, kv head), each taking every
                    // xcd_qsplit-th query block of all its head subsets
+  int ng;          // groups of nw waves per workgroup walking alternate
+                   // K/V tiles of the same rows (1 or 2)
 };
 
 bool sizes_ok(int B, int Sq, int Sk, int Hq, int Hkv) {
@@ -324,7 +326,25 @@ Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
   const long long grid = qt * pl.ncols;
   pl.grid = (grid > 0x7fffffffll || pl.qtiles < 0) ? -1 : (int)grid;
   pl.lds_bytes = 4 * BC * padded_head(d) * 2;
+  pl.ng = 1;  // set by the caller that knows the key split (two_groups)
   return pl;
+}
+
+// Two groups of 4 waves per workgroup, taking alternate K/V tiles of the same
+// query rows, when the workgroups with work number at most one per CU (256 on
+// MI355X): a lone 4-wave workgroup then leaves each SIMD one wave, and a
+// second group's softmax runs beside the first one's matrix products.  Their
+// tile buffers take twice the LDS (128 KiB at d = 128), so padded head sizes
+// above 128 keep one group.  Measured on MI355X (f16, d = 128): two waves
+// per SIMD finish a tile pair about 14 % sooner than one wave does a tile
+// each, while the second group's first loads and the merge of the two states
+// add about 3 us per workgroup; below 8 tiles in the longest workgroup (4 per
+// group) that costs more than it saves.
+constexpr int kCUCount = 256;
+constexpr int kTwoGroupMinTiles = 8;
+inline bool two_groups(long long active_workgroups, int d, int max_tiles) {
+  return active_workgroups <= kCUCount && padded_head(d) <= 128 &&
+         max_tiles >= kTwoGroupMinTiles;
 }
 
 using attn_detail::DecodeArgs;

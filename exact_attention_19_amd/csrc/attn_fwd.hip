@@ -135,10 +135,19 @@ struct PFrag {
   PT lo[BC / 16];  // fp16 only (hi + lo split); unused for bf16
 };
 
-template <int DT, int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_kernel(Params p) {
+// NG groups of 4 waves per workgroup.  With NG = 2 (grids of at most one
+// workgroup per CU: short sequences, few heads), the two groups walk
+// alternate K/V tiles of the same query rows, two waves per SIMD, each with
+// its own tile buffers and online-softmax state; at the end group 1 hands
+// its state (running max, sums, unnormalised O) to group 0 through LDS and
+// group 0 combines the two with the online-softmax rescale (personal-notes
+// page, section "Online Softmax", applied to the two key subsets).
+template <int DT, int D, bool CAUSAL, int NG>
+__global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fwd_pipe_kernel(
+    Params p) {
   using T = Ty<DT>;
-  constexpr int NT = NW * 64;
+  constexpr int NW = 4;               // waves per group
+  constexpr int NT = NW * 64;         // threads per group
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int CPT = BC * CPR / NT;  // direct loads per lane per tile
   constexpr int KB = BC / 32;
@@ -153,15 +162,23 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
   // alias analysis then separates the direct loads into one buffer from the
   // reads of another, so no read waits for an unrelated tile load (with one
   // LDS array every read of a tile waited for all loads in flight).
-  __shared__ __attribute__((aligned(1024))) char lds_k0[TB], lds_k1[TB], lds_v0[TB], lds_v1[TB];
-  auto kbuf_of = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_k1 : (LDS_PTR(char))lds_k0; };
-  auto vbuf_of = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_v1 : (LDS_PTR(char))lds_v0; };
+  // (one set per group)
+  __shared__ __attribute__((aligned(1024))) char lds_k0[NG][TB], lds_k1[NG][TB], lds_v0[NG][TB],
+      lds_v1[NG][TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR
+  const int grp = NG > 1 ? wave_all >> 2 : 0;  // group
+  const int wave = wave_all & 3;   // wave within the group
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  auto kbuf_of = [&](int n) {
+    return (n & 1) ? (LDS_PTR(char))lds_k1[grp] : (LDS_PTR(char))lds_k0[grp];
+  };
+  auto vbuf_of = [&](int n) {
+    return (n & 1) ? (LDS_PTR(char))lds_v1[grp] : (LDS_PTR(char))lds_v0[grp];
+  };
 
   // ---- work decode: heaviest row blocks first, optionally grouped per XCD;
   // with a key split, all first pieces, then all second pieces, ...
@@ -198,15 +215,22 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
   const int q0wg = qt * p.rows_wg;
   const int q0w = q0wg + rowblk * 32;
 
-  // ---- KV tile range of the workgroup (all waves walk the same tiles):
-  // tiles [j_lo, j_hi) of the row block's n_end.  j_lo is even (the chunk is
-  // even), so tile j always sits in buffer j & 1.
+  // ---- KV tile range of the workgroup: tiles [j_lo, j_hi) of the row
+  // block's n_end.  Group g walks tiles j_lo + g, j_lo + g + NG, ...: its
+  // local tile i (buffer i & 1) is tile_of(i).  Both groups run n_loc
+  // iterations so that they pass the same barriers; a group with one tile
+  // fewer runs a filler tile past j_hi whose keys are all masked.
   const int n_end = block_tiles(q0wg, p.rows_wg, p.Sq, p.Sk, p.off, CAUSAL);
   const int pieces = block_pieces(n_end, p.chunk);
   if (piece >= pieces) return;  // an empty piece: uniform over the workgroup
   const bool split = pieces > 1;
   const int j_lo = piece * p.chunk;
   const int j_hi = split ? min(n_end, j_lo + p.chunk) : n_end;
+  const int n_loc = j_hi > j_lo ? (j_hi - j_lo + NG - 1) / NG : 0;
+  auto tile_of = [&](int i) { return j_lo + grp + NG * i; };
+  // the tile a load reads: a filler tile reads the block's last tile (its
+  // keys are masked), so that no load addresses memory past the tensors
+  auto load_of = [&](int i) { return min(tile_of(i), j_hi - 1); };
   int n_full = p.Sk / BC;
   if (CAUSAL) {
     const int lim = q0wg + p.off + 1;
@@ -403,22 +427,26 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
     return NSC;
   };
   static_assert(KB == 2, "two 32-key blocks per tile");
-  static_assert(NPV + KK + 2 <= NOPS, "the skewed softmax ends inside the step list");
+  constexpr int SK = D <= 128 ? 1 : 0;  // softmax skew, in steps
+  static_assert(NPV + KK + 2 * SK <= NOPS, "the skewed softmax ends inside the step list");
 
-  auto iter = [&](auto par, int j, f32x16 (&Sc)[KB], f32x16 (&Sn)[KB],
+  // (i: the group's local tile index; j: the tile)
+  auto iter = [&](auto par, int i, f32x16 (&Sc)[KB], f32x16 (&Sn)[KB],
                   const PFrag<i16x8>& Pp, PFrag<i16x8>& Pc) {
     constexpr int PAR = decltype(par)::value;
+    const int j = tile_of(i);
     LDS_PTR(char) const K_NEXT = kbuf_of(PAR ^ 1);  // K(j+1)
     LDS_PTR(char) const V_PREV = vbuf_of(PAR ^ 1);  // V(j-1)
     LDS_PTR(char) const K_LOAD = kbuf_of(PAR);      // K(j+2)
     LDS_PTR(char) const V_LOAD = vbuf_of(PAR);      // V(j)
-    if (j + 2 < j_hi) issue_rows(kslice, rbk, ld_off_k, j + 2, K_LOAD);
-    issue_rows(vslice, rbv, ld_off_v, j, V_LOAD);
-    // mask the straddling tiles, then the row max and the max update
-    if (j >= n_full) {
+    if (i + 2 < n_loc) issue_rows(kslice, rbk, ld_off_k, load_of(i + 2), K_LOAD);
+    issue_rows(vslice, rbv, ld_off_v, load_of(i), V_LOAD);
+    // mask the straddling tiles (and a filler tile past j_hi, wholly), then
+    // the row max and the max update
+    if (j >= n_full || j >= j_hi) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int L = lim_row - j * BC - kb * 32 - 8 * hh;
+        const int L = j >= j_hi ? -BC : lim_row - j * BC - kb * 32 - 8 * hh;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (key_of_reg(r) > L) Sc[kb][r] = -INFINITY;
@@ -485,22 +513,25 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
         }
         Sn[kb] = T::mfma(f, qf[kk], Sn[kb]);
       }
-      // P(j) = exp2(S(j) * c - m), skewed over three steps: the argument
-      // of this step's scores, the exp2 of the previous step's, the sums
-      // and conversion of the one before, so that no op of a step waits on
-      // the op just before it (measured: 1.5-2 % on the long GQA
+      // P(j) = exp2(S(j) * c - m), skewed over three steps (SK = 1): the
+      // argument of this step's scores, the exp2 of the previous step's,
+      // the sums and conversion of the one before, so that no op of a step
+      // waits on the op just before it (measured: 1.5-2 % on the long GQA
       // workloads).  The last scores (step NPV + KK - 1) finish two steps
-      // later, inside the QK steps of key block 1.
+      // later, inside the QK steps of key block 1.  Head sizes above 128
+      // have no registers to spare for the values in flight (SK = 0).
 #pragma unroll
       for (int sc = score_lo(i); sc < score_lo(i + 1); ++sc) {
         const int kb = sc / 16, r = sc % 16;
         xa[sc] = __builtin_fmaf(Sc[kb][r], p.scale_log2, neg_m);
       }
 #pragma unroll
-      for (int sc = (i >= 1 ? score_lo(i - 1) : 0); sc < (i >= 1 ? score_lo(i) : 0); ++sc)
+      for (int sc = (i >= SK ? score_lo(i - SK) : 0); sc < (i >= SK ? score_lo(i - SK + 1) : 0);
+           ++sc)
         xa[sc] = __builtin_amdgcn_exp2f(xa[sc]);
 #pragma unroll
-      for (int sc = (i >= 2 ? score_lo(i - 2) : 0); sc < (i >= 2 ? score_lo(i - 1) : 0); ++sc) {
+      for (int sc = (i >= 2 * SK ? score_lo(i - 2 * SK) : 0);
+           sc < (i >= 2 * SK ? score_lo(i - 2 * SK + 1) : 0); ++sc) {
         {
           e[sc % 8] = xa[sc];
           if constexpr (T::LSE_FROM_FP32_SUM) {
@@ -545,30 +576,76 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 8 / NW) void attn_fwd_pipe_k
     __syncthreads();
   };
 
-  if (j_hi > j_lo) {
-    // prologue: K(j_lo) and K(j_lo+1) in flight; the V buffer read for the
-    // tile before j_lo in the first iteration is cleared so that 0 * V stays 0.
-    issue_rows(kslice, rbk, ld_off_k, j_lo, kbuf_of(0));
-    if (j_lo + 1 < j_hi) issue_rows(kslice, rbk, ld_off_k, j_lo + 1, kbuf_of(1));
+  if (n_loc > 0) {
+    // prologue: the group's first two K tiles in flight; the V buffer read
+    // for the tile before the first in the first iteration is cleared so
+    // that 0 * V stays 0.
+    issue_rows(kslice, rbk, ld_off_k, load_of(0), kbuf_of(0));
+    if (n_loc > 1) issue_rows(kslice, rbk, ld_off_k, load_of(1), kbuf_of(1));
     {
       LDS_PTR(u32x4) z = (LDS_PTR(u32x4))vbuf_of(1);
-      for (int i = tid; i < TB / 16; i += NT) z[i] = (u32x4){0u, 0u, 0u, 0u};
+      for (int x = tid & (NT - 1); x < TB / 16; x += NT) z[x] = (u32x4){0u, 0u, 0u, 0u};
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(0), K(1) landed
     __syncthreads();
     qk(SA, kbuf_of(0));
     __syncthreads();  // every wave has read K(0) before K(2) overwrites it
-    int j = j_lo;
-    for (; j + 1 < j_hi; j += 2) {
-      iter(std::integral_constant<int, 0>{}, j, SA, SB, PB, PA);
-      iter(std::integral_constant<int, 1>{}, j + 1, SB, SA, PA, PB);
+    int i = 0;
+    for (; i + 1 < n_loc; i += 2) {
+      iter(std::integral_constant<int, 0>{}, i, SA, SB, PB, PA);
+      iter(std::integral_constant<int, 1>{}, i + 1, SB, SA, PA, PB);
     }
-    if (j < j_hi) {
-      iter(std::integral_constant<int, 0>{}, j, SA, SB, PB, PA);
-      pv(PA, vbuf_of(j));  // drain: the last tile's P is in PA
+    if (i < n_loc) {
+      iter(std::integral_constant<int, 0>{}, i, SA, SB, PB, PA);
+      pv(PA, vbuf_of(0));  // drain: the last tile's P is in PA
     } else {
-      pv(PB, vbuf_of(j - 1));  // drain: the last tile's P is in PB
+      pv(PB, vbuf_of(1));  // drain: the last tile's P is in PB
     }
+  }
+
+  if constexpr (NG > 1) {
+    // group 1's state to group 0: wave w of group 1 writes its O^T
+    // accumulators into its tile buffer w (free once every wave is past the
+    // loop), lane-contiguous 16-byte slots; its max and partial sums go to a
+    // small array.  Group 0 combines: m = max(m0, m1), a_g = 2^(m_g - m),
+    // O = a0 O0 + a1 O1, l = a0 l0 + a1 l1.
+    __shared__ float lds_state[4][3][64];
+    __syncthreads();
+    LDS_PTR(char) const mbuf = wave == 0   ? (LDS_PTR(char))lds_k0[NG - 1]
+                               : wave == 1 ? (LDS_PTR(char))lds_k1[NG - 1]
+                               : wave == 2 ? (LDS_PTR(char))lds_v0[NG - 1]
+                                           : (LDS_PTR(char))lds_v1[NG - 1];
+    static_assert(CB * 4 * 1024 <= TB, "a wave's accumulators fit one tile buffer");
+    if (grp == 1) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(LDS_PTR(f32x4))(mbuf + ((cb * 4 + g) * 64 + lane) * 16) =
+              (f32x4){acc_o[cb][4 * g], acc_o[cb][4 * g + 1], acc_o[cb][4 * g + 2],
+                      acc_o[cb][4 * g + 3]};
+      lds_state[wave][0][lane] = m_run;
+      lds_state[wave][1][lane] = l_rnd;
+      lds_state[wave][2][lane] = l_fp32;
+    }
+    __syncthreads();
+    if (grp == 1) return;  // group 0 finishes the rows
+    const float m1 = lds_state[wave][0][lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - m);
+    m_run = m;
+    l_rnd = a0 * l_rnd + a1 * lds_state[wave][1][lane];
+    l_fp32 = a0 * l_fp32 + a1 * lds_state[wave][2][lane];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 y = *(LDS_PTR(const f32x4))(mbuf + ((cb * 4 + g) * 64 + lane) * 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc_o[cb][4 * g + r] = a0 * acc_o[cb][4 * g + r] + a1 * y[r];
+      }
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
@@ -878,8 +955,11 @@ SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int cau
   sp.npieces = 1;
   sp.q_first = Sq;
   sp.grid = pl.grid;
-  if (pl.grid <= 0 || kv_split == 1) return sp;
+  if (pl.grid <= 0) return sp;
+  // tiles of the longest row block (the last one: causal rows see the most keys)
   const int nmax = block_tiles((pl.qtiles - 1) * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0);
+  sp.base.ng = two_groups(pl.grid, d, nmax) ? 2 : 1;
+  if (kv_split == 1) return sp;
   int chunk;
   if (kv_split == 0) {
     if ((long long)pl.qtiles * pl.ncols >= kCUs) return sp;
@@ -912,6 +992,13 @@ SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int cau
     ++qt0;  // ends: the last block has npieces > 1 pieces
   sp.q_first = qt0 * pl.rows_wg;
   sp.grid = (long long)sp.npieces * pl.qtiles * pl.ncols;
+  {
+    long long active = 0;  // workgroups with a piece to run
+    for (int qt = 0; qt < pl.qtiles; ++qt)
+      active += block_pieces(block_tiles(qt * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0),
+                             chunk);
+    sp.base.ng = two_groups(active * pl.ncols, d, chunk) ? 2 : 1;
+  }
   sp.merge_rows = (long long)B * (Sq - sp.q_first) * Hq;
   const int D = padded_head(d);
   const int rpb = 256 / (D / 4);
@@ -951,9 +1038,15 @@ hipError_t launch_merge_any(int parts_dtype, int dtype, int d, long long grid,
 
 template <int DT, int D, bool CAUSAL>
 hipError_t launch_t(const Plan& pl, long long nwg, const Params& p, hipStream_t st) {
-  dim3 grid((unsigned)nwg), block(pl.nw * 64);
+  const dim3 grid((unsigned)nwg), block(pl.ng * pl.nw * 64);
   // the tile buffers are static LDS (pl.lds_bytes reports their size)
-  hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 4>), grid, block, 0, st, p);
+  if constexpr (D <= 128) {
+    if (pl.ng == 2) {
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 2>), grid, block, 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
@@ -1234,9 +1327,14 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
   attn_status st = attn_fwd_check(pp, pp, pp, (void*)pp, nullptr, B, Sq, Sk, Hq,
                                   Hkv, d, 1.0f, causal, dtype);
   if (st != ATTN_OK) return st;
-  const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
-  int vals[10] = {pl.grid, pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
-                  pl.lds_bytes, pl.xcd_cols > 0 || pl.xcd_qsplit > 0 ? 1 : 0, pl.pipelined, 0};
+  Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
+  // attn_fwd: no key split; the last row block is the longest
+  const int nmax = block_tiles((pl.qtiles - 1) * pl.rows_wg, pl.rows_wg, Sq, Sk, Sk - Sq,
+                               causal != 0);
+  pl.ng = two_groups(pl.grid, d, nmax) ? 2 : 1;
+  int vals[10] = {pl.grid, pl.ng * pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
+                  pl.ng * pl.lds_bytes, pl.xcd_cols > 0 || pl.xcd_qsplit > 0 ? 1 : 0,
+                  pl.pipelined, 0};
   if (decode_eligible(Sq, Hq, Hkv, d)) {
     // the decode kernel, unsplit: a workgroup per (batch, kv head) with all
     // g * Sq rows in one wave, DEC_WAVES waves over the keys
@@ -1271,17 +1369,17 @@ attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, i
     if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
     const long long mrows = (long long)B * Sq * Hq;
     const int rpb = 256 / (padded_head(d) / 4);
-    const int vals[5] = {(int)dp.grid, dp.pieces, dp.pieces > 1 ? dp.piece_tiles * 32 : 0,
+    const int vals[6] = {(int)dp.grid, dp.pieces, dp.pieces > 1 ? dp.piece_tiles * 32 : 0,
                          dp.pieces > 1 ? 0 : Sq,
-                         dp.pieces > 1 ? (int)((mrows + rpb - 1) / rpb) : 0};
-    for (int i = 0; i < n && i < 5; ++i) out[i] = vals[i];
+                         dp.pieces > 1 ? (int)((mrows + rpb - 1) / rpb) : 0, DEC_WAVES * 64};
+    for (int i = 0; i < n && i < 6; ++i) out[i] = vals[i];
     return ATTN_OK;
   }
   const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, Sk - Sq);
   if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
-  const int vals[5] = {(int)sp.grid, sp.npieces, sp.chunk * BC, sp.q_first,
-                       (int)sp.merge_grid};
-  for (int i = 0; i < n && i < 5; ++i) out[i] = vals[i];
+  const int vals[6] = {(int)sp.grid, sp.npieces, sp.chunk * BC, sp.q_first,
+                       (int)sp.merge_grid, sp.base.ng * sp.base.nw * 64};
+  for (int i = 0; i < n && i < 6; ++i) out[i] = vals[i];
   return ATTN_OK;
 }
 

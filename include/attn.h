@@ -284,11 +284,13 @@ attn_status attn_fwd_split_workspace(int B, int Sq, int Sk, int Hq, int Hkv,
 
 /*
  * attn_fwd_split_plan -- the launches attn_fwd_split would make, without any
- * device call.  Writes up to n (at most 5) ints into `out`:
+ * device call.  Writes up to n (at most 6) ints into `out`:
  *   [0] attention workgroups     [1] pieces of the longest query block
  *   [2] keys per piece (0 = no split)
  *   [3] first query row of a split block (Sq when nothing is split)
  *   [4] merge workgroups (0 when nothing is split)
+ *   [5] threads per attention workgroup (512: two 4-wave groups that take
+ *       alternate key tiles of the same rows, as attn_fwd_plan [1])
  */
 attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
                                 int causal, int dtype, int kv_split, int* out,

@@ -109,7 +109,8 @@ def test_padded_head_sizes_pass_validation(d):
     assert _check(d=d) == ATTN_OK
     D = next(x for x in (32, 64, 96, 128, 192, 256) if x >= d)
     plan = binding.attn_fwd_plan(2, 1000, 1000, 8, 2, d, 1, ATTN_DTYPE_BF16)
-    assert plan["lds_bytes"] == 4 * 64 * D * 2
+    groups = plan["threads"] // 256
+    assert plan["lds_bytes"] == groups * 4 * 64 * D * 2
     # the split path's workspace holds rows of the padded size
     n = binding.attn_fwd_split_workspace(1, 300, 2000, 8, 2, d, 1, ATTN_DTYPE_BF16, kv_split=4)
     m = binding.attn_fwd_split_workspace(1, 300, 2000, 8, 2, D, 1, ATTN_DTYPE_BF16, kv_split=4)
@@ -649,3 +650,24 @@ def test_noalloc_refuses_a_split_beyond_the_scratch_before_any_device_call():
     assert lib.attn_fwd_split_noalloc(A, A, A, A, None, 1, 64, 64, 4, 4, 64,
                                       ctypes.c_float(0.1), 1, ATTN_DTYPE_BF16, -1,
                                       None) == ATTN_ERR_INVALID_ARG
+
+
+def test_two_group_workgroups_for_grids_of_at_most_one_per_cu():
+    """Up to 256 workgroups with work (one per CU), padded head sizes up to
+    128 and at least 8 key tiles in the longest workgroup take two 4-wave
+    groups per workgroup (512 threads, twice the tile LDS); larger grids and
+    head sizes, and short rows, take one."""
+    _lib()
+    two = binding.attn_fwd_plan(2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16)   # 256 blocks
+    assert two["grid"] == 256 and two["threads"] == 512
+    assert two["lds_bytes"] == 2 * 4 * 64 * 128 * 2 <= 160 * 1024
+    # 8 tiles of 64 keys in every block (non-causal 512 keys): two groups;
+    # 7 tiles (448 keys) or a causal block of 4 (256 keys): one
+    assert binding.attn_fwd_plan(1, 512, 512, 8, 8, 64, 0, ATTN_DTYPE_F16)["threads"] == 512
+    assert binding.attn_fwd_plan(1, 512, 448, 8, 8, 64, 0, ATTN_DTYPE_F16)["threads"] == 256
+    assert binding.attn_fwd_plan(1, 256, 256, 16, 16, 128, 1, ATTN_DTYPE_F16)["threads"] == 256
+    assert binding.attn_fwd_plan(1, 128, 128, 2, 2, 64, 1, ATTN_DTYPE_F16)["threads"] == 256
+    one = binding.attn_fwd_plan(1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16)   # 2048 blocks
+    assert one["threads"] == 256 and one["lds_bytes"] == 4 * 64 * 128 * 2
+    big_d = binding.attn_fwd_plan(1, 1000, 1000, 8, 2, 160, 1, ATTN_DTYPE_BF16)
+    assert big_d["threads"] == 256
