@@ -41,9 +41,9 @@ PEAK_HBM_GBS = 8000.0
 # set on (the 8K one runs with --workload gqa4_causal_bf16_b1_hq32_hkv8_s8192_d128)
 DEFAULT_WORKLOAD = "gqa8_causal_outlier_bf16_b1_hq32_hkv4_s16384_d128"
 # untimed warmup: at least --warmup steps and at least this many seconds of
-# back-to-back steps, so that the board's power management has settled the
-# clock before the timed steps (the first tens of milliseconds of a burst run
-# at a dipped clock)
+# back-to-back steps (--min-warmup-s), so that the board's power management
+# has settled the clock before the timed steps (the first tens of milliseconds
+# of a burst run at a dipped clock)
 MIN_WARMUP_S = 1.0
 
 
@@ -189,6 +189,10 @@ def main():
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
                     help="decode workloads: time attn_decode_paged with K and V in a "
                          "shuffled pool of BLOCK-token blocks (every sequence Sk long)")
+    ap.add_argument("--min-warmup-s", type=float, default=MIN_WARMUP_S, metavar="S",
+                    help="untimed warmup lasts at least S seconds as well as --warmup steps "
+                         "(default 1.0; 0 under counter collection, where every warmup "
+                         "dispatch is recorded and the clock does not matter)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a device copy of MIB MiB --steps times "
@@ -264,7 +268,7 @@ def main():
 
     t_w = time.perf_counter()
     n_warm = 0
-    while n_warm < args.warmup or time.perf_counter() - t_w < MIN_WARMUP_S:
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         step()
         n_warm += 1
         if n_warm % 8 == 0:
