@@ -3,6 +3,10 @@
 The library is built with hipcc straight from ``csrc/*.hip``; it exports the
 C ABI declared in ``include/attn.h``.  All HIP code is compiled with packed
 fp32 arithmetic disabled (``-packed-fp32-ops``).
+
+    python -m exact_attention_19_amd.build                # libattn.so in the package
+    python -m exact_attention_19_amd.build --sanitize     # host ASan/UBSan, _build/sanitize/
+    python -m exact_attention_19_amd.build --poison-lds   # LDS poisoned with NaN, libattn_poison.so
 """
 from __future__ import annotations
 
@@ -37,28 +41,40 @@ HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsa
                        "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
 
 
-def build_command(out: str, src: str | None = None, sanitize: bool = False) -> list[str]:
+# LDS-poison debug build (GPU checks): every kernel fills its LDS with NaN
+# bytes before use, so a read of LDS before the kernel wrote it shows up as
+# NaN in parity.  The result goes to POISON_LIB (beside LIB, so that it
+# travels with the package), never over LIB.
+POISON_LIB = os.path.join(os.path.dirname(LIB), "libattn_poison.so")
+
+
+def build_command(out: str, src: str | None = None, sanitize: bool = False,
+                  poison: bool = False) -> list[str]:
     """hipcc for one source (-c, to an object) or, src None, all of them into a
     shared library."""
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE]
     if sanitize:
         cmd += HOST_SANITIZE_FLAGS
+    if poison:
+        cmd += ["-DATTN_POISON_LDS"]
     if src is not None:
         return cmd + ["-c", src, "-o", out]
     return cmd + ["-shared", *SOURCES, "-o", out]
 
 
-def build_library(verbose: bool = False, sanitize: bool = False) -> str:
+def build_library(verbose: bool = False, sanitize: bool = False, poison: bool = False) -> str:
     """Compile every HIP source into libattn.so (always recompiles).  The
     sources are compiled in parallel, then linked."""
-    lib = SANITIZE_LIB if sanitize else LIB
+    if sanitize and poison:
+        raise ValueError("the sanitizer and LDS-poison builds are separate")
+    lib = SANITIZE_LIB if sanitize else POISON_LIB if poison else LIB
     os.makedirs(os.path.dirname(lib), exist_ok=True)
     tmp = lib + ".tmp"
     objs = [tmp + "." + os.path.basename(s) + ".o" for s in SOURCES]
     procs = []
     for s, o in zip(SOURCES, objs):
-        cmd = build_command(o, s, sanitize)
+        cmd = build_command(o, s, sanitize, poison)
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
@@ -90,4 +106,5 @@ def build_library(verbose: bool = False, sanitize: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build_library(verbose=True, sanitize="--sanitize" in sys.argv))
+    print(build_library(verbose=True, sanitize="--sanitize" in sys.argv,
+                        poison="--poison-lds" in sys.argv))

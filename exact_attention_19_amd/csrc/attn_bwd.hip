@@ -117,6 +117,11 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
   constexpr int KK = D / 16;
   constexpr int TB = 64 * D * 2;
   __shared__ __attribute__((aligned(1024))) char lds_k0[TB], lds_k1[TB], lds_v0[TB], lds_v1[TB];
+  ATTN_POISON_LDS_ARRAY(lds_k0);
+  ATTN_POISON_LDS_ARRAY(lds_k1);
+  ATTN_POISON_LDS_ARRAY(lds_v0);
+  ATTN_POISON_LDS_ARRAY(lds_v1);
+  ATTN_POISON_LDS_DONE();
   auto kbuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_k1 : (LDS_PTR(char))lds_k0; };
   auto vbuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_v1 : (LDS_PTR(char))lds_v0; };
 
@@ -319,6 +324,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char lds_q0[TB], lds_q1[TB], lds_o0[TB], lds_o1[TB];
   __shared__ __attribute__((aligned(1024))) char lds_k[2][TB], lds_v[2][TB];
   __shared__ __attribute__((aligned(256))) float lds_l2[2][64], lds_d[2][64];
+  ATTN_POISON_LDS_ARRAY(lds_q0);
+  ATTN_POISON_LDS_ARRAY(lds_q1);
+  ATTN_POISON_LDS_ARRAY(lds_o0);
+  ATTN_POISON_LDS_ARRAY(lds_o1);
+  ATTN_POISON_LDS_ARRAY(lds_k);
+  ATTN_POISON_LDS_ARRAY(lds_v);
+  ATTN_POISON_LDS_ARRAY(lds_l2);
+  ATTN_POISON_LDS_ARRAY(lds_d);
+  ATTN_POISON_LDS_DONE();
   // a wave's dK (or dV) partial sums, CB x 16 floats per lane, fill exactly
   // one tile buffer
   static_assert(CB * 16 * 64 * 4 == TB, "reduction area = tile area");

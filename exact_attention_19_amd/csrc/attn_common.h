@@ -69,6 +69,25 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
+
+// LDS poison (debug builds, -DATTN_POISON_LDS): every kernel starts by filling
+// each of its LDS arrays with 0xFF bytes, a NaN in fp32, fp16 and bf16 alike,
+// so that a read of LDS the kernel has not written first shows up as NaN in
+// its outputs.  Product builds compile it away.  Four-byte stores: every LDS
+// array is a whole number of words, whatever its alignment.
+#ifdef ATTN_POISON_LDS
+template <int BYTES>
+__device__ __forceinline__ void poison_lds(LDS_PTR(char) p) {
+  static_assert(BYTES % 4 == 0, "LDS arrays are whole words");
+  for (int i = (int)threadIdx.x * 4; i < BYTES; i += (int)blockDim.x * 4)
+    *(LDS_PTR(unsigned))(p + i) = ~0u;
+}
+#define ATTN_POISON_LDS_ARRAY(a) poison_lds<sizeof(a)>((LDS_PTR(char))(a))
+#define ATTN_POISON_LDS_DONE() __syncthreads()
+#else
+#define ATTN_POISON_LDS_ARRAY(a) ((void)0)
+#define ATTN_POISON_LDS_DONE() ((void)0)
+#endif
 #define GLOBAL_PTR(T) __attribute__((address_space(1))) T*
 
 constexpr int BC = 64;              // keys per K/V tile

@@ -48,6 +48,11 @@ __global__ __launch_bounds__(DEC_WAVES * 64, D > 128 ? 1 : 8 / DEC_WAVES) void a
   // rows x D floats = exactly the same size)
   __shared__ __attribute__((aligned(1024))) char lds_v[NW][2][VTB];
   __shared__ float lds_m[NW][32], lds_lr[NW][32], lds_lf[NW][32];
+  ATTN_POISON_LDS_ARRAY(lds_v);
+  ATTN_POISON_LDS_ARRAY(lds_m);
+  ATTN_POISON_LDS_ARRAY(lds_lr);
+  ATTN_POISON_LDS_ARRAY(lds_lf);
+  ATTN_POISON_LDS_DONE();
   static_assert(NW * 2 * VTB == NW * 32 * D * 4, "merge area = tile area");
 
   const int tid = threadIdx.x;

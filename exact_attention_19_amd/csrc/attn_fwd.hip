@@ -165,6 +165,11 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   // (one set per group)
   __shared__ __attribute__((aligned(1024))) char lds_k0[NG][TB], lds_k1[NG][TB], lds_v0[NG][TB],
       lds_v1[NG][TB];
+  ATTN_POISON_LDS_ARRAY(lds_k0);
+  ATTN_POISON_LDS_ARRAY(lds_k1);
+  ATTN_POISON_LDS_ARRAY(lds_v0);
+  ATTN_POISON_LDS_ARRAY(lds_v1);
+  ATTN_POISON_LDS_DONE();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -610,6 +615,7 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
     // small array.  Group 0 combines: m = max(m0, m1), a_g = 2^(m_g - m),
     // O = a0 O0 + a1 O1, l = a0 l0 + a1 l1.
     __shared__ float lds_state[4][3][64];
+    ATTN_POISON_LDS_ARRAY(lds_state);  // before the barrier below
     __syncthreads();
     LDS_PTR(char) const mbuf = wave == 0   ? (LDS_PTR(char))lds_k0[NG - 1]
                                : wave == 1 ? (LDS_PTR(char))lds_k1[NG - 1]

@@ -14,12 +14,11 @@ value is so large that its own rounding exceeds half of it; LSE within 1e-3).
 """
 import math
 
-import numpy as np
 import pytest
 import torch
 
 from exact_attention_19_amd.workloads import Workload, make_inputs
-from parity_common import TOL_LSE, _check_full, _say
+from parity_common import _check_full, _say
 
 pytestmark = pytest.mark.gpu
 
@@ -94,3 +93,28 @@ def test_two_groups_short_rows_take_one_group():
     o, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=causal)
     torch.cuda.synchronize()
     _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+
+
+@pytest.mark.parametrize("d", [128, 72])
+def test_two_groups_no_writes_outside_outputs(d):
+    """Canaries around O and LSE stay untouched, and every O element and LSE
+    entry between them is written.  At d = 72 (run on the 96-column kernel)
+    O is dense with 72 columns, so a column past d written by mistake would
+    land on the next row or on a canary."""
+    from exact_attention_19_amd import attn_fwd
+    from exact_attention_19_amd.binding import attn_fwd_plan
+    w = Workload(f"ng2_canary_d{d}", 1, 8, 2, 333, 700, d, "bf16", True, 1.0 / math.sqrt(d))
+    assert attn_fwd_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, d, 1, _code("bf16"))["threads"] == 512
+    q, k, v = (t.cuda() for t in make_inputs(w, seed=11))
+    n_o = w.B * w.Sq * w.Hq * w.d
+    pad = 4096
+    obuf = torch.full((n_o + 2 * pad,), 1234.0, dtype=torch.bfloat16, device="cuda")
+    n_l = w.B * w.Hq * w.Sq
+    lbuf = torch.full((n_l + 2 * pad,), 777.0, dtype=torch.float32, device="cuda")
+    o = obuf[pad:pad + n_o].view(w.B, w.Sq, w.Hq, w.d)
+    lse = lbuf[pad:pad + n_l].view(w.B, w.Hq, w.Sq)
+    attn_fwd(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:pad] == 1234.0) and torch.all(obuf[pad + n_o:] == 1234.0)
+    assert torch.all(lbuf[:pad] == 777.0) and torch.all(lbuf[pad + n_l:] == 777.0)
+    assert torch.all(lse != 777.0) and torch.all(o != 1234.0)
