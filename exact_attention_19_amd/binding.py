@@ -50,8 +50,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     import torch  # noqa: F401
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m exact_attention_19_amd.build` "
-            "(or __graft_entry__.build()); there is no fallback implementation")
+            f"{path} is missing: build it with `python -m exact_attention_19_amd.build`; "
+            "there is no fallback implementation")
     lib = ctypes.CDLL(path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.restype = i

@@ -70,7 +70,8 @@ def _load():
 
 def default_threads() -> int:
     """Threads for the oracle: the CPUs this process may run on, at most 16
-    (a GPU machine gives one GPU's jobs a 16-CPU share whatever it reports)."""
+    (a machine shared by several GPUs' jobs may give each a 16-CPU share
+    whatever the affinity mask reports)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
