@@ -16,7 +16,7 @@ Prints ONE JSON line:
                 of rows of the same workload (a baseline, not a target)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--kv-split N]
+                       [--kv-split N] [--backward] [--head-size D]
 """
 from __future__ import annotations
 
@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -195,6 +196,9 @@ def main():
                     help="untimed warmup lasts at least S seconds as well as --warmup steps "
                          "(default 1.0; 0 under counter collection, where every warmup "
                          "dispatch is recorded and the clock does not matter)")
+    ap.add_argument("--head-size", type=int, default=0, metavar="D",
+                    help="run the named workload with head size D (scale 1/sqrt(D)); "
+                         "the workload's name then ends in _dD")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a device copy of MIB MiB --steps times "
@@ -219,6 +223,9 @@ def main():
 
     load_library()
     w = WORKLOADS[args.workload]
+    if args.head_size:
+        hd = args.head_size
+        w = w.with_(name=re.sub(r"_d\d+$", f"_d{hd}", w.name), d=hd, scale=1.0 / math.sqrt(hd))
     dev = torch.device("cuda:0")
     q_cpu, k_cpu, v_cpu = make_inputs(w, seed=0)
     digest = input_digest(q_cpu, k_cpu, v_cpu)

@@ -315,15 +315,26 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
 // the keys, for every query head of the kv head's group; tile t sits in LDS
 // buffer t & 1 (Q and dO double-buffered, with the rows' lse * log2(e) and
 // D).
+//
+// Head sizes above 128: two key groups (64 keys, 4 waves, one per SIMD) so
+// that a wave has the registers for its 2 x (D / 32) x 16 dK/dV sums, and at
+// 256 one Q/dO buffer (K and V of 64 keys plus two Q/dO buffers would take
+// 192 KiB of the CU's 160): the next tile is then loaded after the current
+// one has been used, behind a second barrier.
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(D > 128 ? 256 : 512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   using T = Ty<DT>;
   constexpr int CB = D / 32;
   constexpr int KK = D / 16;
   constexpr int TB = 64 * D * 2;
-  __shared__ __attribute__((aligned(1024))) char lds_q0[TB], lds_q1[TB], lds_o0[TB], lds_o1[TB];
-  __shared__ __attribute__((aligned(1024))) char lds_k[2][TB], lds_v[2][TB];
-  __shared__ __attribute__((aligned(256))) float lds_l2[2][64], lds_d[2][64];
+  constexpr int KG = D > 128 ? 2 : 4;  // key groups of 32 keys
+  constexpr int KT = KG / 2;           // 64-key tiles of K (and of V)
+  constexpr int NB = D > 192 ? 1 : 2;  // Q/dO tile buffers
+  constexpr int VW = 4 / KG;           // 16-row load slices per wave of a 64-row tile
+  __shared__ __attribute__((aligned(1024))) char lds_q0[TB], lds_q1[NB > 1 ? TB : 16],
+      lds_o0[TB], lds_o1[NB > 1 ? TB : 16];
+  __shared__ __attribute__((aligned(1024))) char lds_k[KT][TB], lds_v[KT][TB];
+  __shared__ __attribute__((aligned(256))) float lds_l2[NB][64], lds_d[NB][64];
   ATTN_POISON_LDS_ARRAY(lds_q0);
   ATTN_POISON_LDS_ARRAY(lds_q1);
   ATTN_POISON_LDS_ARRAY(lds_o0);
@@ -336,14 +347,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   // a wave's dK (or dV) partial sums, CB x 16 floats per lane, fill exactly
   // one tile buffer
   static_assert(CB * 16 * 64 * 4 == TB, "reduction area = tile area");
-  auto qbuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_q1 : (LDS_PTR(char))lds_q0; };
-  auto obuf = [&](int n) { return (n & 1) ? (LDS_PTR(char))lds_o1 : (LDS_PTR(char))lds_o0; };
+  auto qbuf = [&](int n) {
+    return (NB > 1 && (n & 1)) ? (LDS_PTR(char))lds_q1 : (LDS_PTR(char))lds_q0;
+  };
+  auto obuf = [&](int n) {
+    return (NB > 1 && (n & 1)) ? (LDS_PTR(char))lds_o1 : (LDS_PTR(char))lds_o0;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kg = wave & 3;   // key group
-  const int qh = wave >> 2;  // row half of each query tile
+  const int kg = wave % KG;  // key group
+  const int qh = wave / KG;  // row half of each query tile
+  // a 64-row tile loaded by the KG waves of one row half: each takes VW of
+  // the four 16-row slices of the shared tile loader
+  auto load64 = [&](const char* slice, uint32_t row_bytes, int n, int nrows, LDS_PTR(char) dst) {
+#pragma unroll
+    for (int s = 0; s < VW; ++s) load_tile<D>(slice, row_bytes, n, nrows, p.d, dst, kg * VW + s, lane);
+  };
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -353,24 +374,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int col = blockIdx.x % ncol;
   const int b = col / p.Hkv;
   const int kvh = col % p.Hkv;
-  const int k0 = kblk * 128;
+  const int k0 = kblk * 32 * KG;
   const int kj = k0 + kg * 32 + l32;  // this lane's key
   const bool kok = kj < p.Sk;
 
-  // K rows (waves 0-3) and V rows (waves 4-7) of the 128 keys into LDS, as
-  // two 64-row tiles each; a tile wholly past Sk is zeroed instead
+  // K rows (row half 0) and V rows (row half 1) of the block's 32 * KG keys
+  // into LDS, as KT 64-row tiles each; a tile wholly past Sk is zeroed instead
   {
     const uint32_t rbk = (uint32_t)p.Hkv * p.d * 2;
     const char* slice =
         (const char*)((qh == 0 ? p.k : p.v) + ((int64_t)b * p.Sk * p.Hkv + kvh) * p.d);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < KT; ++i) {
       LDS_PTR(char) const dst = (LDS_PTR(char))(qh == 0 ? lds_k[i] : lds_v[i]);
       if (k0 + 64 * i < p.Sk) {
-        load_tile<D>(slice, rbk, 2 * kblk + i, p.Sk, p.d, dst, kg, lane);
+        load64(slice, rbk, KT * kblk + i, p.Sk, dst);
       } else {
         LDS_PTR(u32x4) z = (LDS_PTR(u32x4))dst;
-        for (int e = kg * 64 + lane; e < TB / 16; e += 256) z[e] = (u32x4){0u, 0u, 0u, 0u};
+        for (int e = kg * 64 + lane; e < TB / 16; e += KG * 64) z[e] = (u32x4){0u, 0u, 0u, 0u};
       }
     }
   }
@@ -386,9 +407,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int steps = per_head * p.group;
   const uint32_t rbq = (uint32_t)p.Hq * p.d * 2;
 
-  // tile t: Q by waves 0-3, dO by waves 4-7, and the 64 rows' lse * log2(e)
-  // (wave 0) and D (wave 4), rows clamped to Sq - 1 (rows past Sq are
-  // masked below)
+  // tile t: Q by row half 0's waves, dO by row half 1's, and the 64 rows'
+  // lse * log2(e) and D (the first wave of each), rows clamped to Sq - 1
+  // (rows past Sq are masked below)
   // walk position of the next tile to load: query head kvh * group + nh,
   // tile qt0 + nq (counters, not divisions: the scalar unit is busy enough)
   int nh = 0, nq = 0;
@@ -396,15 +417,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     const int h = kvh * p.group + nh;
     const int qt = qt0 + nq;
     const int64_t head0 = (int64_t)b * p.Sq * p.Hq + h;
-    load_tile<D>((const char*)((qh == 0 ? p.q : p.dout) + head0 * p.d), rbq, qt, p.Sq, p.d,
-                 qh == 0 ? qbuf(t) : obuf(t), kg, lane);
+    load64((const char*)((qh == 0 ? p.q : p.dout) + head0 * p.d), rbq, qt, p.Sq,
+           qh == 0 ? qbuf(t) : obuf(t));
     if (kg == 0) {
       const float* src = (qh == 0 ? p.l2 : p.dvec) + ((int64_t)b * p.Hq + h) * p.Sq;
       const uint32_t r = (uint32_t)min(qt * 64 + lane, p.Sq - 1);
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, p.Sq * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (LDS_PTR(void))(qh == 0 ? &lds_l2[t & 1][0] : &lds_d[t & 1][0]), 4, r * 4, 0, 0, 0);
+          rs, (LDS_PTR(void))(qh == 0 ? &lds_l2[t % NB][0] : &lds_d[t % NB][0]), 4, r * 4, 0,
+          0, 0);
     }
   };
 
@@ -431,27 +453,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       adv[cb][r] = 0.f;
     }
 
-  if (steps > 0) issue(0);
-  int cq = 0;  // tile index within its head of the tile being computed
-  for (int t = 0; t < steps; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < steps) {
-      if (++nq == per_head) {
-        nq = 0;
-        ++nh;
-      }
-      issue(t + 1);
+  // the next tile's loads: into the other buffer while this tile is
+  // computed (two buffers), or after every wave is done with the one buffer
+  auto next = [&](int t) {
+    if (++nq == per_head) {
+      nq = 0;
+      ++nh;
     }
-    const int qt = qt0 + cq;
-    if (++cq == per_head) cq = 0;
+    issue(t + 1);
+  };
+  // tile t's contributions of the wave's 32 query rows to its 32 keys
+  auto body = [&](int t, int qt) {
     const int i0 = qt * 64 + 32 * qh;  // first query row of this wave
     // rows that see none of the wave's keys, or lie past Sq: nothing to add
-    if (i0 >= p.Sq || (CAUSAL && i0 + 31 + p.off < k0 + 32 * kg)) continue;
+    if (i0 >= p.Sq || (CAUSAL && i0 + 31 + p.off < k0 + 32 * kg)) return;
     LDS_PTR(char) const qtile = qbuf(t);
     LDS_PTR(char) const otile = obuf(t);
-    LDS_PTR(const float) const l2t = (LDS_PTR(const float)) & lds_l2[t & 1][0];
-    LDS_PTR(const float) const dtt = (LDS_PTR(const float)) & lds_d[t & 1][0];
+    LDS_PTR(const float) const l2t = (LDS_PTR(const float)) & lds_l2[t % NB][0];
+    LDS_PTR(const float) const dtt = (LDS_PTR(const float)) & lds_d[t % NB][0];
     // rows need masking: a causal row that does not see every key of the
     // wave, or a row past Sq
     const int kmax = k0 + 32 * kg + 31;
@@ -547,18 +566,32 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
         adk[(st + 1) % CB] = T::mfma(fb[1], dsf[(st + 1) / CB], adk[(st + 1) % CB]);
       }
     }
+  };
+
+  if (steps > 0) issue(0);
+  int cq = 0;  // tile index within its head of the tile being computed
+  for (int t = 0; t < steps; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (NB > 1 && t + 1 < steps) next(t);
+    body(t, qt0 + cq);
+    if (++cq == per_head) cq = 0;
+    if (NB == 1 && t + 1 < steps) {
+      __syncthreads();
+      next(t);
+    }
   }
 
-  // add the row halves: waves 4-7 hand their sums to waves 0-3 through LDS
-  // (dK into the K/V area, dV into the Q/dO area; lane-contiguous 16-byte
-  // slots)
+  // add the row halves: the waves of row half 1 hand their sums to those of
+  // row half 0 through LDS (dK into the K/V area, dV into the Q/dO area;
+  // lane-contiguous 16-byte slots; KG = 2 leaves one K and one V tile, so
+  // dK goes to K (key group 0) or V (key group 1), and dV to Q or dO)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  LDS_PTR(char) const red_k = (LDS_PTR(char))(kg < 2 ? lds_k[kg] : lds_v[kg - 2]);
-  LDS_PTR(char) const red_v = kg == 0   ? (LDS_PTR(char))lds_q0
-                              : kg == 1 ? (LDS_PTR(char))lds_q1
-                              : kg == 2 ? (LDS_PTR(char))lds_o0
-                                        : (LDS_PTR(char))lds_o1;
+  LDS_PTR(char) const red_k = (LDS_PTR(char))(kg < KT ? lds_k[kg % KT] : lds_v[kg % KT]);
+  LDS_PTR(char) const red_v = kg < KT    ? (kg == 0 ? (LDS_PTR(char))lds_q0 : (LDS_PTR(char))lds_q1)
+                              : kg == KT ? (LDS_PTR(char))lds_o0
+                                         : (LDS_PTR(char))lds_o1;
   if (qh == 1) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
@@ -620,9 +653,8 @@ attn_status validate_bwd(const void* q, const void* k, const void* v, const void
     return ATTN_ERR_INVALID_ARG;
   if (((uintptr_t)lse) & 3u) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
-  // any multiple of 8 up to 128, padded to 32, 64, 96 or 128 (d above 128
-  // would need 256 registers of dK/dV sums per wave alone)
-  if (!head_size_ok(d) || d > 128) return ATTN_ERR_UNSUPPORTED;
+  // any multiple of 8 up to 256, padded to 32, 64, 96, 128, 192 or 256
+  if (!head_size_ok(d)) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)Sq + Sk >= (1ll << 30)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)Hq * d * 2 * 64 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * Sq * Hq >= (1ll << 31) || (int64_t)B * Sk * Hkv >= (1ll << 31))
@@ -644,9 +676,11 @@ hipError_t launch_bwd_t(const Plan& pl, const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((attn_bwd_prep_kernel<DT, D>), dim3((unsigned)((rows + 31) / 32)), dim3(256),
                      0, st, p);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3(pl.grid), dim3(256), 0, st, p);
-  const long long kgrid = (long long)p.B * p.Hkv * ((p.Sk + 127) / 128);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)kgrid), dim3(512), 0,
-                     st, p);
+  // 32 keys per key group: 4 groups (512 threads) up to d = 128, 2 above
+  constexpr int KG = D > 128 ? 2 : 4;
+  const long long kgrid = (long long)p.B * p.Hkv * ((p.Sk + 32 * KG - 1) / (32 * KG));
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)kgrid),
+                     dim3(2 * KG * 64), 0, st, p);
   return hipGetLastError();
 }
 
@@ -661,7 +695,9 @@ hipError_t launch_bwd_d(int d, bool causal, const Plan& pl, const BwdParams& p, 
     case 32: return launch_bwd_c<DT, 32>(causal, pl, p, st);
     case 64: return launch_bwd_c<DT, 64>(causal, pl, p, st);
     case 96: return launch_bwd_c<DT, 96>(causal, pl, p, st);
-    default: return launch_bwd_c<DT, 128>(causal, pl, p, st);
+    case 128: return launch_bwd_c<DT, 128>(causal, pl, p, st);
+    case 192: return launch_bwd_c<DT, 192>(causal, pl, p, st);
+    default: return launch_bwd_c<DT, 256>(causal, pl, p, st);
   }
 }
 

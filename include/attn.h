@@ -352,8 +352,9 @@ attn_status attn_merge_check(const void* o_parts, const float* lse_parts,
  *   dout              dO, (B, Sq, Hq, d), the dtype of q
  *   dq                (B, Sq, Hq, d); written
  *   dk, dv            (B, Sk, Hkv, d); written
- *   B ... dtype       as for attn_fwd; d a multiple of 8 up to 128 (padded
- *                     to 32, 64, 96 or 128 inside the loads, as the forward)
+ *   B ... dtype       as for attn_fwd; d a multiple of 8 up to 256 (padded
+ *                     to 32, 64, 96, 128, 192 or 256 inside the loads, as
+ *                     the forward)
  *   workspace         device pointer, 256-byte aligned, of at least
  *                     attn_bwd_workspace bytes (two fp32 values per query row)
  *   stream            as for attn_fwd; three kernels are queued on it

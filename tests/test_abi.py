@@ -368,9 +368,10 @@ def test_bwd_validation():
             assert _bcheck(p) == ATTN_ERR_INVALID_ARG, i
     for over in (dict(Hq=7), dict(B=0), dict(Sk=0), dict(scale=0.0), dict(causal=3)):
         assert _bcheck(**over) == ATTN_ERR_INVALID_ARG, over
-    for over in (dict(d=84), dict(d=136), dict(d=256), dict(dtype=2)):
+    for over in (dict(d=84), dict(d=4), dict(d=264), dict(d=260), dict(dtype=2)):
         assert _bcheck(**over) == ATTN_ERR_UNSUPPORTED, over
-    for over in (dict(d=32), dict(d=96), dict(d=8), dict(d=40), dict(d=80), dict(d=120)):
+    for over in (dict(d=32), dict(d=96), dict(d=8), dict(d=40), dict(d=80), dict(d=120),
+                 dict(d=136), dict(d=192), dict(d=200), dict(d=256)):
         assert _bcheck(**over) == ATTN_OK, over
 
 

@@ -296,3 +296,57 @@ def test_bwd_padded_head_sizes(w):
     """Head sizes that are multiples of 8 but not of 32 run on the kernels of
     the next built size: columns past d load as zeros and are not stored."""
     _check(w, *_run(w))
+
+
+@pytest.mark.parametrize("w", [
+    Workload("bwd_d192_causal_off_bf16", 1, 8, 2, 200, 333, 192, "bf16", True, 1 / math.sqrt(192)),
+    Workload("bwd_d192_gqa_nc_f16", 2, 4, 1, 150, 270, 192, "f16", False, 1 / math.sqrt(192)),
+    Workload("bwd_d256_causal_sq_f16", 2, 4, 4, 257, 257, 256, "f16", True, 1 / math.sqrt(256)),
+    Workload("bwd_d256_causal_off_bf16", 1, 8, 2, 200, 333, 256, "bf16", True, 1 / math.sqrt(256)),
+    Workload("bwd_d256_gqa_nc_bf16", 2, 8, 2, 190, 450, 256, "bf16", False, 1 / math.sqrt(256)),
+    Workload("bwd_pad136_empty_rows_f16", 1, 4, 1, 333, 200, 136, "f16", True, 0.2),
+    Workload("bwd_pad160_causal_off_f16", 1, 8, 2, 200, 333, 160, "f16", True, 1 / math.sqrt(160)),
+    Workload("bwd_pad200_gqa_nc_bf16", 2, 4, 1, 150, 270, 200, "bf16", False, 1 / math.sqrt(200)),
+    Workload("bwd_pad248_causal_bf16", 1, 4, 2, 300, 300, 248, "bf16", True, 1 / math.sqrt(248)),
+    Workload("bwd_d256_one_row_f16", 1, 4, 2, 1, 700, 256, "f16", True, 1 / math.sqrt(256)),
+    Workload("bwd_d192_one_key_bf16", 1, 4, 2, 100, 1, 192, "bf16", False, 0.3),
+], ids=lambda w: w.name)
+def test_bwd_large_head_sizes(w):
+    """Head sizes above 128 run on the 192- and 256-column kernels, whose
+    dK/dV workgroups hold 64 keys in 4 waves (and, at 256, one Q/dO buffer
+    instead of two); d below the built size pads as for the smaller ones.
+    Every case spans several 64-key blocks with a ragged last one."""
+    _check(w, *_run(w))
+
+
+@pytest.mark.parametrize("w", [
+    Workload("bwd_d256_after_fwd_bf16", 1, 8, 2, 200, 333, 256, "bf16", True, 1 / math.sqrt(256)),
+    Workload("bwd_pad200_after_fwd_f16", 1, 4, 4, 257, 257, 200, "f16", True, 1 / math.sqrt(200)),
+], ids=lambda w: w.name)
+def test_bwd_large_head_after_gpu_forward(w):
+    """GPU forward, then GPU backward, at head sizes above 128."""
+    _check(w, *_run(w, fwd="gpu"), stated=True)
+
+
+def test_bwd_large_head_no_writes_outside_outputs():
+    """d = 200 on the 256-column kernels: rows of the gradients are dense
+    with 200 columns, so a column past d written by mistake would land on
+    the next row or on a canary; every element between the canaries is
+    written."""
+    from exact_attention_19_amd import attn_bwd, attn_fwd
+    w = Workload("bwd_canary_d200", 1, 4, 2, 150, 170, 200, "bf16", True, 0.1)
+    q, k, v = (t.cuda() for t in make_inputs(w, seed=7))
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(8)).to(q.dtype).cuda()
+    o, lse = attn_fwd(q, k, v, scale=w.scale, causal=True)
+    pad = 4096
+    bufs = []
+    for ref in (q, k, v):
+        n = ref.numel()
+        buf = torch.full((n + 2 * pad,), 1234.0, dtype=ref.dtype, device="cuda")
+        bufs.append((buf, buf[pad:pad + n].view(ref.shape), n))
+    attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True,
+             dq=bufs[0][1], dk=bufs[1][1], dv=bufs[2][1])
+    torch.cuda.synchronize()
+    for buf, inner, n in bufs:
+        assert torch.all(buf[:pad] == 1234.0) and torch.all(buf[pad + n:] == 1234.0)
+        assert torch.all(inner != 1234.0)
