@@ -131,12 +131,12 @@ def _dtype_code(t, allow_f32: bool = False) -> int:
 
 def attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype_code) -> dict:
     """The launch attn_fwd would make (no device call)."""
-    out = (ctypes.c_int * 10)()
-    st = load_library().attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), dtype_code, out, 10)
+    out = (ctypes.c_int * 11)()
+    st = load_library().attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), dtype_code, out, 11)
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_plan")
     keys = ("grid", "threads", "rows_per_wg", "keys_per_tile", "heads_per_wg",
-            "rows_per_wave", "lds_bytes", "xcd_ordered", "pipelined", "decode")
+            "rows_per_wave", "lds_bytes", "xcd_ordered", "pipelined", "decode", "key_halves")
     return dict(zip(keys, list(out)))
 
 
@@ -150,12 +150,13 @@ def attn_fwd_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Sq, Sk, Hq, Hkv, d,
 
 def attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, dtype_code, kv_split=0) -> dict:
     """The launches attn_fwd_split would make (no device call)."""
-    out = (ctypes.c_int * 6)()
+    out = (ctypes.c_int * 7)()
     st = load_library().attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), dtype_code,
-                                            int(kv_split), out, 6)
+                                            int(kv_split), out, 7)
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_split_plan")
-    keys = ("grid", "pieces", "keys_per_piece", "first_split_row", "merge_grid", "threads")
+    keys = ("grid", "pieces", "keys_per_piece", "first_split_row", "merge_grid", "threads",
+            "key_halves")
     return dict(zip(keys, list(out)))
 
 

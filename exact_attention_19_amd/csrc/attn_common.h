@@ -307,26 +307,30 @@ struct Plan {
                    // xcd_qsplit-th query block of all its head subsets
   int ng;          // groups of nw waves per workgroup walking alternate
                    // K/V tiles of the same rows (1 or 2)
+  int kh;          // 2: the waves are row waves x 2 key halves of each
+                   // tile (nw / 2 row waves per workgroup); else 1
 };
 
 bool sizes_ok(int B, int Sq, int Sk, int Hq, int Hkv) {
   return B >= 1 && Sq >= 1 && Sk >= 1 && Hq >= 1 && Hkv >= 1;
 }
 
-Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal) {
+Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal, int kh = 1) {
   (void)Sk;
   (void)causal;
   Plan pl{};
   pl.nw = 4;
+  pl.kh = kh;
+  const int rwaves = pl.nw / kh;  // waves with rows of their own
   const int group = Hq / Hkv;
   int gh = 1;
-  while (gh * 2 <= pl.nw && group % (gh * 2) == 0) gh *= 2;
+  while (gh * 2 <= rwaves && group % (gh * 2) == 0) gh *= 2;
   pl.gh = gh;
   const int hsub = group / gh;
   pl.ncols = B * Hkv * hsub;
   pl.qb = 1;
   pl.pipelined = 1;
-  pl.rows_wg = (pl.nw / gh) * 32;
+  pl.rows_wg = (rwaves / gh) * 32;
   const long long qt = (Sq + pl.rows_wg - 1) / pl.rows_wg;
   pl.qtiles = qt > 0x7fffffffll ? -1 : (int)qt;
   pl.xcd_cols = (pl.ncols % 8 == 0) ? pl.ncols / 8 : 0;
@@ -364,6 +368,14 @@ constexpr int kTwoGroupMinTiles = 8;
 inline bool two_groups(long long active_workgroups, int d, int max_tiles) {
   return active_workgroups <= kCUCount && padded_head(d) <= 128 &&
          max_tiles >= kTwoGroupMinTiles;
+}
+
+// Key halves instead, for an unsplit launch in the same regime (at most one
+// 4-wave workgroup per CU, at least 8 tiles in the longest block): 64-row
+// workgroups, twice as many, whose two key-half waves per row wave run on
+// different SIMDs, so the longest block's rows spread over two CUs.
+inline bool key_halves(long long workgroups, int d, int max_tiles) {
+  return workgroups <= kCUCount && padded_head(d) <= 128 && max_tiles >= kTwoGroupMinTiles;
 }
 
 using attn_detail::DecodeArgs;

@@ -129,10 +129,10 @@ struct Params {
 // S(j); the rescale of the accumulators by alpha(j) is applied at the END of
 // the iteration, after O has absorbed V(j-1)^T P(j-1), whose probabilities
 // were taken against the previous max.
-template <typename PT>
+template <typename PT, int N>
 struct PFrag {
-  PT hi[BC / 16];
-  PT lo[BC / 16];  // fp16 only (hi + lo split); unused for bf16
+  PT hi[N];
+  PT lo[N];  // fp16 only (hi + lo split); unused for bf16
 };
 
 // NG groups of 4 waves per workgroup.  With NG = 2 (grids of at most one
@@ -142,7 +142,16 @@ struct PFrag {
 // its state (running max, sums, unnormalised O) to group 0 through LDS and
 // group 0 combines the two with the online-softmax rescale (personal-notes
 // page, section "Online Softmax", applied to the two key subsets).
-template <int DT, int D, bool CAUSAL, int NG>
+//
+// KH = 2 (key halves, NG = 1): the 4 waves are 2 row waves x 2 key halves.
+// Both waves of a row wave take the same 32 query rows, one the first and
+// one the second 32-key block of every tile, each with its own online-
+// softmax state, merged through LDS at the end as the two groups are.  A
+// workgroup then holds 64 rows instead of 128 with the same tile buffers,
+// so a launch that would leave most CUs with one workgroup has twice as
+// many workgroups, two per CU, and the snake order below puts a long row
+// block and a short one on each CU.
+template <int DT, int D, bool CAUSAL, int NG, int KH>
 __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fwd_pipe_kernel(
     Params p) {
   using T = Ty<DT>;
@@ -150,10 +159,11 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   constexpr int NT = NW * 64;         // threads per group
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int CPT = BC * CPR / NT;  // direct loads per lane per tile
-  constexpr int KB = BC / 32;
+  constexpr int KB = BC / 32;         // 32-key blocks per tile
+  constexpr int KBW = KB / KH;        // ... per wave
   constexpr int CB = D / 32;
   constexpr int KK = D / 16;
-  constexpr int NP = BC / 16;
+  constexpr int NP = BC / 16 / KH;    // 16-key P fragments per wave
   constexpr int TB = BC * D * 2;      // bytes per K or V tile buffer
   static_assert(CPT * NT == BC * CPR, "tile must split evenly over threads");
   static_assert(CPT == CB, "one load round per 32-column block");
@@ -176,6 +186,9 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR
   const int grp = NG > 1 ? wave_all >> 2 : 0;  // group
   const int wave = wave_all & 3;   // wave within the group
+  static_assert(KH == 1 || (KH == 2 && NG == 1), "key halves run as one group");
+  const int kh = KH > 1 ? (wave & 1) : 0;        // key half of every tile
+  const int rw = KH > 1 ? (wave >> 1) : wave;    // row wave: 32 rows of one head
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   auto kbuf_of = [&](int n) {
@@ -189,7 +202,25 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   // with a key split, all first pieces, then all second pieces, ...
   int qt, col, piece;
   {
-    const int L = blockIdx.x;
+    int L = blockIdx.x;
+    // Snake order (key halves): a grid of two workgroups per CU places
+    // workgroup k + 256 on the CU of workgroup k (k + 32 and k within one
+    // XCD's ids), so every other run of 256 (32 per XCD) is taken in reverse
+    // order of weight: the heaviest block shares its CU with the lightest.
+    // The order only moves work between CUs; any placement gives the same
+    // results.
+    auto snake = [](int k, int n, int s) {
+      const int base = k / s * s;
+      if (!((k / s) & 1)) return k;
+      return base + min(s, n - base) - 1 - (k - base);
+    };
+    if (KH > 1) {
+      const int n = (int)gridDim.x;
+      if (p.xcd_qsplit > 0 || p.xcd_cols > 0)
+        L = (snake(L >> 3, n >> 3, kCUCount / 8) << 3) | (L & 7);
+      else
+        L = snake(L, n, kCUCount);
+    }
     int u;
     if (p.xcd_qsplit > 0) {
       // XCD x: (batch, kv head) x / xcd_qsplit, every head subset, query
@@ -214,8 +245,8 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   const int hs = col % p.hsub;
   const int kvh = (col / p.hsub) % p.Hkv;
   const int b = col / (p.hsub * p.Hkv);
-  const int head_in_wg = wave % p.gh;
-  const int rowblk = wave / p.gh;
+  const int head_in_wg = rw % p.gh;
+  const int rowblk = rw / p.gh;
   const int hq = kvh * p.group + hs * p.gh + head_in_wg;
   const int q0wg = qt * p.rows_wg;
   const int q0w = q0wg + rowblk * 32;
@@ -261,24 +292,26 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   // fill one bank cycle exactly.
   constexpr int BLK = 64 * 64;  // bytes per column block of a tile
   // K fragment (kb, kk): row 32kb + sigma(l32), logical chunk 2kk + hh, i.e.
-  // block kk/2, in-block chunk 2(kk&1) + hh.
+  // block kk/2, in-block chunk 2(kk&1) + hh.  kb counts the wave's own key
+  // blocks, which start at block kh * KBW of the tile.
   uint32_t kbase_lds[2];
   {
-    const int row = sigma(l32);
+    const int row = 32 * KBW * kh + sigma(l32);
     const int sw = (row >> 2) & 3;
 #pragma unroll
     for (int par = 0; par < 2; ++par)
       kbase_lds[par] = (uint32_t)(row * 64 + (((2 * par + hh) ^ sw) << 4));
   }
   // V^T fragment (t, cb, half): transpose read of rows 16t + 8(g16>>1) +
-  // 4half + (s16>>2), columns 32cb + 16(g16&1) + 4(s16&3).
+  // 4half + (s16>>2), columns 32cb + 16(g16&1) + 4(s16&3).  t counts the
+  // wave's own 16-key groups, which start at group kh * NP of the tile.
   uint32_t vbase_lds[2];
   {
     const int g16 = lane >> 4;
     const int s16 = lane & 15;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int row = 8 * (g16 >> 1) + 4 * half + (s16 >> 2);
+      const int row = 16 * NP * kh + 8 * (g16 >> 1) + 4 * half + (s16 >> 2);
       const int cc = 16 * (g16 & 1) + 4 * (s16 & 3);  // column inside the block
       vbase_lds[half] =
           (uint32_t)(row * 64 + ((((cc >> 3) ^ ((row >> 2) & 3))) << 4) + (cc & 7) * 2);
@@ -368,9 +401,9 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
     if (CAUSAL) lim_row = min(lim_row, qi + p.off);
   }
   // S^T = K(kbuf) Q^T
-  auto qk = [&](f32x16 (&S)[KB], LDS_PTR(char) kbuf) {
+  auto qk = [&](f32x16 (&S)[KBW], LDS_PTR(char) kbuf) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KBW; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
 #pragma unroll
@@ -381,7 +414,7 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
     }
   };
   // O^T += V(vbuf)^T P^T
-  auto pv = [&](const PFrag<i16x8>& P, LDS_PTR(char) vbuf) {
+  auto pv = [&](const PFrag<i16x8, NP>& P, LDS_PTR(char) vbuf) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -397,8 +430,8 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
     }
   };
 
-  f32x16 SA[KB], SB[KB];
-  PFrag<i16x8> PA, PB;
+  f32x16 SA[KBW], SB[KBW];
+  PFrag<i16x8, NP> PA, PB;
 #pragma unroll
   for (int t = 0; t < NP; ++t) {
     PB.hi[t] = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
@@ -417,27 +450,32 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   // keeps the steps in order, so LDS reads run ahead of their MFMAs and the
   // vector ALU works beside the matrix core.
   constexpr int NPV = CB * NP;   // O^T += V^T P^T steps (t, cb)
-  constexpr int NQK = KB * KK;   // S^T = K Q^T steps (kb, kk)
+  constexpr int NQK = KBW * KK;  // S^T = K Q^T steps (kb, kk)
   constexpr int NOPS = NPV + NQK;
-  constexpr int NSC = KB * 16;   // scores per lane
+  constexpr int NSC = KBW * 16;  // scores per lane
   constexpr int LA = 3;          // read-ahead, in steps
   // Softmax work per step: the scores of key block 0 of S(j) are spread over
   // the P V steps and those of key block 1 over the first QK steps (those of
   // key block 0 of S(j+1)), so each block of S(j) is dead before the MFMAs
   // of the same block of S(j+1) start and both tiles share one register set.
-  // score_lo(i) is the first score of step i.
+  // With one key block per wave (key halves) S(j) and S(j+1) have registers
+  // of their own, and its scores are spread over the whole step list, QK
+  // steps included.  score_lo(i) is the first score of step i.
+  constexpr int SK = D <= 128 ? 1 : 0;  // softmax skew, in steps
+  // step after the last scores' arguments
+  constexpr int SC_END = KBW > 1 ? NPV + KK : NOPS - 2 * SK;
   auto score_lo = [&](int i) {
+    if (KBW == 1) return i <= SC_END ? 16 * i / SC_END : NSC;
     if (i <= NPV) return 16 * i / NPV;
     if (i <= NPV + KK) return 16 + 16 * (i - NPV) / KK;
     return NSC;
   };
   static_assert(KB == 2, "two 32-key blocks per tile");
-  constexpr int SK = D <= 128 ? 1 : 0;  // softmax skew, in steps
-  static_assert(NPV + KK + 2 * SK <= NOPS, "the skewed softmax ends inside the step list");
+  static_assert(SC_END + 2 * SK <= NOPS, "the skewed softmax ends inside the step list");
 
   // (i: the group's local tile index; j: the tile)
-  auto iter = [&](auto par, int i, f32x16 (&Sc)[KB], f32x16 (&Sn)[KB],
-                  const PFrag<i16x8>& Pp, PFrag<i16x8>& Pc) {
+  auto iter = [&](auto par, int i, f32x16 (&Sc)[KBW], f32x16 (&Sn)[KBW],
+                  const PFrag<i16x8, NP>& Pp, PFrag<i16x8, NP>& Pc) {
     constexpr int PAR = decltype(par)::value;
     const int j = tile_of(i);
     LDS_PTR(char) const K_NEXT = kbuf_of(PAR ^ 1);  // K(j+1)
@@ -450,8 +488,8 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
     // the row max and the max update
     if (j >= n_full || j >= j_hi) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int L = j >= j_hi ? -BC : lim_row - j * BC - kb * 32 - 8 * hh;
+      for (int kb = 0; kb < KBW; ++kb) {
+        const int L = j >= j_hi ? -BC : lim_row - j * BC - (KBW * kh + kb) * 32 - 8 * hh;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (key_of_reg(r) > L) Sc[kb][r] = -INFINITY;
@@ -459,7 +497,7 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sc[kb][r]);
     mx = other_half_max(mx) * p.scale_log2;
@@ -608,21 +646,28 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
     }
   }
 
-  if constexpr (NG > 1) {
-    // group 1's state to group 0: wave w of group 1 writes its O^T
-    // accumulators into its tile buffer w (free once every wave is past the
-    // loop), lane-contiguous 16-byte slots; its max and partial sums go to a
-    // small array.  Group 0 combines: m = max(m0, m1), a_g = 2^(m_g - m),
-    // O = a0 O0 + a1 O1, l = a0 l0 + a1 l1.
+  // Key halves with two or more column blocks: both waves of a row wave
+  // finish its rows, key half h the column blocks from h * (CB / 2) on.
+  constexpr bool KH_SPLIT_END = KH > 1 && CB >= 2;
+  auto mine = [&](int cb) { return !KH_SPLIT_END || ((cb >= CB / 2) == (kh == 1)); };
+  if constexpr (NG > 1 || (KH > 1 && !KH_SPLIT_END)) {
+    // group 1's state to group 0 (key halves: key half 1's to key half 0 of
+    // the same row wave): the handing wave writes its O^T accumulators into
+    // a tile buffer of its own (free once every wave is past the loop),
+    // lane-contiguous 16-byte slots; its max and partial sums go to a small
+    // array.  The receiving wave combines: m = max(m0, m1),
+    // a_g = 2^(m_g - m), O = a0 O0 + a1 O1, l = a0 l0 + a1 l1.
     __shared__ float lds_state[4][3][64];
     ATTN_POISON_LDS_ARRAY(lds_state);  // before the barrier below
     __syncthreads();
-    LDS_PTR(char) const mbuf = wave == 0   ? (LDS_PTR(char))lds_k0[NG - 1]
-                               : wave == 1 ? (LDS_PTR(char))lds_k1[NG - 1]
-                               : wave == 2 ? (LDS_PTR(char))lds_v0[NG - 1]
+    const int slot = NG > 1 ? wave : rw;  // the pair's buffer and state row
+    const bool hands = NG > 1 ? grp == 1 : kh == 1;
+    LDS_PTR(char) const mbuf = slot == 0   ? (LDS_PTR(char))lds_k0[NG - 1]
+                               : slot == 1 ? (LDS_PTR(char))lds_k1[NG - 1]
+                               : slot == 2 ? (LDS_PTR(char))lds_v0[NG - 1]
                                            : (LDS_PTR(char))lds_v1[NG - 1];
     static_assert(CB * 4 * 1024 <= TB, "a wave's accumulators fit one tile buffer");
-    if (grp == 1) {
+    if (hands) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -630,19 +675,19 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
           *(LDS_PTR(f32x4))(mbuf + ((cb * 4 + g) * 64 + lane) * 16) =
               (f32x4){acc_o[cb][4 * g], acc_o[cb][4 * g + 1], acc_o[cb][4 * g + 2],
                       acc_o[cb][4 * g + 3]};
-      lds_state[wave][0][lane] = m_run;
-      lds_state[wave][1][lane] = l_rnd;
-      lds_state[wave][2][lane] = l_fp32;
+      lds_state[slot][0][lane] = m_run;
+      lds_state[slot][1][lane] = l_rnd;
+      lds_state[slot][2][lane] = l_fp32;
     }
     __syncthreads();
-    if (grp == 1) return;  // group 0 finishes the rows
-    const float m1 = lds_state[wave][0][lane];
+    if (hands) return;  // the receiving wave finishes the rows
+    const float m1 = lds_state[slot][0][lane];
     const float m = fmaxf(m_run, m1);
     const float a0 = __builtin_amdgcn_exp2f(m_run - m);
     const float a1 = __builtin_amdgcn_exp2f(m1 - m);
     m_run = m;
-    l_rnd = a0 * l_rnd + a1 * lds_state[wave][1][lane];
-    l_fp32 = a0 * l_fp32 + a1 * lds_state[wave][2][lane];
+    l_rnd = a0 * l_rnd + a1 * lds_state[slot][1][lane];
+    l_fp32 = a0 * l_fp32 + a1 * lds_state[slot][2][lane];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -652,6 +697,64 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
         for (int r = 0; r < 4; ++r)
           acc_o[cb][4 * g + r] = a0 * acc_o[cb][4 * g + r] + a1 * y[r];
       }
+  }
+  if constexpr (KH_SPLIT_END) {
+    // Each key half writes the column blocks the other one finishes into
+    // its own slot (a tile buffer, free once every wave is past the loop)
+    // and its max and partial sums into a small array; then both combine
+    // the two states the same way, in the order (key half 0, key half 1),
+    // so that both get the same sums and the same LSE.
+    __shared__ float lds_st[2][2][3][64];  // [row wave][key half][m, l_rnd, l_fp32][lane]
+    ATTN_POISON_LDS_ARRAY(lds_st);  // before the barrier below
+    __syncthreads();
+    auto xbuf = [&](int slot) {
+      const int x = 2 * rw + slot;
+      return x == 0   ? (LDS_PTR(char))lds_k0[0]
+             : x == 1 ? (LDS_PTR(char))lds_k1[0]
+             : x == 2 ? (LDS_PTR(char))lds_v0[0]
+                      : (LDS_PTR(char))lds_v1[0];
+    };
+    // column block cb's place in a slot
+    auto cslot = [](int cb) { return cb >= CB / 2 ? cb - CB / 2 : cb; };
+    static_assert((CB + 1) / 2 * 4 * 1024 <= TB, "half of a wave's accumulators fit a tile buffer");
+    {
+      LDS_PTR(char) const w = xbuf(kh);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        if (mine(cb)) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(LDS_PTR(f32x4))(w + ((cslot(cb) * 4 + g) * 64 + lane) * 16) =
+              (f32x4){acc_o[cb][4 * g], acc_o[cb][4 * g + 1], acc_o[cb][4 * g + 2],
+                      acc_o[cb][4 * g + 3]};
+      }
+      lds_st[rw][kh][0][lane] = m_run;
+      lds_st[rw][kh][1][lane] = l_rnd;
+      lds_st[rw][kh][2][lane] = l_fp32;
+    }
+    __syncthreads();
+    const float m0 = lds_st[rw][0][0][lane];
+    const float m1 = lds_st[rw][1][0][lane];
+    const float m = fmaxf(m0, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m0 - m);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - m);
+    m_run = m;
+    l_rnd = a0 * lds_st[rw][0][1][lane] + a1 * lds_st[rw][1][1][lane];
+    l_fp32 = a0 * lds_st[rw][0][2][lane] + a1 * lds_st[rw][1][2][lane];
+    const float a_own = kh ? a1 : a0;
+    const float a_oth = kh ? a0 : a1;
+    LDS_PTR(const char) const rbuf = xbuf(kh ^ 1);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      if (!mine(cb)) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 y = *(LDS_PTR(const f32x4))(rbuf + ((cslot(cb) * 4 + g) * 64 + lane) * 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc_o[cb][4 * g + r] = a_own * acc_o[cb][4 * g + r] + a_oth * y[r];
+      }
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
@@ -674,7 +777,8 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
       float* prow = p.part_o +
                     ((((int64_t)piece * p.B + b) * p.sq_split + ii) * p.Hq + hq) * D;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb) {
+        if (!mine(cb)) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 x;
@@ -682,14 +786,16 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
           for (int r = 0; r < 4; ++r) x[r] = acc_o[cb][4 * g + r] * inv;
           if (cb * 32 + 8 * g + 4 * hh < p.d) *(f32x4*)(prow + cb * 32 + 8 * g + 4 * hh) = x;
         }
-      if (hh == 0) {
+      }
+      if (hh == 0 && kh == 0) {
         const float lse = has ? (m_run + __builtin_amdgcn_logf(l_lse)) * LN2 : -INFINITY;
         p.part_lse[(((int64_t)piece * p.B + b) * p.Hq + hq) * p.sq_split + ii] = lse;
       }
     } else if (qi < p.Sq) {
       uint16_t* orow = p.o + (int64_t)b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)hq * p.o_sh;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb) {
+        if (!mine(cb)) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x8 x;
@@ -703,7 +809,8 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
                            (unsigned)(uint16_t)y[2] | ((unsigned)(uint16_t)y[3] << 16)};
           if (cb * 32 + 8 * g + 4 * hh < p.d) *(u32x2*)(orow + cb * 32 + 8 * g + 4 * hh) = w;
         }
-      if (p.lse != nullptr && hh == 0) {
+      }
+      if (p.lse != nullptr && hh == 0 && kh == 0) {
         const float lse = has ? (m_run + __builtin_amdgcn_logf(l_lse)) * LN2 : -INFINITY;
         p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] = lse;
       }
@@ -951,9 +1058,11 @@ struct SplitPlan {
 };
 
 // off: the causal offset (query i sees key j <= i + off), Sk - Sq unless
-// the caller gives another (a key shard of a longer sequence)
-SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
-                          int kv_split, int off) {
+// the caller gives another (a key shard of a longer sequence).  The plan of
+// 4-wave workgroups of 32 rows per wave: one or two groups, key split as
+// asked (kv_split > 1), automatic (0) or none (1).
+SplitPlan make_split_plan_rows(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
+                               int kv_split, int off) {
   SplitPlan sp{};
   sp.base = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
   const Plan& pl = sp.base;
@@ -1016,6 +1125,37 @@ SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int cau
   return sp;
 }
 
+// The launch plan of a forward call.  In the regime of the two groups (at
+// most one 4-wave workgroup per CU, at least 8 tiles in the longest block)
+// an unsplit call takes the key halves, and so does an automatic one unless
+// the key split would cut the longest block into kSplitOverKeyHalves pieces
+// or more.  Measured on MI355X against the plan without key halves (one or
+// two groups, automatic split): 2 x 1024 causal fp16 23.5 against 28.9 us,
+// bf16 19.1 against 22.9, 1280 x 1536 causal 27.8 against 33.0 (2 pieces),
+// 1100 x 1100 causal (8 heads) 19.5 against 24.1 (5 pieces), 200 x 520 (GQA,
+// 2 x 4 heads) 11.2 against 13.4 (5 pieces); but 512 x 2048 non-causal
+// (8 heads) 30.6 against 24.5 and d = 40 1000 x 1000 causal (4 heads) 13.5
+// against 12.1, whose split takes 8 pieces: many short pieces and the merge
+// beat one long chain of half tiles.
+constexpr int kSplitOverKeyHalves = 6;
+SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
+                          int kv_split, int off) {
+  const SplitPlan sp = make_split_plan_rows(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, off);
+  if (kv_split > 1 || sp.grid <= 0 || sp.npieces >= kSplitOverKeyHalves) return sp;
+  const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
+  const int nmax = block_tiles((pl.qtiles - 1) * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0);
+  if (!key_halves(pl.grid, d, nmax)) return sp;
+  SplitPlan k{};
+  k.base = make_plan(B, Sq, Sk, Hq, Hkv, d, causal, 2);
+  if (k.base.grid <= 0) return sp;
+  k.base.ng = 1;
+  k.chunk = 0;
+  k.npieces = 1;
+  k.q_first = Sq;
+  k.grid = k.base.grid;
+  return k;
+}
+
 template <int PDT, int ODT>
 hipError_t launch_merge(int d, long long grid, const MergeParams& mp, hipStream_t st) {
   const dim3 g((unsigned)grid), b(256);
@@ -1048,11 +1188,15 @@ hipError_t launch_t(const Plan& pl, long long nwg, const Params& p, hipStream_t 
   // the tile buffers are static LDS (pl.lds_bytes reports their size)
   if constexpr (D <= 128) {
     if (pl.ng == 2) {
-      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 2>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 2, 1>), grid, block, 0, st, p);
+      return hipGetLastError();
+    }
+    if (pl.kh == 2) {
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 2>), grid, block, 0, st, p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1>), grid, block, 0, st, p);
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 1>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
@@ -1333,14 +1477,11 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
   attn_status st = attn_fwd_check(pp, pp, pp, (void*)pp, nullptr, B, Sq, Sk, Hq,
                                   Hkv, d, 1.0f, causal, dtype);
   if (st != ATTN_OK) return st;
-  Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
-  // attn_fwd: no key split; the last row block is the longest
-  const int nmax = block_tiles((pl.qtiles - 1) * pl.rows_wg, pl.rows_wg, Sq, Sk, Sk - Sq,
-                               causal != 0);
-  pl.ng = two_groups(pl.grid, d, nmax) ? 2 : 1;
-  int vals[10] = {pl.grid, pl.ng * pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
+  // attn_fwd: no key split
+  const Plan pl = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, 1, Sk - Sq).base;
+  int vals[11] = {pl.grid, pl.ng * pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
                   pl.ng * pl.lds_bytes, pl.xcd_cols > 0 || pl.xcd_qsplit > 0 ? 1 : 0,
-                  pl.pipelined, 0};
+                  pl.pipelined, 0, pl.kh == 2 ? 1 : 0};
   if (decode_eligible(Sq, Hq, Hkv, d)) {
     // the decode kernel, unsplit: a workgroup per (batch, kv head) with all
     // g * Sq rows in one wave, DEC_WAVES waves over the keys
@@ -1350,8 +1491,9 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
     const int vals_dec[10] = {(int)dp.grid, DEC_WAVES * 64, Sq, 32, g, 32,
                               DEC_WAVES * 2 * 32 * padded_head(d) * 2, 0, 0, 1};
     for (int i = 0; i < 10; ++i) vals[i] = vals_dec[i];
+    vals[10] = 0;
   }
-  for (int i = 0; i < n && i < 10; ++i) out[i] = vals[i];
+  for (int i = 0; i < n && i < 11; ++i) out[i] = vals[i];
   return ATTN_OK;
 }
 
@@ -1375,17 +1517,18 @@ attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, i
     if (dp.grid <= 0) return ATTN_ERR_INVALID_ARG;
     const long long mrows = (long long)B * Sq * Hq;
     const int rpb = 256 / (padded_head(d) / 4);
-    const int vals[6] = {(int)dp.grid, dp.pieces, dp.pieces > 1 ? dp.piece_tiles * 32 : 0,
+    const int vals[7] = {(int)dp.grid, dp.pieces, dp.pieces > 1 ? dp.piece_tiles * 32 : 0,
                          dp.pieces > 1 ? 0 : Sq,
-                         dp.pieces > 1 ? (int)((mrows + rpb - 1) / rpb) : 0, DEC_WAVES * 64};
-    for (int i = 0; i < n && i < 6; ++i) out[i] = vals[i];
+                         dp.pieces > 1 ? (int)((mrows + rpb - 1) / rpb) : 0, DEC_WAVES * 64, 0};
+    for (int i = 0; i < n && i < 7; ++i) out[i] = vals[i];
     return ATTN_OK;
   }
   const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, Sk - Sq);
   if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
-  const int vals[6] = {(int)sp.grid, sp.npieces, sp.chunk * BC, sp.q_first,
-                       (int)sp.merge_grid, sp.base.ng * sp.base.nw * 64};
-  for (int i = 0; i < n && i < 6; ++i) out[i] = vals[i];
+  const int vals[7] = {(int)sp.grid, sp.npieces, sp.chunk * BC, sp.q_first,
+                       (int)sp.merge_grid, sp.base.ng * sp.base.nw * 64,
+                       sp.base.kh == 2 ? 1 : 0};
+  for (int i = 0; i < n && i < 7; ++i) out[i] = vals[i];
   return ATTN_OK;
 }
 

@@ -104,7 +104,7 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
 
 /*
  * attn_fwd_plan -- describe the launch attn_fwd would make for these sizes,
- * without any device call.  Writes up to n (at most 10) ints into `out`:
+ * without any device call.  Writes up to n (at most 11) ints into `out`:
  *   [0] workgroups in the grid   [1] threads per workgroup
  *   [2] query rows per workgroup [3] keys per K/V tile
  *   [4] query heads per workgroup (GQA packing)
@@ -118,6 +118,11 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
  *       of up to 32 of them shares one wave and the 4 waves of a workgroup
  *       split the keys (then [0] counts a workgroup per (batch, kv head,
  *       32-row group), [2] is Sq and [4] the GQA group size)
+ *   [10] 1 if the waves take key halves: of the 4 waves of a workgroup, two
+ *       take the same 32 query rows, one the first and one the second 32
+ *       keys of every tile, and their two partial states are merged in the
+ *       workgroup (rows per workgroup halve, workgroups double; chosen when
+ *       the plain grid would leave most CUs with one workgroup)
  * Returns the status attn_fwd_check would return.
  */
 attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
@@ -284,13 +289,15 @@ attn_status attn_fwd_split_workspace(int B, int Sq, int Sk, int Hq, int Hkv,
 
 /*
  * attn_fwd_split_plan -- the launches attn_fwd_split would make, without any
- * device call.  Writes up to n (at most 6) ints into `out`:
+ * device call.  Writes up to n (at most 7) ints into `out`:
  *   [0] attention workgroups     [1] pieces of the longest query block
  *   [2] keys per piece (0 = no split)
  *   [3] first query row of a split block (Sq when nothing is split)
  *   [4] merge workgroups (0 when nothing is split)
  *   [5] threads per attention workgroup (512: two 4-wave groups that take
  *       alternate key tiles of the same rows, as attn_fwd_plan [1])
+ *   [6] 1 if the waves take key halves (as attn_fwd_plan [10]; then nothing
+ *       is split)
  */
 attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
                                 int causal, int dtype, int kv_split, int* out,

@@ -162,6 +162,46 @@ def _tiles(q0, rows, Sq, Sk, causal):
     return -(-end // 64) if end > 0 else 0
 
 
+def _rows_plan(B, Sq, Sk, Hq, Hkv, row_waves=4):
+    """Rows per workgroup, query blocks and columns of a plan whose
+    workgroups hold row_waves waves of 32 rows (4; 2 with key halves): up to
+    that many query heads of one GQA group share a workgroup."""
+    group = Hq // Hkv
+    gh = 1
+    while gh * 2 <= row_waves and group % (gh * 2) == 0:
+        gh *= 2
+    rows = row_waves // gh * 32
+    return rows, -(-Sq // rows), B * Hkv * (group // gh)
+
+
+def _auto_chunk(tiles, ncols):
+    """The automatic key split's piece length in tiles (0: no split)."""
+    if len(tiles) * ncols >= 256:
+        return 0
+    for c in range(2, max(tiles), 2):
+        if sum(-(-t // c) if t > c else 1 for t in tiles) * ncols <= 256:
+            return c
+    return 0
+
+
+def _key_halves_expected(B, Sq, Sk, Hq, Hkv, d, causal, kv_split):
+    """The key-halves rule: an unsplit or automatic call whose 4-row-wave
+    plan has at most 256 workgroups, padded head size at most 128 and at
+    least 8 tiles in its longest block, unless the automatic split would cut
+    that block into 6 pieces or more."""
+    if kv_split > 1 or d > 128:
+        return False
+    rows, qtiles, ncols = _rows_plan(B, Sq, Sk, Hq, Hkv)
+    tiles = [_tiles(t * rows, rows, Sq, Sk, causal) for t in range(qtiles)]
+    if qtiles * ncols > 256 or max(tiles) < 8:
+        return False
+    if kv_split == 0:
+        c = _auto_chunk(tiles, ncols)
+        if c and -(-max(tiles) // c) >= 6:
+            return False
+    return True
+
+
 @pytest.mark.parametrize("cfg", [
     (2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16),
     (1, 1280, 1536, 16, 16, 128, 1, ATTN_DTYPE_F16),
@@ -177,15 +217,14 @@ def test_split_plan_follows_the_piece_rule(cfg, kv_split):
     holding one fp32 row state per piece and split row."""
     _lib()
     B, Sq, Sk, Hq, Hkv, d, causal, dt = cfg
-    base = binding.attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, causal, dt)
     sp = binding.attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, dt, kv_split)
     ws = binding.attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, causal, dt, kv_split)
-    rows = base["rows_per_wg"]
-    qtiles = -(-Sq // rows)
-    ncols = base["grid"] // qtiles
+    kh = _key_halves_expected(B, Sq, Sk, Hq, Hkv, d, causal, kv_split)
+    assert sp["key_halves"] == int(kh)
+    rows, qtiles, ncols = _rows_plan(B, Sq, Sk, Hq, Hkv, 2 if kh else 4)
     tiles = [_tiles(t * rows, rows, Sq, Sk, causal) for t in range(qtiles)]
     if sp["keys_per_piece"] == 0:
-        assert sp["pieces"] == 1 and sp["grid"] == base["grid"] and ws == 0
+        assert sp["pieces"] == 1 and sp["grid"] == qtiles * ncols and ws == 0
         assert sp["first_split_row"] == Sq and sp["merge_grid"] == 0
         if kv_split > 1:  # a requested split is dropped only when it cannot cut
             assert -(-max(tiles) // kv_split) + (-(-max(tiles) // kv_split)) % 2 >= max(tiles)
@@ -210,7 +249,7 @@ def test_split_plan_follows_the_piece_rule(cfg, kv_split):
 def test_split_automatic_choice():
     """kv_split = 0: no split when the query blocks number at least the 256
     CUs; otherwise the shortest even piece length (in 64-key tiles) whose
-    pieces number at most 256."""
+    pieces number at most 256, unless the key halves take the call."""
     _lib()
     for cfg in ((1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16),
                 (2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16),
@@ -220,19 +259,12 @@ def test_split_automatic_choice():
                 (1, 300, 300, 4, 2, 64, 1, ATTN_DTYPE_F16),
                 (1, 128, 128, 2, 2, 64, 0, ATTN_DTYPE_F16)):
         B, Sq, Sk, Hq, Hkv, d, causal, dt = cfg
-        base = binding.attn_fwd_plan(*cfg)
         sp = binding.attn_fwd_split_plan(*cfg, 0)
-        rows = base["rows_per_wg"]
-        qtiles = -(-Sq // rows)
-        ncols = base["grid"] // qtiles
+        rows, qtiles, ncols = _rows_plan(B, Sq, Sk, Hq, Hkv)
         tiles = [_tiles(t * rows, rows, Sq, Sk, causal) for t in range(qtiles)]
-        want = 0
-        if qtiles * ncols < 256:
-            for c in range(2, max(tiles), 2):
-                n = sum(-(-t // c) if t > c else 1 for t in tiles) * ncols
-                if n <= 256:
-                    want = c
-                    break
+        kh = _key_halves_expected(B, Sq, Sk, Hq, Hkv, d, causal, 0)
+        assert sp["key_halves"] == int(kh), cfg
+        want = 0 if kh else _auto_chunk(tiles, ncols)
         assert sp["keys_per_piece"] == 64 * want, cfg
 
 
@@ -653,22 +685,43 @@ def test_noalloc_refuses_a_split_beyond_the_scratch_before_any_device_call():
                                       None) == ATTN_ERR_INVALID_ARG
 
 
-def test_two_group_workgroups_for_grids_of_at_most_one_per_cu():
-    """Up to 256 workgroups with work (one per CU), padded head sizes up to
-    128 and at least 8 key tiles in the longest workgroup take two 4-wave
-    groups per workgroup (512 threads, twice the tile LDS); larger grids and
-    head sizes, and short rows, take one."""
+def test_key_halves_for_grids_of_at_most_one_per_cu():
+    """Up to 256 workgroups of 4 row waves (one per CU), padded head sizes up
+    to 128 and at least 8 key tiles in the longest block: attn_fwd takes the
+    key halves (4 waves = 2 row waves x 2 key halves, rows per workgroup
+    halved, twice the workgroups, the same tile LDS); larger grids and head
+    sizes, and short rows, keep the 4 row waves."""
     _lib()
-    two = binding.attn_fwd_plan(2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16)   # 256 blocks
-    assert two["grid"] == 256 and two["threads"] == 512
-    assert two["lds_bytes"] == 2 * 4 * 64 * 128 * 2 <= 160 * 1024
-    # 8 tiles of 64 keys in every block (non-causal 512 keys): two groups;
-    # 7 tiles (448 keys) or a causal block of 4 (256 keys): one
-    assert binding.attn_fwd_plan(1, 512, 512, 8, 8, 64, 0, ATTN_DTYPE_F16)["threads"] == 512
-    assert binding.attn_fwd_plan(1, 512, 448, 8, 8, 64, 0, ATTN_DTYPE_F16)["threads"] == 256
-    assert binding.attn_fwd_plan(1, 256, 256, 16, 16, 128, 1, ATTN_DTYPE_F16)["threads"] == 256
-    assert binding.attn_fwd_plan(1, 128, 128, 2, 2, 64, 1, ATTN_DTYPE_F16)["threads"] == 256
+    kh = binding.attn_fwd_plan(2, 1024, 1024, 16, 16, 128, 1, ATTN_DTYPE_F16)   # 256 blocks
+    assert kh["key_halves"] == 1 and kh["grid"] == 512 and kh["threads"] == 256
+    assert kh["rows_per_wg"] == 64 and kh["lds_bytes"] == 4 * 64 * 128 * 2
+    # GQA: two heads of the group per workgroup (one per row wave)
+    g = binding.attn_fwd_plan(1, 1024, 1024, 32, 8, 128, 1, ATTN_DTYPE_BF16)
+    assert g["key_halves"] == 1 and g["heads_per_wg"] == 2 and g["rows_per_wg"] == 32
+    assert g["grid"] == 32 * 8 * 2
+    # 8 tiles of 64 keys in every block (non-causal 512 keys): key halves;
+    # 7 tiles (448 keys) or a causal block of 4 (256 keys): not
+    assert binding.attn_fwd_plan(1, 512, 512, 8, 8, 64, 0, ATTN_DTYPE_F16)["key_halves"] == 1
+    for cfg in ((1, 512, 448, 8, 8, 64, 0), (1, 256, 256, 16, 16, 128, 1),
+                (1, 128, 128, 2, 2, 64, 1)):
+        p = binding.attn_fwd_plan(*cfg, ATTN_DTYPE_F16)
+        assert p["key_halves"] == 0 and p["threads"] == 256, cfg
     one = binding.attn_fwd_plan(1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16)   # 2048 blocks
-    assert one["threads"] == 256 and one["lds_bytes"] == 4 * 64 * 128 * 2
+    assert one["key_halves"] == 0 and one["threads"] == 256
+    assert one["lds_bytes"] == 4 * 64 * 128 * 2
     big_d = binding.attn_fwd_plan(1, 1000, 1000, 8, 2, 160, 1, ATTN_DTYPE_BF16)
-    assert big_d["threads"] == 256
+    assert big_d["key_halves"] == 0 and big_d["threads"] == 256
+
+
+def test_two_group_workgroups_for_split_pieces():
+    """A key split whose pieces number at most 256 and hold at least 8 tiles
+    runs two 4-wave groups per workgroup over alternate tiles (512 threads,
+    twice the tile LDS); shorter pieces keep one group."""
+    _lib()
+    sp = binding.attn_fwd_split_plan(1, 1100, 1100, 8, 8, 128, 1, ATTN_DTYPE_F16, 2)
+    assert sp["threads"] == 512 and sp["pieces"] == 2 and sp["key_halves"] == 0
+    sp = binding.attn_fwd_split_plan(1, 1100, 1100, 8, 8, 128, 1, ATTN_DTYPE_F16, 4)
+    assert sp["threads"] == 256 and sp["pieces"] == 3  # pieces of 6 of the 18 tiles
+    # the automatic split into 8 pieces of 4 tiles: one group
+    sp = binding.attn_fwd_split_plan(1, 512, 2048, 8, 8, 128, 0, ATTN_DTYPE_F16, 0)
+    assert sp["pieces"] == 8 and sp["threads"] == 256 and sp["key_halves"] == 0

@@ -35,9 +35,9 @@ def test_noalloc_matches_workspace_path_two_calls():
     from exact_attention_19_amd.binding import ATTN_DTYPE_BF16, ATTN_DTYPE_F16, ATTN_OK
     lib = load_library()
     stream = torch.cuda.current_stream()
-    big = WORKLOADS["mha_causal_offset_f16_b1_h16_sq1280_sk1536_d128"]   # automatic split
+    big = WORKLOADS["mha_causal_offset_f16_b1_h16_sq1280_sk1536_d128"]
     small = Workload("noalloc_small", 2, 8, 2, 300, 1000, 128, "bf16", True, 1 / math.sqrt(128))
-    runs = [(big, 0), (small, 4)]
+    runs = [(big, 2), (small, 4)]  # both split: pieces in the scratch
     outs = []
     for w, kv_split in runs:
         code = ATTN_DTYPE_BF16 if w.dtype == "bf16" else ATTN_DTYPE_F16
