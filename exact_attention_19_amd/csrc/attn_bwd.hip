@@ -19,10 +19,11 @@
 //          K and V tiles stream through LDS, dQ^T = K^T dS^T accumulates in
 //          registers,
 //   dkdv   key outer: two waves own 32 keys of one kv head (each half of
-//          the rows of every query tile), the Q and dO tiles of every query
-//          row (and every query head of the GQA group) that sees them stream
-//          through LDS, dK^T = Q^T dS and dV^T = dO^T P accumulate in
-//          registers and the two halves are added at the end.
+//          the rows of every query tile; above d = 128 two more, one wave of
+//          each pair summing dV and the other dK), the Q and dO tiles of
+//          every query row (and every query head of the GQA group) that sees
+//          them stream through LDS, dK^T = Q^T dS and dV^T = dO^T P
+//          accumulate in registers and the two halves are added at the end.
 // Each gradient element is written once by one lane: no atomics, and the
 // results do not depend on scheduling.
 //
@@ -305,32 +306,42 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
 
 // ------------------------------------------------------------ dK, dV
 //
-// Workgroup: 8 waves over 128 keys of one (batch, kv head).  Wave w owns the
-// 32 keys 32 (w & 3) .. +31 and, of every 64-row query tile, the rows
-// 32 (w >> 2) .. +31: the two waves of a key group run on one SIMD side by
-// side (one's softmax beside the other's MFMAs) and split the rows, and
-// their dK/dV partial sums are added through LDS at the end.  The keys' K
-// and V rows stay in LDS for the whole walk (the B operands of S and dP,
-// read as row fragments).  The walk covers the query tiles that see any of
-// the keys, for every query head of the kv head's group; tile t sits in LDS
-// buffer t & 1 (Q and dO double-buffered, with the rows' lse * log2(e) and
-// D).
+// Workgroup: 8 waves over 32 * KG keys of one (batch, kv head).  Each wave
+// owns the 32 keys of its key group kg and, of every 64-row query tile, the
+// 32 rows of its row half qh; the dK/dV partial sums of the two row halves
+// are added through LDS at the end.  The keys' K and V rows stay in LDS for
+// the whole walk (the B operands of S and dP, read as row fragments).  The
+// walk covers the query tiles that see any of the keys, for every query
+// head of the kv head's group; tile t sits in LDS buffer t % NB (Q and dO
+// double-buffered up to d = 192, with the rows' lse * log2(e) and D).
 //
-// Head sizes above 128: two key groups (64 keys, 4 waves, one per SIMD) so
-// that a wave has the registers for its 2 x (D / 32) x 16 dK/dV sums, and at
-// 256 one Q/dO buffer (K and V of 64 keys plus two Q/dO buffers would take
-// 192 KiB of the CU's 160): the next tile is then loaded after the current
-// one has been used, behind a second barrier.
+// Up to d = 128 (KG = 4, 128 keys): wave w is key group w & 3, row half
+// w >> 2, and sums both dK and dV; the two waves of a key group share a SIMD
+// (one's softmax beside the other's MFMAs).
+//
+// Above 128 a wave's dK and dV sums alone would take 2 x (D / 32) x 16
+// registers, leaving one wave per SIMD.  There the workgroup has 2 key groups
+// (64 keys) x 2 row halves x 2 roles: a dV wave computes S, P and
+// dV^T += dO^T P; a dK wave computes S, dP, dS and dK^T += Q^T dS.  S is
+// computed by both (5 products per row block and key group instead of 4),
+// but each wave holds one set of sums, so two waves share each SIMD again.
+// At 256 there is one Q/dO buffer (K and V of 64 keys plus two Q/dO buffers
+// would take 192 KiB of the CU's 160): the next tile is then loaded after
+// the current one has been used, behind a second barrier.
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(D > 128 ? 256 : 512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   using T = Ty<DT>;
   constexpr int CB = D / 32;
   constexpr int KK = D / 16;
   constexpr int TB = 64 * D * 2;
-  constexpr int KG = D > 128 ? 2 : 4;  // key groups of 32 keys
+  constexpr bool ROLES = D > 128;      // a wave sums dK or dV, not both
+  constexpr int KG = ROLES ? 2 : 4;    // key groups of 32 keys
+  constexpr int NR = ROLES ? 2 : 1;    // roles per key group and row half
   constexpr int KT = KG / 2;           // 64-key tiles of K (and of V)
   constexpr int NB = D > 192 ? 1 : 2;  // Q/dO tile buffers
-  constexpr int VW = 4 / KG;           // 16-row load slices per wave of a 64-row tile
+  constexpr int LW = KG * NR;          // waves per row half
+  constexpr int VW = 4 / LW;           // 16-row load slices per wave of a 64-row tile
+  static_assert(2 * LW == 8, "eight waves");
   __shared__ __attribute__((aligned(1024))) char lds_q0[TB], lds_q1[NB > 1 ? TB : 16],
       lds_o0[TB], lds_o1[NB > 1 ? TB : 16];
   __shared__ __attribute__((aligned(1024))) char lds_k[KT][TB], lds_v[KT][TB];
@@ -357,13 +368,15 @@ __global__ __launch_bounds__(D > 128 ? 256 : 512, 1) void attn_bwd_dkdv_kernel(B
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kg = wave % KG;  // key group
-  const int qh = wave / KG;  // row half of each query tile
-  // a 64-row tile loaded by the KG waves of one row half: each takes VW of
+  const int kg = wave % KG;          // key group
+  const int qh = (wave / KG) & 1;    // row half of each query tile
+  const int role = wave / (2 * KG);  // with roles: 0 sums dV, 1 sums dK
+  const int lw = kg + KG * role;     // the wave's place among its row half's
+  // a 64-row tile loaded by the LW waves of one row half: each takes VW of
   // the four 16-row slices of the shared tile loader
   auto load64 = [&](const char* slice, uint32_t row_bytes, int n, int nrows, LDS_PTR(char) dst) {
 #pragma unroll
-    for (int s = 0; s < VW; ++s) load_tile<D>(slice, row_bytes, n, nrows, p.d, dst, kg * VW + s, lane);
+    for (int s = 0; s < VW; ++s) load_tile<D>(slice, row_bytes, n, nrows, p.d, dst, lw * VW + s, lane);
   };
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -391,7 +404,7 @@ __global__ __launch_bounds__(D > 128 ? 256 : 512, 1) void attn_bwd_dkdv_kernel(B
         load64(slice, rbk, KT * kblk + i, p.Sk, dst);
       } else {
         LDS_PTR(u32x4) z = (LDS_PTR(u32x4))dst;
-        for (int e = kg * 64 + lane; e < TB / 16; e += KG * 64) z[e] = (u32x4){0u, 0u, 0u, 0u};
+        for (int e = lw * 64 + lane; e < TB / 16; e += LW * 64) z[e] = (u32x4){0u, 0u, 0u, 0u};
       }
     }
   }
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(D > 128 ? 256 : 512, 1) void attn_bwd_dkdv_kernel(B
     const int64_t head0 = (int64_t)b * p.Sq * p.Hq + h;
     load64((const char*)((qh == 0 ? p.q : p.dout) + head0 * p.d), rbq, qt, p.Sq,
            qh == 0 ? qbuf(t) : obuf(t));
-    if (kg == 0) {
+    if (lw == 0) {
       const float* src = (qh == 0 ? p.l2 : p.dvec) + ((int64_t)b * p.Hq + h) * p.Sq;
       const uint32_t r = (uint32_t)min(qt * 64 + lane, p.Sq - 1);
       const __amdgpu_buffer_rsrc_t rs =
@@ -428,6 +441,15 @@ __global__ __launch_bounds__(D > 128 ? 256 : 512, 1) void attn_bwd_dkdv_kernel(B
           rs, (LDS_PTR(void))(qh == 0 ? &lds_l2[t % NB][0] : &lds_d[t % NB][0]), 4, r * 4, 0,
           0, 0);
     }
+  };
+  // the next tile's loads: into the other buffer while this tile is
+  // computed (two buffers), or after every wave is done with the one buffer
+  auto next = [&](int t) {
+    if (++nq == per_head) {
+      nq = 0;
+      ++nh;
+    }
+    issue(t + 1);
   };
 
   uint32_t rbase[2], tbase[2], kbase[2];
@@ -444,197 +466,234 @@ __global__ __launch_bounds__(D > 128 ? 256 : 512, 1) void attn_bwd_dkdv_kernel(B
   LDS_PTR(char) const ktile = (LDS_PTR(char))lds_k[kg >> 1];
   LDS_PTR(char) const vtile = (LDS_PTR(char))lds_v[kg >> 1];
 
-  f32x16 adk[CB], adv[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      adk[cb][r] = 0.f;
-      adv[cb][r] = 0.f;
-    }
+  if (steps > 0) issue(0);
 
-  // the next tile's loads: into the other buffer while this tile is
-  // computed (two buffers), or after every wave is done with the one buffer
-  auto next = [&](int t) {
-    if (++nq == per_head) {
-      nq = 0;
-      ++nh;
-    }
-    issue(t + 1);
-  };
-  // tile t's contributions of the wave's 32 query rows to its 32 keys
-  auto body = [&](int t, int qt) {
-    const int i0 = qt * 64 + 32 * qh;  // first query row of this wave
-    // rows that see none of the wave's keys, or lie past Sq: nothing to add
-    if (i0 >= p.Sq || (CAUSAL && i0 + 31 + p.off < k0 + 32 * kg)) return;
-    LDS_PTR(char) const qtile = qbuf(t);
-    LDS_PTR(char) const otile = obuf(t);
-    LDS_PTR(const float) const l2t = (LDS_PTR(const float)) & lds_l2[t % NB][0];
-    LDS_PTR(const float) const dtt = (LDS_PTR(const float)) & lds_d[t % NB][0];
-    // rows need masking: a causal row that does not see every key of the
-    // wave, or a row past Sq
-    const int kmax = k0 + 32 * kg + 31;
-    const bool edge = (CAUSAL && i0 + p.off < kmax) || i0 + 32 > p.Sq;
-    // S = Q K^T and dP = dO V^T: rows = the wave's 32 query rows in the
-    // sigma order, columns = its 32 keys (lane)
-    f32x16 S, dP;
+  // The walk, the row-half reduction and the stores of one kind of wave:
+  // M = 0 sums dV, 1 sums dK, 2 both.  Only the sums a wave keeps are
+  // declared in its instance, so a role's registers hold one set.
+  auto run = [&](auto mode) {
+    constexpr int M = decltype(mode)::value;
+    constexpr bool DV = M != 1;
+    constexpr bool DK = M != 0;
+    f32x16 adk[DK ? CB : 1], adv[DV ? CB : 1];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      S[r] = 0.f;
-      dP[r] = 0.f;
-    }
-    {
-      // fragments of step kk + 1 are read while the MFMAs of step kk run
-      auto rd = [&](int kk, i16x8 (&f)[4]) {
-        const uint32_t ko = row_frag_off(kbase, kg & 1, kk);
-        f[0] = read_row_frag(qtile, rbase, qh, kk);
-        f[1] = *(LDS_PTR(const i16x8))(ktile + ko);
-        f[2] = read_row_frag(otile, rbase, qh, kk);
-        f[3] = *(LDS_PTR(const i16x8))(vtile + ko);
-      };
-      i16x8 fa[4], fb[4];
-      rd(0, fa);
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int kk = 0; kk < KK; kk += 2) {
-        rd(kk + 1, fb);
-        __builtin_amdgcn_sched_barrier(0);
-        S = T::mfma(fa[0], fa[1], S);
-        dP = T::mfma(fa[2], fa[3], dP);
-        if (kk + 2 < KK) rd(kk + 2, fa);
-        __builtin_amdgcn_sched_barrier(0);
-        S = T::mfma(fb[0], fb[1], S);
-        dP = T::mfma(fb[2], fb[3], dP);
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (DK) adk[cb][r] = 0.f;
+        if constexpr (DV) adv[cb][r] = 0.f;
       }
-    }
-    // register r holds query row 32 qh + key_of_reg(r) + 8 hh of the tile;
-    // registers 4g .. 4g+3 are 4 consecutive rows
-    i16x8 pf[2], dsf[2];
+
+    // tile t's contributions of the wave's 32 query rows to its 32 keys
+    auto body = [&](int t, int qt) {
+      const int i0 = qt * 64 + 32 * qh;  // first query row of this wave
+      // rows that see none of the wave's keys, or lie past Sq: nothing to add
+      if (i0 >= p.Sq || (CAUSAL && i0 + 31 + p.off < k0 + 32 * kg)) return;
+      LDS_PTR(char) const qtile = qbuf(t);
+      LDS_PTR(char) const otile = obuf(t);
+      LDS_PTR(const float) const l2t = (LDS_PTR(const float)) & lds_l2[t % NB][0];
+      LDS_PTR(const float) const dtt = (LDS_PTR(const float)) & lds_d[t % NB][0];
+      // rows need masking: a causal row that does not see every key of the
+      // wave, or a row past Sq
+      const int kmax = k0 + 32 * kg + 31;
+      const bool edge = (CAUSAL && i0 + p.off < kmax) || i0 + 32 > p.Sq;
+      // S = Q K^T and dP = dO V^T: rows = the wave's 32 query rows in the
+      // sigma order, columns = its 32 keys (lane)
+      f32x16 S, dP;
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      f32x8 pe, de;
+      for (int r = 0; r < 16; ++r) {
+        S[r] = 0.f;
+        dP[r] = 0.f;
+      }
+      {
+        // fragments of step kk + 1 are read while the MFMAs of step kk run
+        auto rd = [&](int kk, i16x8 (&f)[4]) {
+          const uint32_t ko = row_frag_off(kbase, kg & 1, kk);
+          f[0] = read_row_frag(qtile, rbase, qh, kk);
+          f[1] = *(LDS_PTR(const i16x8))(ktile + ko);
+          if constexpr (DK) {
+            f[2] = read_row_frag(otile, rbase, qh, kk);
+            f[3] = *(LDS_PTR(const i16x8))(vtile + ko);
+          }
+        };
+        i16x8 fa[4], fb[4];
+        rd(0, fa);
 #pragma unroll
-      for (int g2 = 0; g2 < 2; ++g2) {
-        const int g = 2 * f + g2;
-        const int row0 = 32 * qh + key_of_reg(4 * g) + 8 * hh;
-        const f32x4 l4 = *(LDS_PTR(const f32x4))(l2t + row0);
-        const f32x4 d4 = *(LDS_PTR(const f32x4))(dtt + row0);
-#pragma unroll
-        for (int r3 = 0; r3 < 4; ++r3) {
-          const int r = 4 * g + r3;
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -l4[r3]));
-          pe[4 * g2 + r3] = pr;
-          de[4 * g2 + r3] = pr * (dP[r] - d4[r3]);
+        for (int kk = 0; kk < KK; kk += 2) {
+          rd(kk + 1, fb);
+          __builtin_amdgcn_sched_barrier(0);
+          S = T::mfma(fa[0], fa[1], S);
+          if constexpr (DK) dP = T::mfma(fa[2], fa[3], dP);
+          if (kk + 2 < KK) rd(kk + 2, fa);
+          __builtin_amdgcn_sched_barrier(0);
+          S = T::mfma(fb[0], fb[1], S);
+          if constexpr (DK) dP = T::mfma(fb[2], fb[3], dP);
         }
       }
-      // masked rows and keys, in one branch per 8 scores (a test per score
-      // would cut the body into a branch per score); the empty volatile asm
-      // keeps it a branch, so that tiles without masked scores skip the
-      // compares instead of running them under a select
-      if (edge) {
-        asm volatile("" ::: "memory");
+      // register r holds query row 32 qh + key_of_reg(r) + 8 hh of the tile;
+      // registers 4g .. 4g+3 are 4 consecutive rows
+      i16x8 pf[2], dsf[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int qi = qt * 64 + 32 * qh + key_of_reg(4 * (2 * f + e / 4)) + 8 * hh + e % 4;
-          if (qi >= p.Sq || (CAUSAL && kj > qi + p.off)) {
-            pe[e] = 0.f;
-            de[e] = 0.f;
+      for (int f = 0; f < 2; ++f) {
+        f32x8 pe, de;
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * f + g2;
+          const int row0 = 32 * qh + key_of_reg(4 * g) + 8 * hh;
+          const f32x4 l4 = *(LDS_PTR(const f32x4))(l2t + row0);
+          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (DK) d4 = *(LDS_PTR(const f32x4))(dtt + row0);
+#pragma unroll
+          for (int r3 = 0; r3 < 4; ++r3) {
+            const int r = 4 * g + r3;
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -l4[r3]));
+            pe[4 * g2 + r3] = pr;
+            de[4 * g2 + r3] = DK ? pr * (dP[r] - d4[r3]) : 0.f;
           }
         }
-      }
-      pf[f] = T::cvt(pe);
-      dsf[f] = T::cvt(de);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (two 16-row steps);
-    // the fragments of the next step are read during the current one
-    {
-      constexpr int NS = 2 * CB;
-      auto rd = [&](int st, i16x8 (&f)[2]) {
-        f[0] = read_tr_frag(otile, tbase, 2 * qh + st / CB, st % CB);
-        f[1] = read_tr_frag(qtile, tbase, 2 * qh + st / CB, st % CB);
-      };
-      i16x8 fa[2], fb[2];
-      rd(0, fa);
+        // masked rows and keys, in one branch per 8 scores (a test per score
+        // would cut the body into a branch per score); the empty volatile asm
+        // keeps it a branch, so that tiles without masked scores skip the
+        // compares instead of running them under a select
+        if (edge) {
+          asm volatile("" ::: "memory");
 #pragma unroll
-      for (int st = 0; st < NS; st += 2) {
-        rd(st + 1, fb);
-        __builtin_amdgcn_sched_barrier(0);
-        adv[st % CB] = T::mfma(fa[0], pf[st / CB], adv[st % CB]);
-        adk[st % CB] = T::mfma(fa[1], dsf[st / CB], adk[st % CB]);
-        if (st + 2 < NS) rd(st + 2, fa);
-        __builtin_amdgcn_sched_barrier(0);
-        adv[(st + 1) % CB] = T::mfma(fb[0], pf[(st + 1) / CB], adv[(st + 1) % CB]);
-        adk[(st + 1) % CB] = T::mfma(fb[1], dsf[(st + 1) / CB], adk[(st + 1) % CB]);
+          for (int e = 0; e < 8; ++e) {
+            const int qi = qt * 64 + 32 * qh + key_of_reg(4 * (2 * f + e / 4)) + 8 * hh + e % 4;
+            if (qi >= p.Sq || (CAUSAL && kj > qi + p.off)) {
+              pe[e] = 0.f;
+              de[e] = 0.f;
+            }
+          }
+        }
+        if constexpr (DV) pf[f] = T::cvt(pe);
+        if constexpr (DK) dsf[f] = T::cvt(de);
       }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (two 16-row
+      // steps); the fragments of the next step are read during the current one
+      {
+        constexpr int NS = 2 * CB;
+        auto rd = [&](int st, i16x8 (&f)[2]) {
+          if constexpr (DV) f[0] = read_tr_frag(otile, tbase, 2 * qh + st / CB, st % CB);
+          if constexpr (DK) f[1] = read_tr_frag(qtile, tbase, 2 * qh + st / CB, st % CB);
+        };
+        i16x8 fa[2], fb[2];
+        rd(0, fa);
+#pragma unroll
+        for (int st = 0; st < NS; st += 2) {
+          rd(st + 1, fb);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (DV) adv[st % CB] = T::mfma(fa[0], pf[st / CB], adv[st % CB]);
+          if constexpr (DK) adk[st % CB] = T::mfma(fa[1], dsf[st / CB], adk[st % CB]);
+          if (st + 2 < NS) rd(st + 2, fa);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (DV)
+            adv[(st + 1) % CB] = T::mfma(fb[0], pf[(st + 1) / CB], adv[(st + 1) % CB]);
+          if constexpr (DK)
+            adk[(st + 1) % CB] = T::mfma(fb[1], dsf[(st + 1) / CB], adk[(st + 1) % CB]);
+        }
+      }
+    };
+
+    int cq = 0;  // tile index within its head of the tile being computed
+    for (int t = 0; t < steps; ++t) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (NB > 1 && t + 1 < steps) next(t);
+      body(t, qt0 + cq);
+      if (++cq == per_head) cq = 0;
+      if (NB == 1 && t + 1 < steps) {
+        __syncthreads();
+        next(t);
+      }
+    }
+
+    // add the row halves: the waves of row half 1 hand their sums to those
+    // of row half 0 through LDS (lane-contiguous 16-byte slots).  Both sums
+    // (KG = 4): dK into the K/V area, dV into the Q/dO area.  Roles: one
+    // area per key group and role, K and V (dV of key groups 0, 1), then Q
+    // and dO (dK).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    LDS_PTR(char) red_k;
+    LDS_PTR(char) red_v;
+    if constexpr (M == 2) {
+      red_k = (LDS_PTR(char))(kg < KT ? lds_k[kg % KT] : lds_v[kg % KT]);
+      red_v = kg < KT    ? (kg == 0 ? (LDS_PTR(char))lds_q0 : (LDS_PTR(char))lds_q1)
+              : kg == KT ? (LDS_PTR(char))lds_o0
+                         : (LDS_PTR(char))lds_o1;
+    } else {
+      static_assert(KT == 1, "roles: one K and one V tile");
+      const int slot = kg + 2 * M;
+      LDS_PTR(char) const area = slot == 0   ? (LDS_PTR(char))lds_k[0]
+                                 : slot == 1 ? (LDS_PTR(char))lds_v[0]
+                                 : slot == 2 ? (LDS_PTR(char))lds_q0
+                                             : (LDS_PTR(char))lds_o0;
+      red_k = area;
+      red_v = area;
+    }
+    if (qh == 1) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t o = (uint32_t)(((cb * 4 + g) * 64 + lane) * 16);
+          if constexpr (DK)
+            *(LDS_PTR(f32x4))(red_k + o) = (f32x4){adk[cb][4 * g], adk[cb][4 * g + 1],
+                                                   adk[cb][4 * g + 2], adk[cb][4 * g + 3]};
+          if constexpr (DV)
+            *(LDS_PTR(f32x4))(red_v + o) = (f32x4){adv[cb][4 * g], adv[cb][4 * g + 1],
+                                                   adv[cb][4 * g + 2], adv[cb][4 * g + 3]};
+        }
+    }
+    __syncthreads();
+    if (qh == 0 && kok) {
+      const int64_t r = ((int64_t)b * p.Sk + kj) * p.Hkv + kvh;
+      uint16_t* dkrow = p.dk + r * p.d;
+      uint16_t* dvrow = p.dv + r * p.d;
+      auto pack = [](const i16x8& x) {
+        return (u32x2){(unsigned)(uint16_t)x[0] | ((unsigned)(uint16_t)x[1] << 16),
+                       (unsigned)(uint16_t)x[2] | ((unsigned)(uint16_t)x[3] << 16)};
+      };
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t o = (uint32_t)(((cb * 4 + g) * 64 + lane) * 16);
+          const bool col_ok = cb * 32 + 8 * g + 4 * hh < p.d;
+          if constexpr (DK) {
+            const f32x4 ok = *(LDS_PTR(const f32x4))(red_k + o);
+            f32x8 x;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              x[r4] = (adk[cb][4 * g + r4] + ok[r4]) * p.scale;
+              x[r4 + 4] = 0.f;
+            }
+            const u32x2 wk = pack(T::cvt(x));
+            if (col_ok) *(u32x2*)(dkrow + cb * 32 + 8 * g + 4 * hh) = wk;
+          }
+          if constexpr (DV) {
+            const f32x4 ov = *(LDS_PTR(const f32x4))(red_v + o);
+            f32x8 y;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              y[r4] = adv[cb][4 * g + r4] + ov[r4];
+              y[r4 + 4] = 0.f;
+            }
+            const u32x2 wv = pack(T::cvt(y));
+            if (col_ok) *(u32x2*)(dvrow + cb * 32 + 8 * g + 4 * hh) = wv;
+          }
+        }
     }
   };
 
-  if (steps > 0) issue(0);
-  int cq = 0;  // tile index within its head of the tile being computed
-  for (int t = 0; t < steps; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (NB > 1 && t + 1 < steps) next(t);
-    body(t, qt0 + cq);
-    if (++cq == per_head) cq = 0;
-    if (NB == 1 && t + 1 < steps) {
-      __syncthreads();
-      next(t);
-    }
-  }
-
-  // add the row halves: the waves of row half 1 hand their sums to those of
-  // row half 0 through LDS (dK into the K/V area, dV into the Q/dO area;
-  // lane-contiguous 16-byte slots; KG = 2 leaves one K and one V tile, so
-  // dK goes to K (key group 0) or V (key group 1), and dV to Q or dO)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  LDS_PTR(char) const red_k = (LDS_PTR(char))(kg < KT ? lds_k[kg % KT] : lds_v[kg % KT]);
-  LDS_PTR(char) const red_v = kg < KT    ? (kg == 0 ? (LDS_PTR(char))lds_q0 : (LDS_PTR(char))lds_q1)
-                              : kg == KT ? (LDS_PTR(char))lds_o0
-                                         : (LDS_PTR(char))lds_o1;
-  if (qh == 1) {
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t o = (uint32_t)(((cb * 4 + g) * 64 + lane) * 16);
-        *(LDS_PTR(f32x4))(red_k + o) =
-            (f32x4){adk[cb][4 * g], adk[cb][4 * g + 1], adk[cb][4 * g + 2], adk[cb][4 * g + 3]};
-        *(LDS_PTR(f32x4))(red_v + o) =
-            (f32x4){adv[cb][4 * g], adv[cb][4 * g + 1], adv[cb][4 * g + 2], adv[cb][4 * g + 3]};
-      }
-  }
-  __syncthreads();
-  if (qh == 0 && kok) {
-    const int64_t r = ((int64_t)b * p.Sk + kj) * p.Hkv + kvh;
-    uint16_t* dkrow = p.dk + r * p.d;
-    uint16_t* dvrow = p.dv + r * p.d;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t o = (uint32_t)(((cb * 4 + g) * 64 + lane) * 16);
-        const f32x4 ok = *(LDS_PTR(const f32x4))(red_k + o);
-        const f32x4 ov = *(LDS_PTR(const f32x4))(red_v + o);
-        f32x8 x, y;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          x[r4] = (adk[cb][4 * g + r4] + ok[r4]) * p.scale;
-          y[r4] = adv[cb][4 * g + r4] + ov[r4];
-          x[r4 + 4] = 0.f;
-          y[r4 + 4] = 0.f;
-        }
-        const i16x8 xk = T::cvt(x);
-        const i16x8 yv = T::cvt(y);
-        const u32x2 wk = {(unsigned)(uint16_t)xk[0] | ((unsigned)(uint16_t)xk[1] << 16),
-                          (unsigned)(uint16_t)xk[2] | ((unsigned)(uint16_t)xk[3] << 16)};
-        const u32x2 wv = {(unsigned)(uint16_t)yv[0] | ((unsigned)(uint16_t)yv[1] << 16),
-                          (unsigned)(uint16_t)yv[2] | ((unsigned)(uint16_t)yv[3] << 16)};
-        if (cb * 32 + 8 * g + 4 * hh < p.d) {
-          *(u32x2*)(dkrow + cb * 32 + 8 * g + 4 * hh) = wk;
-          *(u32x2*)(dvrow + cb * 32 + 8 * g + 4 * hh) = wv;
-        }
-      }
+  if constexpr (ROLES) {
+    if (role == 0)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, 2>{});
   }
 }
 
@@ -676,11 +735,11 @@ hipError_t launch_bwd_t(const Plan& pl, const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((attn_bwd_prep_kernel<DT, D>), dim3((unsigned)((rows + 31) / 32)), dim3(256),
                      0, st, p);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3(pl.grid), dim3(256), 0, st, p);
-  // 32 keys per key group: 4 groups (512 threads) up to d = 128, 2 above
+  // 8 waves over 32 keys per key group: 4 groups up to d = 128, 2 above
   constexpr int KG = D > 128 ? 2 : 4;
   const long long kgrid = (long long)p.B * p.Hkv * ((p.Sk + 32 * KG - 1) / (32 * KG));
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)kgrid),
-                     dim3(2 * KG * 64), 0, st, p);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)kgrid), dim3(512), 0,
+                     st, p);
   return hipGetLastError();
 }
 
