@@ -56,6 +56,9 @@ CASES = [
     (1, 6, 3, 513, 1031, 64, "f16", False),      # 17 tiles, ragged keys
     (1, 8, 8, 1000, 600, 96, "bf16", True),      # Sq > Sk: rows with no key; 3 column blocks
     (4, 16, 16, 256, 512, 32, "f16", True),      # d = 32 (one column block), 8 tiles exactly
+    (1, 16, 16, 40, 2048, 128, "f16", True),     # 40 rows: row wave 1 mostly past Sq
+    (2, 32, 4, 300, 900, 64, "bf16", True),      # GQA 8: two heads per workgroup, snake per XCD
+    (3, 6, 2, 333, 700, 128, "f16", False),      # GQA 3, columns not a multiple of 8: no XCD order
 ]
 
 
