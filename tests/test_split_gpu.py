@@ -126,20 +126,28 @@ def test_split_workspace_contents_do_not_matter_and_reuse():
         _check_full(w, q, k, v, o, lse, strict=w is w1)
 
 
-def test_split_graph_replays():
-    """A split call (the attention kernel writing the pieces' states, then the
-    merge kernel) captured in a HIP graph: every replay gives the eager
+@pytest.mark.parametrize("kv_split", [2, 0])
+def test_split_graph_replays(kv_split):
+    """A forward call captured in a HIP graph: every replay gives the eager
     result, with eager split calls of another shape reusing the same
-    workspace between the replays."""
-    from exact_attention_19_amd import attn_fwd_split, attn_fwd_split_workspace
+    workspace between the replays.  kv_split = 2: the attention kernel writes
+    two pieces' states and the merge kernel combines them; 0: the library's
+    choice, here the unsplit key halves (one launch, the two halves' states
+    merged in LDS)."""
+    from exact_attention_19_amd import attn_fwd_split, attn_fwd_split_plan, attn_fwd_split_workspace
     w = WORKLOADS["mha_causal_offset_f16_b1_h16_sq1280_sk1536_d128"]
+    plan = attn_fwd_split_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.d, 1, _code("f16"), kv_split)
+    assert plan["pieces"] == (2 if kv_split == 2 else 1), plan
+    assert plan["key_halves"] == (1 if kv_split == 0 else 0), plan
     q, k, v = (t.cuda() for t in make_inputs(w, seed=0))
     w2 = Workload("graph_other", 1, 4, 2, 700, 900, 64, "f16", True, 0.2)
     q2, k2, v2 = (t.cuda() for t in make_inputs(w2, seed=3))
-    n = max(attn_fwd_split_workspace(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.d, 1, _code("f16"), 0),
+    n = max(attn_fwd_split_workspace(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.d, 1, _code("f16"),
+                                     kv_split),
             attn_fwd_split_workspace(w2.B, w2.Sq, w2.Sk, w2.Hq, w2.Hkv, w2.d, 1, _code("f16"), 3))
     ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
-    o_ref, l_ref = attn_fwd_split(q, k, v, scale=w.scale, causal=True, kv_split=0, workspace=ws)
+    o_ref, l_ref = attn_fwd_split(q, k, v, scale=w.scale, causal=True, kv_split=kv_split,
+                                  workspace=ws)
     o2_ref, l2_ref = attn_fwd_split(q2, k2, v2, scale=w2.scale, causal=True, kv_split=3,
                                     workspace=ws)
     out = torch.empty_like(o_ref)
@@ -147,14 +155,14 @@ def test_split_graph_replays():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # warm-up off the default stream before capture
-        attn_fwd_split(q, k, v, scale=w.scale, causal=True, kv_split=0, out=out, lse=lse,
-                       workspace=ws)
+        attn_fwd_split(q, k, v, scale=w.scale, causal=True, kv_split=kv_split, out=out,
+                       lse=lse, workspace=ws)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        attn_fwd_split(q, k, v, scale=w.scale, causal=True, kv_split=0, out=out, lse=lse,
-                       workspace=ws)
+        attn_fwd_split(q, k, v, scale=w.scale, causal=True, kv_split=kv_split, out=out,
+                       lse=lse, workspace=ws)
     for rep in range(4):
         out.fill_(float("nan"))
         lse.fill_(float("nan"))
