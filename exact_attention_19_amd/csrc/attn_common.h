@@ -315,11 +315,12 @@ bool sizes_ok(int B, int Sq, int Sk, int Hq, int Hkv) {
   return B >= 1 && Sq >= 1 && Sk >= 1 && Hq >= 1 && Hkv >= 1;
 }
 
-Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal, int kh = 1) {
+Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal, int kh = 1,
+               int nw = 4) {
   (void)Sk;
   (void)causal;
   Plan pl{};
-  pl.nw = 4;
+  pl.nw = nw;
   pl.kh = kh;
   const int rwaves = pl.nw / kh;  // waves with rows of their own
   const int group = Hq / Hkv;

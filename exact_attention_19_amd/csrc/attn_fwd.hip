@@ -151,11 +151,16 @@ struct PFrag {
 // so a launch that would leave most CUs with one workgroup has twice as
 // many workgroups, two per CU, and the snake order below puts a long row
 // block and a short one on each CU.
-template <int DT, int D, bool CAUSAL, int NG, int KH>
-__global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fwd_pipe_kernel(
-    Params p) {
+//
+// NW = 8 (key halves at d = 192, where a workgroup's tile buffers leave one
+// workgroup per CU): 4 row waves x 2 key halves over the same tiles, so that
+// two waves share each SIMD; the two halves of the waves load alternate
+// column blocks of a tile.
+template <int DT, int D, bool CAUSAL, int NG, int KH, int NW>
+__global__ __launch_bounds__(NG * NW * 64, (D > 128 || NG > 1 || NW > 4) ? 1 : 2) void
+attn_fwd_pipe_kernel(Params p) {
   using T = Ty<DT>;
-  constexpr int NW = 4;               // waves per group
+  static_assert(NW == 4 || (NW == 8 && KH == 2 && NG == 1), "8 waves run as key halves");
   constexpr int NT = NW * 64;         // threads per group
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int CPT = BC * CPR / NT;  // direct loads per lane per tile
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   constexpr int NP = BC / 16 / KH;    // 16-key P fragments per wave
   constexpr int TB = BC * D * 2;      // bytes per K or V tile buffer
   static_assert(CPT * NT == BC * CPR, "tile must split evenly over threads");
-  static_assert(CPT == CB, "one load round per 32-column block");
+  static_assert(CPT * (NW / 4) == CB, "one load round per 32-column block and wave quad");
 
   // Two K and two V tile buffers, each its own LDS object: the compiler's
   // alias analysis then separates the direct loads into one buffer from the
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   const int lane = tid & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR
   const int grp = NG > 1 ? wave_all >> 2 : 0;  // group
-  const int wave = wave_all & 3;   // wave within the group
+  const int wave = wave_all & (NW - 1);       // wave within the group
   static_assert(KH == 1 || (KH == 2 && NG == 1), "key halves run as one group");
   const int kh = KH > 1 ? (wave & 1) : 0;        // key half of every tile
   const int rw = KH > 1 ? (wave >> 1) : wave;    // row wave: 32 rows of one head
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
       if (!((k / s) & 1)) return k;
       return base + min(s, n - base) - 1 - (k - base);
     };
-    if (KH > 1) {
+    if (KH > 1 && NW == 4) {
       const int n = (int)gridDim.x;
       if (p.xcd_qsplit > 0 || p.xcd_cols > 0)
         L = (snake(L >> 3, n >> 3, kCUCount / 8) << 3) | (L & 7);
@@ -323,11 +328,13 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
   auto v_addr = [&](LDS_PTR(char) vbuf, int t, int cb, int half) {
     return vbuf + (cb * BLK + t * 16 * 64 + vbase_lds[half]);
   };
-  // Direct global -> LDS load round u of a wave writes LDS bytes
-  // [(u*NW + wave) * 1024, +1024) of the tile: block (u*NW + wave) / 4, rows
-  // 16 * ((u*NW + wave) % 4) + lane / 4, slot lane % 4.
-  static_assert(NW == 4, "the load mapping assumes four waves");
-  const int ld_row = 16 * wave + (lane >> 2);
+  // Direct global -> LDS load round u of a wave writes column block
+  // cbk = u * (NW / 4) + wave / 4 of the tile, LDS bytes
+  // [(cbk * 4 + wave % 4) * 1024, +1024): rows 16 * (wave % 4) + lane / 4,
+  // slot lane % 4.
+  const int wq = NW == 8 ? wave & 3 : wave;   // wave within its quad
+  const int wh = NW == 8 ? wave >> 2 : 0;     // quad
+  const int ld_row = 16 * wq + (lane >> 2);
   const int ld_chunk = (lane & 3) ^ ((ld_row >> 2) & 3);
   const int ld_col = ld_chunk * 8;  // + 32 * u: the column block of round u
 
@@ -361,9 +368,10 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
                                           0x00020000);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const uint32_t o = u < FULL || 32 * u + ld_col < p.d ? off : OOB_OFFSET;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_PTR(void))(buf + (u * NW + wave) * 1024),
-                                               16, o, 64 * u, 0, 0);
+      const int cbk = u * (NW / 4) + wh;  // column block (uniform)
+      const uint32_t o = cbk < FULL || 32 * cbk + ld_col < p.d ? off : OOB_OFFSET;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (LDS_PTR(void))(buf + (cbk * 4 + wq) * 1024), 16, o, 64 * cbk, 0, 0);
     }
   };
 
@@ -704,19 +712,25 @@ __global__ __launch_bounds__(NG * 256, (D > 128 || NG > 1) ? 1 : 2) void attn_fw
     // and its max and partial sums into a small array; then both combine
     // the two states the same way, in the order (key half 0, key half 1),
     // so that both get the same sums and the same LSE.
-    __shared__ float lds_st[2][2][3][64];  // [row wave][key half][m, l_rnd, l_fp32][lane]
+    // [row wave][key half][m, l_rnd, l_fp32][lane]
+    __shared__ float lds_st[NW / 2][2][3][64];
     ATTN_POISON_LDS_ARRAY(lds_st);  // before the barrier below
     __syncthreads();
+    // slot x = 2 rw + key half: a tile buffer each with 4 waves, half of one
+    // with 8 (an even number of column blocks)
+    constexpr int SLOT = (CB + 1) / 2 * 4 * 1024;
+    static_assert(SLOT * (NW / 4) <= TB, "a slot of half a wave's accumulators fits");
     auto xbuf = [&](int slot) {
       const int x = 2 * rw + slot;
-      return x == 0   ? (LDS_PTR(char))lds_k0[0]
-             : x == 1 ? (LDS_PTR(char))lds_k1[0]
-             : x == 2 ? (LDS_PTR(char))lds_v0[0]
-                      : (LDS_PTR(char))lds_v1[0];
+      const int bx = NW == 8 ? x >> 1 : x;
+      LDS_PTR(char) const base = bx == 0   ? (LDS_PTR(char))lds_k0[0]
+                                 : bx == 1 ? (LDS_PTR(char))lds_k1[0]
+                                 : bx == 2 ? (LDS_PTR(char))lds_v0[0]
+                                           : (LDS_PTR(char))lds_v1[0];
+      return NW == 8 ? base + (x & 1) * SLOT : base;
     };
     // column block cb's place in a slot
     auto cslot = [](int cb) { return cb >= CB / 2 ? cb - CB / 2 : cb; };
-    static_assert((CB + 1) / 2 * 4 * 1024 <= TB, "half of a wave's accumulators fit a tile buffer");
     {
       LDS_PTR(char) const w = xbuf(kh);
 #pragma unroll
@@ -1141,6 +1155,14 @@ constexpr int kSplitOverKeyHalves = 6;
 SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
                           int kv_split, int off) {
   const SplitPlan sp = make_split_plan_rows(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, off);
+  if (sp.grid > 0 && sp.chunk == 0 && padded_head(d) == 192) {
+    // unsplit at d = 192: the same grid in 8-wave workgroups of key halves
+    SplitPlan e = sp;
+    e.base = make_plan(B, Sq, Sk, Hq, Hkv, d, causal, 2, 8);
+    e.base.ng = 1;
+    e.grid = e.base.grid;
+    return e;
+  }
   if (kv_split > 1 || sp.grid <= 0 || sp.npieces >= kSplitOverKeyHalves) return sp;
   const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
   const int nmax = block_tiles((pl.qtiles - 1) * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0);
@@ -1188,15 +1210,21 @@ hipError_t launch_t(const Plan& pl, long long nwg, const Params& p, hipStream_t 
   // the tile buffers are static LDS (pl.lds_bytes reports their size)
   if constexpr (D <= 128) {
     if (pl.ng == 2) {
-      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 2, 1>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 2, 1, 4>), grid, block, 0, st, p);
       return hipGetLastError();
     }
     if (pl.kh == 2) {
-      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 2>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 2, 4>), grid, block, 0, st, p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 1>), grid, block, 0, st, p);
+  if constexpr (D == 192) {
+    if (pl.kh == 2 && pl.nw == 8) {
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 2, 8>), grid, block, 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 1, 4>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 

@@ -118,11 +118,13 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
  *       of up to 32 of them shares one wave and the 4 waves of a workgroup
  *       split the keys (then [0] counts a workgroup per (batch, kv head,
  *       32-row group), [2] is Sq and [4] the GQA group size)
- *   [10] 1 if the waves take key halves: of the 4 waves of a workgroup, two
- *       take the same 32 query rows, one the first and one the second 32
- *       keys of every tile, and their two partial states are merged in the
- *       workgroup (rows per workgroup halve, workgroups double; chosen when
- *       the plain grid would leave most CUs with one workgroup)
+ *   [10] 1 if the waves take key halves: two waves take the same 32 query
+ *       rows, one the first and one the second 32 keys of every tile, and
+ *       their two partial states are merged in the workgroup.  With 4 waves
+ *       (rows per workgroup halve, workgroups double) when the plain grid
+ *       would leave most CUs with one workgroup; with 8 waves ([1] = 512,
+ *       the plain grid) at padded head size 192, whose tile buffers leave
+ *       one workgroup per CU
  * Returns the status attn_fwd_check would return.
  */
 attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,

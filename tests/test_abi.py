@@ -109,7 +109,9 @@ def test_padded_head_sizes_pass_validation(d):
     assert _check(d=d) == ATTN_OK
     D = next(x for x in (32, 64, 96, 128, 192, 256) if x >= d)
     plan = binding.attn_fwd_plan(2, 1000, 1000, 8, 2, d, 1, ATTN_DTYPE_BF16)
-    groups = plan["threads"] // 256
+    # 512 threads: two groups with their own tiles, or (key halves) 8 waves
+    # over one set of tiles
+    groups = 1 if plan["key_halves"] else plan["threads"] // 256
     assert plan["lds_bytes"] == groups * 4 * 64 * D * 2
     # the split path's workspace holds rows of the padded size
     n = binding.attn_fwd_split_workspace(1, 300, 2000, 8, 2, d, 1, ATTN_DTYPE_BF16, kv_split=4)
@@ -709,8 +711,25 @@ def test_key_halves_for_grids_of_at_most_one_per_cu():
     one = binding.attn_fwd_plan(1, 8192, 8192, 32, 8, 128, 1, ATTN_DTYPE_BF16)   # 2048 blocks
     assert one["key_halves"] == 0 and one["threads"] == 256
     assert one["lds_bytes"] == 4 * 64 * 128 * 2
-    big_d = binding.attn_fwd_plan(1, 1000, 1000, 8, 2, 160, 1, ATTN_DTYPE_BF16)
+    big_d = binding.attn_fwd_plan(1, 1000, 1000, 8, 2, 256, 1, ATTN_DTYPE_BF16)
     assert big_d["key_halves"] == 0 and big_d["threads"] == 256
+
+
+@pytest.mark.parametrize("d", [136, 160, 192])
+def test_eight_wave_key_halves_at_d192(d):
+    """Padded head size 192, unsplit: 8-wave workgroups (4 row waves x 2 key
+    halves) over the plain plan's grid and tile buffers; a key split keeps
+    4-wave workgroups."""
+    _lib()
+    plain = dict(grid=2048, rows_per_wg=32, heads_per_wg=4)
+    p = binding.attn_fwd_plan(1, 8192, 8192, 32, 8, d, 1, ATTN_DTYPE_BF16)
+    assert p["key_halves"] == 1 and p["threads"] == 512, p
+    assert all(p[k] == v for k, v in plain.items()), p
+    assert p["lds_bytes"] == 4 * 64 * 192 * 2
+    sp = binding.attn_fwd_split_plan(1, 8192, 8192, 32, 8, d, 1, ATTN_DTYPE_BF16, 0)
+    assert sp["key_halves"] == 1 and sp["pieces"] == 1 and sp["threads"] == 512
+    sp = binding.attn_fwd_split_plan(1, 300, 2000, 8, 2, d, 1, ATTN_DTYPE_BF16, 4)
+    assert sp["key_halves"] == 0 and sp["pieces"] > 1 and sp["threads"] == 256
 
 
 def test_two_group_workgroups_for_split_pieces():

@@ -174,3 +174,52 @@ def test_no_writes_outside_outputs(d, split):
     assert torch.all(obuf[:pad] == 1234.0) and torch.all(obuf[pad + n_o:] == 1234.0)
     assert torch.all(lbuf[:pad] == 777.0) and torch.all(lbuf[pad + n_l:] == 777.0)
     assert torch.all(lse != 777.0) and torch.all(o != 1234.0)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,d,dt,causal", [
+    (1, 8, 2, 700, 900, 192, "bf16", True),      # GQA 4: one head per row wave
+    (2, 4, 4, 333, 517, 192, "f16", True),       # MHA, ragged rows and keys
+    (1, 16, 2, 300, 1000, 160, "bf16", True),    # GQA 8, padded 160 -> 192
+    (1, 6, 3, 129, 300, 176, "f16", False),      # GQA 2, padded 176 -> 192
+    (1, 4, 4, 200, 130, 192, "bf16", True),      # Sq > Sk: rows with no key
+])
+def test_eight_wave_key_halves_d192(B, Hq, Hkv, Sq, Sk, d, dt, causal):
+    """At padded head size 192 an unsplit call runs 8-wave workgroups: 4 row
+    waves x 2 key halves over one set of tile buffers (two waves per SIMD),
+    the 8 waves loading alternate column blocks of each tile and merging the
+    key halves through two slots per tile buffer."""
+    from exact_attention_19_amd import attn_fwd
+    from exact_attention_19_amd.binding import attn_fwd_plan
+    plan = attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), _code(dt))
+    assert plan["key_halves"] == 1 and plan["threads"] == 512, plan
+    w = _workload("kh8", B, Hq, Hkv, Sq, Sk, d, dt, causal)
+    q, k, v = make_inputs(w, seed=Sq + Sk + d)
+    _say(f"[gpu] attn_fwd (8-wave key halves) {w.name} {plan}")
+    o = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    o, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=causal, out=o)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+
+
+def test_eight_wave_key_halves_no_writes_outside_outputs():
+    """Canaries around O and LSE at d = 184 on the 8-wave d = 192 kernel: O
+    is dense with 184 columns, so a column past d written by mistake would
+    land on the next row or on a canary."""
+    from exact_attention_19_amd import attn_fwd
+    from exact_attention_19_amd.binding import attn_fwd_plan
+    d = 184
+    w = Workload("kh8_canary", 1, 8, 2, 333, 700, d, "bf16", True, 1.0 / math.sqrt(d))
+    assert attn_fwd_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, d, 1, _code("bf16"))["threads"] == 512
+    q, k, v = (t.cuda() for t in make_inputs(w, seed=12))
+    n_o = w.B * w.Sq * w.Hq * w.d
+    pad = 4096
+    obuf = torch.full((n_o + 2 * pad,), 1234.0, dtype=torch.bfloat16, device="cuda")
+    n_l = w.B * w.Hq * w.Sq
+    lbuf = torch.full((n_l + 2 * pad,), 777.0, dtype=torch.float32, device="cuda")
+    o = obuf[pad:pad + n_o].view(w.B, w.Sq, w.Hq, w.d)
+    lse = lbuf[pad:pad + n_l].view(w.B, w.Hq, w.Sq)
+    attn_fwd(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:pad] == 1234.0) and torch.all(obuf[pad + n_o:] == 1234.0)
+    assert torch.all(lbuf[:pad] == 777.0) and torch.all(lbuf[pad + n_l:] == 777.0)
+    assert torch.all(lse != 777.0) and torch.all(o != 1234.0)
