@@ -1213,7 +1213,7 @@ hipError_t launch_t(const Plan& pl, long long nwg, const Params& p, hipStream_t 
       hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 2, 1, 4>), grid, block, 0, st, p);
       return hipGetLastError();
     }
-    if (pl.kh == 2) {
+    if (pl.kh == 2 && pl.nw == 4) {
       hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 2, 4>), grid, block, 0, st, p);
       return hipGetLastError();
     }
