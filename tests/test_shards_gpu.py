@@ -45,6 +45,8 @@ def _w(B, Hq, Hkv, Sq, Sk, d, dt):
     (1, 16, 2, 700, 2100, 128, "bf16", [0, 1500, 2100]),
     (2, 32, 8, 1, 3000, 128, "bf16", [0, 1000, 2999, 3000]),   # decode kernel
     (1, 16, 4, 4, 1000, 64, "f16", [0, 500, 1000]),             # decode kernel
+    (1, 8, 2, 300, 1000, 192, "bf16", [0, 250, 640, 1000]),     # 8-wave key halves
+    (1, 6, 6, 200, 700, 176, "f16", [0, 333, 700]),             # padded 176 -> 192
 ])
 def test_key_shards(B, Hq, Hkv, Sq, Sk, d, dt, cuts, kv_split):
     from exact_attention_19_amd import attn_fwd_causal_offset, attn_merge

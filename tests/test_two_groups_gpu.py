@@ -223,3 +223,31 @@ def test_eight_wave_key_halves_no_writes_outside_outputs():
     assert torch.all(obuf[:pad] == 1234.0) and torch.all(obuf[pad + n_o:] == 1234.0)
     assert torch.all(lbuf[:pad] == 777.0) and torch.all(lbuf[pad + n_l:] == 777.0)
     assert torch.all(lse != 777.0) and torch.all(o != 1234.0)
+
+
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+def test_eight_wave_key_halves_strided(layout):
+    """Strided views at d = 192, unsplit: q, k, v as (B, H, S, d) transposes
+    or as slices of wider rows; the 8-wave workgroups read them through the
+    element strides."""
+    from exact_attention_19_amd import attn_fwd_strided, attn_fwd_split_plan
+    B, Hq, Hkv, Sq, Sk, d = 2, 8, 4, 300, 700, 192
+    plan = attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, 1, _code("bf16"), 1)
+    assert plan["key_halves"] == 1 and plan["threads"] == 512, plan
+    w = _workload(f"kh8_strided_{layout}", B, Hq, Hkv, Sq, Sk, d, "bf16", True)
+    q, k, v = make_inputs(w, seed=21)
+    if layout == "bhsd":
+        qs, ks, vs = (t.transpose(1, 2).contiguous().cuda() for t in (q, k, v))
+    else:
+        wide = 256
+        def embed(t):
+            x = torch.full(t.shape[:3] + (wide,), float("nan"), dtype=t.dtype)
+            x[..., :d] = t
+            return x.cuda()[..., :d]
+        qs, ks, vs = embed(q), embed(k), embed(v)
+    _say(f"[gpu] attn_fwd_strided (8-wave key halves) {w.name} {plan}")
+    o, lse = attn_fwd_strided(qs, ks, vs, scale=w.scale, causal=True, layout=layout, kv_split=1)
+    torch.cuda.synchronize()
+    if layout == "bhsd":
+        o = o.transpose(1, 2)
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
