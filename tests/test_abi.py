@@ -744,3 +744,51 @@ def test_two_group_workgroups_for_split_pieces():
     # the automatic split into 8 pieces of 4 tiles: one group
     sp = binding.attn_fwd_split_plan(1, 512, 2048, 8, 8, 128, 0, ATTN_DTYPE_F16, 0)
     assert sp["pieces"] == 8 and sp["threads"] == 256 and sp["key_halves"] == 0
+
+
+def test_plan_queries_agree_over_random_shapes():
+    """For 3000 seeded random shapes (both dtypes, causal or not, GQA groups,
+    head sizes 8..256): attn_fwd_plan equals the unsplit split plan; the
+    8-wave key halves appear exactly at padded head size 192 unsplit; the
+    4-wave key halves only at padded head sizes up to 128 and at most 256
+    four-row-wave workgroups; a plan with key halves never splits and needs
+    no workspace; a split plan needs a workspace and a merge; the automatic
+    split never takes 6 or more pieces where the key halves could run."""
+    import random
+    _lib()
+    rng = random.Random(1234)
+    for _ in range(3000):
+        B = rng.choice([1, 1, 2, 3, 4])
+        Hkv = rng.choice([1, 2, 4, 8])
+        Hq = Hkv * rng.choice([1, 2, 3, 4, 8])
+        Sq = rng.choice([1, 2, 4, 8, 17, 64, 100, 333, 1000, 1237, 2048, 4096])
+        Sk = rng.choice([1, 64, 130, 512, 700, 1531, 2048, 4096, 8192])
+        d = 8 * rng.randint(1, 32)
+        causal = rng.randint(0, 1)
+        dt = rng.choice([ATTN_DTYPE_F16, ATTN_DTYPE_BF16])
+        D = next(x for x in (32, 64, 96, 128, 192, 256) if x >= d)
+        fp = binding.attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, causal, dt)
+        s1 = binding.attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, dt, 1)
+        s0 = binding.attn_fwd_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, dt, 0)
+        ws0 = binding.attn_fwd_split_workspace(B, Sq, Sk, Hq, Hkv, d, causal, dt, 0)
+        cfg = (B, Sq, Sk, Hq, Hkv, d, causal, dt)
+        assert s1["pieces"] == 1 and s1["grid"] == fp["grid"] and s1["threads"] == fp["threads"], cfg
+        assert s1["key_halves"] == fp["key_halves"], cfg
+        if fp["decode"]:
+            continue
+        if fp["key_halves"]:
+            assert D <= 192, cfg
+            if D == 192:
+                assert fp["threads"] == 512, cfg
+            else:
+                assert D <= 128 and fp["threads"] == 256, cfg
+        elif D == 192:
+            raise AssertionError(f"unsplit d = {d} without the 8-wave key halves: {cfg}")
+        if s0["key_halves"]:
+            assert s0["pieces"] == 1 and ws0 == 0 and s0["merge_grid"] == 0, cfg
+        if s0["pieces"] > 1:
+            assert ws0 > 0 and s0["merge_grid"] > 0 and s0["key_halves"] == 0, cfg
+            if D <= 128 and fp["key_halves"] == 1:
+                assert s0["pieces"] >= 6, cfg  # the key halves give way only to long splits
+        else:
+            assert ws0 == 0 and s0["merge_grid"] == 0, cfg
