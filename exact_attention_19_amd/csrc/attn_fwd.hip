@@ -35,7 +35,10 @@
 //   max is only moved when a tile's max exceeds it by more than RESCALE_TAU
 //   (2^8): the result is mathematically identical, because numerator and
 //   denominator use the same stale max, and most tiles then skip the
-//   rescaling of the accumulator.
+//   rescaling of the accumulator.  With bf16 (whose exponent range is
+//   fp32's) the max is taken on a row block's first tile only; a later tile
+//   whose probabilities against it overshoot a bound is redone with its own
+//   max (DEFER_SUM_LIMIT).
 // * The softmax denominator sums the very 16-bit probabilities that multiply
 //   V (v_dot2 against 1.0: exact products, fp32 accumulation), so the
 //   normalisation O = sum P~ V / sum P~ uses one consistent set of rounded
@@ -69,6 +72,15 @@
 namespace {
 
 constexpr float RESCALE_TAU = 8.0f; // log2 headroom before the max is moved
+// bf16: after the first tile of a row block the running max is not taken per
+// tile; a tile whose probabilities against it sum past this bound in a lane
+// (some score more than about 2^35 above the max, or an overflow to inf) is
+// redone with its true max.  bf16 has the fp32 exponent range, so
+// probabilities up to 2^40 round with the same relative error as those up to
+// 1.  A lane's sum then grows by less than 2^40 per 32 keys, so a row's sum
+// stays below 2^35 Sk and its accumulators below 2^35 Sk max|V|: finite in
+// fp32 while Sk max|V| < 2^93.
+constexpr float DEFER_SUM_LIMIT = 1099511627776.0f;  // 2^40
 
 // ------------------------------------------------------------ parameters
 struct Params {
@@ -126,9 +138,10 @@ struct Params {
 // stream in, so two K and two V buffers live in LDS.
 //
 // The thresholded max update is decided at the start of an iteration from
-// S(j); the rescale of the accumulators by alpha(j) is applied at the END of
-// the iteration, after O has absorbed V(j-1)^T P(j-1), whose probabilities
-// were taken against the previous max.
+// S(j) (bf16: on the first tile, or at the end of an iteration whose P(j)
+// overshot); the rescale of the accumulators by alpha(j) is applied at the
+// END of the iteration, after O has absorbed V(j-1)^T P(j-1), whose
+// probabilities were taken against the previous max.
 template <typename PT, int N>
 struct PFrag {
   PT hi[N];
@@ -172,6 +185,11 @@ attn_fwd_pipe_kernel(Params p) {
   constexpr int TB = BC * D * 2;      // bytes per K or V tile buffer
   static_assert(CPT * NT == BC * CPR, "tile must split evenly over threads");
   static_assert(CPT * (NW / 4) == CB, "one load round per 32-column block and wave quad");
+  // bf16 up to d = 128: the running max is taken on a row block's first tile
+  // and then only for a tile whose probabilities overshoot (DEFER_SUM_LIMIT);
+  // above 128 the redo finds no registers
+  constexpr bool DEFER_MAX = DT == ATTN_DTYPE_BF16 && D <= 128;
+  static_assert(!DEFER_MAX || !T::SPLIT_P, "the deferred max redoes a single-part P");
 
   // Two K and two V tile buffers, each its own LDS object: the compiler's
   // alias analysis then separates the direct loads into one buffer from the
@@ -494,29 +512,40 @@ attn_fwd_pipe_kernel(Params p) {
     issue_rows(vslice, rbv, ld_off_v, load_of(i), V_LOAD);
     // mask the straddling tiles (and a filler tile past j_hi, wholly), then
     // the row max and the max update
-    if (j >= n_full || j >= j_hi) {
+    auto mask = [&](f32x16 (&S)[KBW]) {
+      if (j >= n_full || j >= j_hi) {
 #pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) {
-        const int L = j >= j_hi ? -BC : lim_row - j * BC - (KBW * kh + kb) * 32 - 8 * hh;
+        for (int kb = 0; kb < KBW; ++kb) {
+          const int L = j >= j_hi ? -BC : lim_row - j * BC - (KBW * kh + kb) * 32 - 8 * hh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key_of_reg(r) > L) Sc[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (key_of_reg(r) > L) S[kb][r] = -INFINITY;
+        }
       }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < KBW; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sc[kb][r]);
-    mx = other_half_max(mx) * p.scale_log2;
-    const float m_new = fmaxf(m_run, mx);
-    // move the max only past the threshold: alpha = 1 (no rescale) otherwise
-    const bool resc = __builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_TAU) != 0;
+    };
+    // the row max of S (scaled to log2 units) and the thresholded max update;
+    // alpha: the factor the accumulators take
     float alpha = 1.f;
-    if (resc) {
-      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-    }
+    bool resc = false;
+    auto max_update = [&](const f32x16 (&S)[KBW], float tau) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+      mx = other_half_max(mx) * p.scale_log2;
+      const float m_new = fmaxf(m_run, mx);
+      // move the max only past the threshold: alpha = 1 (no rescale) otherwise
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + tau) != 0) {
+        alpha *= __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        resc = true;
+      }
+    };
+    mask(Sc);
+    // bf16: the max is taken on the first tile only (a tile that overshoots
+    // it is redone below)
+    if (!DEFER_MAX || i == 0) max_update(Sc, RESCALE_TAU);
     const float neg_m = -m_run;
     float ls = 0.f;   // unrounded P (LSE)
     float lr = 0.f;   // rounded P (normalisation of O)
@@ -612,6 +641,53 @@ attn_fwd_pipe_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (DEFER_MAX) {
+      // A lane whose probabilities of this tile sum past the bound (a score
+      // far above the running max, or an overflow to inf): the wave takes
+      // S(j) again, from K(j) in global memory (its LDS buffer is already
+      // taking K(j+2)), moves the max to the tile's max and redoes P(j) and
+      // its sums.  The accumulators take the factor at the end of the
+      // iteration, as with the per-tile max.
+      if (__builtin_amdgcn_ballot_w64(ls > DEFER_SUM_LIMIT) != 0) {
+        f32x16 S[KBW];
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          // key row 32 (KBW kh + kb) + sigma(l32) of tile j (rows past Sk
+          // re-read row Sk - 1 and are masked), columns 16 kk + 8 hh .. +7
+          const int krow = min(j * BC + 32 * (KBW * kh + kb) + sigma(l32), p.Sk - 1);
+          const char* src = kslice + (int64_t)krow * rbk + hh * 16;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
+          u32x4 x[KK];
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            x[kk] = (u32x4){0u, 0u, 0u, 0u};  // columns past d are zeros
+            if (kk * 16 + hh * 8 < p.d) x[kk] = *(const u32x4*)(src + kk * 32);
+          }
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk)
+            S[kb] = T::mfma(__builtin_bit_cast(i16x8, x[kk]), qf[kk], S[kb]);
+          // one key block's fragments at a time (a cold path, kept out of
+          // the register peak of the steps)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mask(S);
+        max_update(S, 0.f);
+        ls = 0.f;
+        lr = 0.f;
+#pragma unroll
+        for (int sc = 0; sc < NSC; ++sc) {
+          e[sc % 8] = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(S[sc / 16][sc % 16], p.scale_log2, -m_run));
+          ls += e[sc % 8];
+          if (sc % 8 == 7) {
+            const i16x8 h = T::cvt(e);
+            Pc.hi[sc / 8] = h;
+            lr = T::sum8(h, lr);
+          }
+        }
+      }
+    }
     l_rnd = l_rnd * alpha + lr;
     if constexpr (T::LSE_FROM_FP32_SUM) l_fp32 = l_fp32 * alpha + ls;
     // rescale after O has absorbed V(j-1)^T P(j-1) (taken against the old max)

@@ -119,6 +119,47 @@ def test_small_integer_inputs_isolate_softmax():
     _check_full(w, q, k, v, o, lse, strict=False)
 
 
+def _late_dominant_inputs(w: Workload, seed: int):
+    """N(0,1) inputs whose first K/V tile is damped (x0.05) and a few later
+    keys scaled up (x1.5 to x6): with scale 1.0 the later scores exceed the
+    first tile's max by up to a few hundred log2 units, so the bf16 kernel's
+    deferred max must redo tiles, some of whose probabilities overflow."""
+    q, k, v = make_inputs(w, seed=seed)
+    k = k.clone()
+    k[:, :64] *= 0.05
+    g = torch.Generator().manual_seed(seed + 1)
+    for f in (1.5, 3.0, 6.0):
+        n = max(1, w.Sk // 300)
+        pos = torch.randint(64, w.Sk, (n,), generator=g) if w.Sk > 64 else torch.tensor([0])
+        k[:, pos] = (k[:, pos].float() * f).to(k.dtype)
+    return q, k, v
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal,d,kv_split", [
+    (4, 16, 4, 1024, 1024, True, 128, None),    # two workgroups per CU
+    (1, 4, 4, 2048, 2048, True, 128, None),     # key halves
+    (1, 8, 2, 300, 2500, False, 128, 4),        # key split, two 4-wave groups
+    (1, 8, 2, 333, 1700, True, 128, 2),         # key split, causal offset
+    (8, 8, 8, 777, 777, True, 64, None),
+    (2, 32, 8, 1100, 1100, False, 128, None),
+])
+def test_late_dominant_keys_bf16(B, Hq, Hkv, Sq, Sk, causal, d, kv_split):
+    """Scores far above the first tile's max in later tiles (bf16 redoes such
+    a tile with its true max) against the oracle, element by element."""
+    from exact_attention_19_amd import attn_fwd, attn_fwd_split
+    w = Workload(f"late_dominant_b{B}_h{Hq}_{Hkv}_sq{Sq}_sk{Sk}_c{int(causal)}_d{d}", B, Hq,
+                 Hkv, Sq, Sk, d, "bf16", causal, 1.0)
+    q, k, v = _late_dominant_inputs(w, seed=Sq + Sk)
+    _say(f"[gpu] {w.name} kv_split={kv_split}")
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    if kv_split is None:
+        o, lse = attn_fwd(qc, kc, vc, scale=1.0, causal=causal)
+    else:
+        o, lse = attn_fwd_split(qc, kc, vc, scale=1.0, causal=causal, kv_split=kv_split)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+
+
 def test_without_lse_and_on_a_side_stream():
     from exact_attention_19_amd import attn_fwd
     w = WORKLOADS["mha_causal_ragged_f16_b1_h16_sq1237_sk1531_d128"].with_(Hq=4, Hkv=4)
