@@ -374,12 +374,17 @@ attn_fwd_pipe_kernel(Params p) {
   // padded head size lacks: those lanes load from past the descriptor's end,
   // which fills zeros.
   constexpr int FULL = full_col_blocks(D);
-  auto issue_rows = [&](const char* slice, uint32_t row_bytes, uint32_t ld_off, int n,
-                        LDS_PTR(char) buf) {
+  // The ragged last tile of K/V (if any): its lanes' offsets, computed once
+  // (rows past Sk re-read row Sk - 1), so that a tile load selects an offset
+  // instead of branching.
+  const int n_rag = p.Sk % BC ? p.Sk / BC : -1;
+  const uint32_t rag_row = (uint32_t)(min(n_rag * BC + ld_row, p.Sk - 1) - n_rag * BC);
+  const uint32_t ld_off_k_rag = rag_row * rbk + (uint32_t)ld_col * 2;
+  const uint32_t ld_off_v_rag = rag_row * rbv + (uint32_t)ld_col * 2;
+  auto issue_rows = [&](const char* slice, uint32_t row_bytes, uint32_t ld_off,
+                        uint32_t ld_off_rag, int n, LDS_PTR(char) buf) {
     const char* tile = slice + (int64_t)n * BC * row_bytes;
-    uint32_t off = ld_off;
-    if ((n + 1) * BC > p.Sk)
-      off = (uint32_t)(min(n * BC + ld_row, p.Sk - 1) - n * BC) * row_bytes + (uint32_t)ld_col * 2;
+    const uint32_t off = n == n_rag ? ld_off_rag : ld_off;
     // raw buffer, 32-bit data format (word 3 of the descriptor)
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)((BC - 1) * row_bytes + p.d * 2),
@@ -480,6 +485,8 @@ attn_fwd_pipe_kernel(Params p) {
   constexpr int NOPS = NPV + NQK;
   constexpr int NSC = KBW * 16;  // scores per lane
   constexpr int LA = 3;          // read-ahead, in steps
+  constexpr int LD_STEP_K = 1;   // steps that issue the tile loads
+  constexpr int LD_STEP_V = 3;
   // Softmax work per step: the scores of key block 0 of S(j) are spread over
   // the P V steps and those of key block 1 over the first QK steps (those of
   // key block 0 of S(j+1)), so each block of S(j) is dead before the MFMAs
@@ -508,8 +515,7 @@ attn_fwd_pipe_kernel(Params p) {
     LDS_PTR(char) const V_PREV = vbuf_of(PAR ^ 1);  // V(j-1)
     LDS_PTR(char) const K_LOAD = kbuf_of(PAR);      // K(j+2)
     LDS_PTR(char) const V_LOAD = vbuf_of(PAR);      // V(j)
-    if (i + 2 < n_loc) issue_rows(kslice, rbk, ld_off_k, load_of(i + 2), K_LOAD);
-    issue_rows(vslice, rbv, ld_off_v, load_of(i), V_LOAD);
+    const int it = i;  // the group's local tile index (the step loop reuses i)
     // mask the straddling tiles (and a filler tile past j_hi, wholly), then
     // the row max and the max update
     auto mask = [&](f32x16 (&S)[KBW]) {
@@ -593,6 +599,13 @@ attn_fwd_pipe_kernel(Params p) {
         }
         Sn[kb] = T::mfma(f, qf[kk], Sn[kb]);
       }
+      // the tile loads of K(j+2) and V(j), issued beside the first MFMAs:
+      // their address arithmetic and descriptors then overlap the matrix
+      // core instead of delaying the first step
+      // (past the group's last tiles the K load re-reads its last tile into
+      // a buffer no later step reads, so that the step has no branch)
+      if (i == LD_STEP_K) issue_rows(kslice, rbk, ld_off_k, ld_off_k_rag, load_of(it + 2), K_LOAD);
+      if (i == LD_STEP_V) issue_rows(vslice, rbv, ld_off_v, ld_off_v_rag, load_of(it), V_LOAD);
       // P(j) = exp2(S(j) * c - m), skewed over three steps (SK = 1): the
       // argument of this step's scores, the exp2 of the previous step's,
       // the sums and conversion of the one before, so that no op of a step
@@ -707,8 +720,8 @@ attn_fwd_pipe_kernel(Params p) {
     // prologue: the group's first two K tiles in flight; the V buffer read
     // for the tile before the first in the first iteration is cleared so
     // that 0 * V stays 0.
-    issue_rows(kslice, rbk, ld_off_k, load_of(0), kbuf_of(0));
-    if (n_loc > 1) issue_rows(kslice, rbk, ld_off_k, load_of(1), kbuf_of(1));
+    issue_rows(kslice, rbk, ld_off_k, ld_off_k_rag, load_of(0), kbuf_of(0));
+    if (n_loc > 1) issue_rows(kslice, rbk, ld_off_k, ld_off_k_rag, load_of(1), kbuf_of(1));
     {
       LDS_PTR(u32x4) z = (LDS_PTR(u32x4))vbuf_of(1);
       for (int x = tid & (NT - 1); x < TB / 16; x += NT) z[x] = (u32x4){0u, 0u, 0u, 0u};
