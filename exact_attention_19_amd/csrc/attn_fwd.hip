@@ -389,12 +389,17 @@ attn_fwd_pipe_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)((BC - 1) * row_bytes + p.d * 2),
                                           0x00020000);
+    // the wave's LDS offset, opaque here, so that each load's destination is
+    // a scalar add at the load instead of a loop-invariant value the compiler
+    // would keep (and, short of scalar registers, reload from a VGPR lane)
+    uint32_t wofs = (uint32_t)wq * 1024;
+    asm volatile("" : "+s"(wofs));
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int cbk = u * (NW / 4) + wh;  // column block (uniform)
       const uint32_t o = cbk < FULL || 32 * cbk + ld_col < p.d ? off : OOB_OFFSET;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (LDS_PTR(void))(buf + (cbk * 4 + wq) * 1024), 16, o, 64 * cbk, 0, 0);
+          rs, (LDS_PTR(void))(buf + cbk * 4096 + wofs), 16, o, 64 * cbk, 0, 0);
     }
   };
 
@@ -523,9 +528,14 @@ attn_fwd_pipe_kernel(Params p) {
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb) {
           const int L = j >= j_hi ? -BC : lim_row - j * BC - (KBW * kh + kb) * 32 - 8 * hh;
+          // key_of_reg(r) > L: the sign of L - key_of_reg(r), spread over the
+          // word, selects -inf bit by bit (v_bfi_b32), with no compare mask in
+          // scalar registers
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key_of_reg(r) > L) S[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t sel = (uint32_t)((L - key_of_reg(r)) >> 31);
+            S[kb][r] = __uint_as_float((sel & 0xff800000u) | (~sel & __float_as_uint(S[kb][r])));
+          }
         }
       }
     };
