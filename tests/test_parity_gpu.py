@@ -119,16 +119,16 @@ def test_small_integer_inputs_isolate_softmax():
     _check_full(w, q, k, v, o, lse, strict=False)
 
 
-def _late_dominant_inputs(w: Workload, seed: int):
+def _late_dominant_inputs(w: Workload, seed: int, factors=(1.5, 3.0, 6.0)):
     """N(0,1) inputs whose first K/V tile is damped (x0.05) and a few later
-    keys scaled up (x1.5 to x6): with scale 1.0 the later scores exceed the
+    keys scaled up (by `factors`): with scale 1.0 the later scores exceed the
     first tile's max by up to a few hundred log2 units, so the bf16 kernel's
     deferred max must redo tiles, some of whose probabilities overflow."""
     q, k, v = make_inputs(w, seed=seed)
     k = k.clone()
     k[:, :64] *= 0.05
     g = torch.Generator().manual_seed(seed + 1)
-    for f in (1.5, 3.0, 6.0):
+    for f in factors:
         n = max(1, w.Sk // 300)
         pos = torch.randint(64, w.Sk, (n,), generator=g) if w.Sk > 64 else torch.tensor([0])
         k[:, pos] = (k[:, pos].float() * f).to(k.dtype)
@@ -156,6 +156,30 @@ def test_late_dominant_keys_bf16(B, Hq, Hkv, Sq, Sk, causal, d, kv_split):
         o, lse = attn_fwd(qc, kc, vc, scale=1.0, causal=causal)
     else:
         o, lse = attn_fwd_split(qc, kc, vc, scale=1.0, causal=causal, kv_split=kv_split)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal,d", [
+    (1, 4, 4, 2048, 2048, True, 128),    # key halves
+    (2, 8, 8, 1024, 1024, True, 128),
+    (1, 8, 2, 700, 1500, True, 64),
+    (1, 4, 4, 1000, 1000, False, 96),
+])
+def test_late_dominant_keys_f16(B, Hq, Hkv, Sq, Sk, causal, d):
+    """fp16 key halves with later keys scaled x4 to x16: scores up to about
+    120 log2 units above the first tile's max (a probability against that max
+    would overflow fp16 in a quarter to two thirds of the rows), so the
+    running max moves by large steps; compared with the oracle element by
+    element."""
+    from exact_attention_19_amd import attn_fwd, attn_fwd_plan
+    from exact_attention_19_amd.binding import ATTN_DTYPE_F16
+    w = Workload(f"late_dominant_f16_b{B}_h{Hq}_{Hkv}_sq{Sq}_sk{Sk}_c{int(causal)}_d{d}", B, Hq,
+                 Hkv, Sq, Sk, d, "f16", causal, 1.0 / math.sqrt(d))
+    assert attn_fwd_plan(B, Sq, Sk, Hq, Hkv, d, int(causal), ATTN_DTYPE_F16)["key_halves"]
+    q, k, v = _late_dominant_inputs(w, seed=Sq + 3 * Sk, factors=(4.0, 8.0, 16.0))
+    _say(f"[gpu] {w.name}")
+    o, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=causal)
     torch.cuda.synchronize()
     _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
 
