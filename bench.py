@@ -16,7 +16,7 @@ Prints ONE JSON line:
                 of rows of the same workload (a baseline, not a target)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--kv-split N] [--backward] [--head-size D]
+                       [--kv-split N] [--backward] [--head-size D] [--dtype T]
 """
 from __future__ import annotations
 
@@ -199,6 +199,9 @@ def main():
     ap.add_argument("--head-size", type=int, default=0, metavar="D",
                     help="run the named workload with head size D (scale 1/sqrt(D)); "
                          "the workload's name then ends in _dD")
+    ap.add_argument("--dtype", choices=("f16", "bf16"), default="",
+                    help="run the named workload in this dtype; the workload's name "
+                         "then has it in place of its own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a device copy of MIB MiB --steps times "
@@ -226,6 +229,8 @@ def main():
     if args.head_size:
         hd = args.head_size
         w = w.with_(name=re.sub(r"_d\d+$", f"_d{hd}", w.name), d=hd, scale=1.0 / math.sqrt(hd))
+    if args.dtype and args.dtype != w.dtype:
+        w = w.with_(name=re.sub(r"_(f16|bf16)_", f"_{args.dtype}_", w.name), dtype=args.dtype)
     dev = torch.device("cuda:0")
     q_cpu, k_cpu, v_cpu = make_inputs(w, seed=0)
     digest = input_digest(q_cpu, k_cpu, v_cpu)
