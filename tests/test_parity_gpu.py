@@ -160,6 +160,37 @@ def test_late_dominant_keys_bf16(B, Hq, Hkv, Sq, Sk, causal, d, kv_split):
     _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
 
 
+@pytest.mark.parametrize("case", ["bhsd", "d72", "shard", "shard_split"])
+def test_late_dominant_keys_bf16_views(case):
+    """The bf16 redo of an overshooting tile reads K(j) from global memory
+    through the call's strides: K and V as (B, H, S, d) views, a padded head
+    size (72 on the 96 kernel), and a causal key shard passed as a slice
+    (explicit mask offset, with and without a key split)."""
+    from exact_attention_19_amd import attn_fwd, attn_fwd_causal_offset, attn_fwd_strided
+    d = 72 if case == "d72" else 128
+    B, Hq, Hkv, Sq, Sk = 2, 8, 2, 600, 1400
+    w = Workload(f"late_dominant_{case}", B, Hq, Hkv, Sq, Sk, d, "bf16", True, 1.0)
+    q, k, v = _late_dominant_inputs(w, seed=17)
+    _say(f"[gpu] late dominant keys, {case}")
+    if case == "bhsd":
+        qh, kh, vh = (t.transpose(1, 2).contiguous().cuda() for t in (q, k, v))
+        o, lse = attn_fwd_strided(qh, kh, vh, scale=1.0, causal=True, layout="bhsd")
+        torch.cuda.synchronize()
+        _check_full(w, q, k, v, o.transpose(1, 2).cpu(), lse.cpu(), strict=False)
+    elif case == "d72":
+        o, lse = attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=1.0, causal=True)
+        torch.cuda.synchronize()
+        _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+    else:
+        a, b = 300, 1400
+        kg, vg = k.cuda(), v.cuda()
+        o, lse = attn_fwd_causal_offset(q.cuda(), kg[:, a:b], vg[:, a:b], Sk - Sq - a, scale=1.0,
+                                        kv_split=3 if case == "shard_split" else 1)
+        torch.cuda.synchronize()
+        ref = attn_fwd_oracle(q, k, v, 1.0, True, key_range=(a, b))
+        _check_full(w, None, None, None, o.cpu(), lse.cpu(), strict=False, ref=ref)
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal,d", [
     (1, 4, 4, 2048, 2048, True, 128),    # key halves
     (2, 8, 8, 1024, 1024, True, 128),
