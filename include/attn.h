@@ -88,6 +88,13 @@ typedef enum { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1, ATTN_DTYPE_F32 = 2 } att
  * B * Sq * Hq < 2^31 and B * Sk * Hkv < 2^31 (rows of each tensor); larger
  * problems are rejected with ATTN_ERR_INVALID_ARG rather than risking index
  * overflow.  attn_fwd_check reports the same status without a device call.
+ *
+ * Value range: the bf16 kernels up to d = 128 move the running row max only
+ * when a tile's probabilities against it overshoot 2^40 (the personal-notes
+ * page's online softmax, section "Online Softmax", with a stale max), so
+ * their unnormalised sums reach 2^35 * Sk * max|V|: inputs with
+ * Sk * max|V| >= 2^93 are outside the domain.  NaN or Inf inputs give
+ * undefined results.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
                      float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int d,
