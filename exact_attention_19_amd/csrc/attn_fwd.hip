@@ -498,6 +498,11 @@ attn_fwd_pipe_kernel(Params p) {
   // have the most time to land (V three quarters in: +3 % on 2 x 1024
   // causal fp16).
   constexpr bool LD_SPREAD = D == 128 && KBW == 2;
+  // Above d = 128 the step list has no registers to spare for the loads'
+  // address arithmetic: there they are issued at the top of the iteration
+  // (inside the steps the d = 256 kernel spilled into scratch and ran ten
+  // times slower).
+  constexpr bool LD_IN_STEPS = D <= 128;
   constexpr int LD_STEP_K = LD_SPREAD ? NOPS / 4 : 1;
   constexpr int LD_STEP_V = LD_SPREAD ? 3 * NOPS / 4 : 3;
   static_assert(LD_STEP_K < NOPS && LD_STEP_V < NOPS, "the loads are issued inside the step list");
@@ -530,6 +535,10 @@ attn_fwd_pipe_kernel(Params p) {
     LDS_PTR(char) const K_LOAD = kbuf_of(PAR);      // K(j+2)
     LDS_PTR(char) const V_LOAD = vbuf_of(PAR);      // V(j)
     const int it = i;  // the group's local tile index (the step loop reuses i)
+    if constexpr (!LD_IN_STEPS) {
+      issue_rows(kslice, rbk, ld_off_k, ld_off_k_rag, load_of(it + 2), K_LOAD);
+      issue_rows(vslice, rbv, ld_off_v, ld_off_v_rag, load_of(it), V_LOAD);
+    }
     // mask the straddling tiles (and a filler tile past j_hi, wholly), then
     // the row max and the max update
     auto mask = [&](f32x16 (&S)[KBW]) {
@@ -623,8 +632,10 @@ attn_fwd_pipe_kernel(Params p) {
       // core instead of delaying the first step
       // (past the group's last tiles the K load re-reads its last tile into
       // a buffer no later step reads, so that the step has no branch)
-      if (i == LD_STEP_K) issue_rows(kslice, rbk, ld_off_k, ld_off_k_rag, load_of(it + 2), K_LOAD);
-      if (i == LD_STEP_V) issue_rows(vslice, rbv, ld_off_v, ld_off_v_rag, load_of(it), V_LOAD);
+      if (LD_IN_STEPS && i == LD_STEP_K)
+        issue_rows(kslice, rbk, ld_off_k, ld_off_k_rag, load_of(it + 2), K_LOAD);
+      if (LD_IN_STEPS && i == LD_STEP_V)
+        issue_rows(vslice, rbv, ld_off_v, ld_off_v_rag, load_of(it), V_LOAD);
       // P(j) = exp2(S(j) * c - m), skewed over three steps (SK = 1): the
       // argument of this step's scores, the exp2 of the previous step's,
       // the sums and conversion of the one before, so that no op of a step
@@ -1181,12 +1192,13 @@ struct SplitPlan {
 
 // off: the causal offset (query i sees key j <= i + off), Sk - Sq unless
 // the caller gives another (a key shard of a longer sequence).  The plan of
-// 4-wave workgroups of 32 rows per wave: one or two groups, key split as
-// asked (kv_split > 1), automatic (0) or none (1).
+// 4-wave workgroups of 32 rows per wave: one or two groups (kh = 1), or
+// key halves (kh = 2: 2 row waves x 2 key halves), key split as asked
+// (kv_split > 1), automatic (0) or none (1).
 SplitPlan make_split_plan_rows(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
-                               int kv_split, int off) {
+                               int kv_split, int off, int kh = 1) {
   SplitPlan sp{};
-  sp.base = make_plan(B, Sq, Sk, Hq, Hkv, d, causal);
+  sp.base = make_plan(B, Sq, Sk, Hq, Hkv, d, causal, kh);
   const Plan& pl = sp.base;
   sp.chunk = 0;
   sp.npieces = 1;
@@ -1195,7 +1207,7 @@ SplitPlan make_split_plan_rows(int B, int Sq, int Sk, int Hq, int Hkv, int d, in
   if (pl.grid <= 0) return sp;
   // tiles of the longest row block (the last one: causal rows see the most keys)
   const int nmax = block_tiles((pl.qtiles - 1) * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0);
-  sp.base.ng = two_groups(pl.grid, d, nmax) ? 2 : 1;
+  sp.base.ng = kh == 1 && two_groups(pl.grid, d, nmax) ? 2 : 1;
   if (kv_split == 1) return sp;
   int chunk;
   if (kv_split == 0) {
@@ -1234,7 +1246,7 @@ SplitPlan make_split_plan_rows(int B, int Sq, int Sk, int Hq, int Hkv, int d, in
     for (int qt = 0; qt < pl.qtiles; ++qt)
       active += block_pieces(block_tiles(qt * pl.rows_wg, pl.rows_wg, Sq, Sk, off, causal != 0),
                              chunk);
-    sp.base.ng = two_groups(active * pl.ncols, d, chunk) ? 2 : 1;
+    sp.base.ng = kh == 1 && two_groups(active * pl.ncols, d, chunk) ? 2 : 1;
   }
   sp.merge_rows = (long long)B * (Sq - sp.q_first) * Hq;
   const int D = padded_head(d);
@@ -1260,9 +1272,15 @@ SplitPlan make_split_plan_rows(int B, int Sq, int Sk, int Hq, int Hkv, int d, in
 // against 12.1, whose split takes 8 pieces: many short pieces and the merge
 // beat one long chain of half tiles.
 constexpr int kSplitOverKeyHalves = 6;
+//
+// fp16 at padded head size 256 runs key halves, split or not: the 4-wave
+// kernel's hi + lo P halves leave it short of registers there, and it spilled
+// into scratch (measured on MI355X, 8K GQA heads at d = 256: 13.4 ms against
+// 1.95 ms with key halves; bf16 keeps the 4-wave kernel, 1.21 against 1.64 ms).
 SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
-                          int kv_split, int off) {
-  const SplitPlan sp = make_split_plan_rows(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, off);
+                          int kv_split, int off, int dtype) {
+  const int kh0 = padded_head(d) == 256 && dtype == ATTN_DTYPE_F16 ? 2 : 1;
+  const SplitPlan sp = make_split_plan_rows(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, off, kh0);
   if (sp.grid > 0 && sp.chunk == 0 && padded_head(d) == 192) {
     // unsplit at d = 192: the same grid in 8-wave workgroups of key halves
     SplitPlan e = sp;
@@ -1321,6 +1339,12 @@ hipError_t launch_t(const Plan& pl, long long nwg, const Params& p, hipStream_t 
       hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 2, 1, 4>), grid, block, 0, st, p);
       return hipGetLastError();
     }
+    if (pl.kh == 2 && pl.nw == 4) {
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 2, 4>), grid, block, 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (D == 256) {
     if (pl.kh == 2 && pl.nw == 4) {
       hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 2, 4>), grid, block, 0, st, p);
       return hipGetLastError();
@@ -1485,7 +1509,7 @@ attn_status run_forward(const void* q, const void* k, const void* v, void* o, fl
   if (decode_eligible(Sq, Hq, Hkv, d))
     return run_decode(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, scale, causal, dtype, st, kv_split,
                       workspace, workspace_bytes, hs, nullptr, off);
-  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, off);
+  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, off, dtype);
   if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   if (sp.chunk > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255u) ||
                        workspace_bytes < sp.ws_bytes))
@@ -1614,7 +1638,7 @@ attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
                                   Hkv, d, 1.0f, causal, dtype);
   if (st != ATTN_OK) return st;
   // attn_fwd: no key split
-  const Plan pl = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, 1, Sk - Sq).base;
+  const Plan pl = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, 1, Sk - Sq, dtype).base;
   int vals[11] = {pl.grid, pl.ng * pl.nw * 64, pl.rows_wg, BC, pl.gh, 32 * pl.qb,
                   pl.ng * pl.lds_bytes, pl.xcd_cols > 0 || pl.xcd_qsplit > 0 ? 1 : 0,
                   pl.pipelined, 0, pl.kh == 2 ? 1 : 0};
@@ -1659,7 +1683,7 @@ attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, i
     for (int i = 0; i < n && i < 7; ++i) out[i] = vals[i];
     return ATTN_OK;
   }
-  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, Sk - Sq);
+  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, Sk - Sq, dtype);
   if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   const int vals[7] = {(int)sp.grid, sp.npieces, sp.chunk * BC, sp.q_first,
                        (int)sp.merge_grid, sp.base.ng * sp.base.nw * 64,
@@ -1676,7 +1700,7 @@ attn_status attn_fwd_split_workspace(int B, int Sq, int Sk, int Hq, int Hkv, int
   if (st != ATTN_OK) return st;
   *bytes = decode_eligible(Sq, Hq, Hkv, d)
                ? make_decode_plan(B, Sq, Sk, Hq, Hkv, d, kv_split).ws_bytes
-               : make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, Sk - Sq).ws_bytes;
+               : make_split_plan(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, Sk - Sq, dtype).ws_bytes;
   return ATTN_OK;
 }
 
@@ -1739,7 +1763,7 @@ attn_status attn_fwd_causal_offset_workspace(int B, int Sq, int Sk, int Hq, int 
     *bytes = dp.ws_bytes;
     return ATTN_OK;
   }
-  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, 1, kv_split, (int)causal_offset);
+  const SplitPlan sp = make_split_plan(B, Sq, Sk, Hq, Hkv, d, 1, kv_split, (int)causal_offset, dtype);
   if (sp.grid <= 0) return ATTN_ERR_INVALID_ARG;
   *bytes = sp.ws_bytes;
   return ATTN_OK;

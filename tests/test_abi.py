@@ -776,18 +776,22 @@ def test_plan_queries_agree_over_random_shapes():
         assert s1["key_halves"] == fp["key_halves"], cfg
         if fp["decode"]:
             continue
+        f16_256 = D == 256 and dt == ATTN_DTYPE_F16  # key halves, split or not
         if fp["key_halves"]:
-            assert D <= 192, cfg
             if D == 192:
                 assert fp["threads"] == 512, cfg
             else:
-                assert D <= 128 and fp["threads"] == 256, cfg
+                assert (D <= 128 or f16_256) and fp["threads"] == 256, cfg
         elif D == 192:
             raise AssertionError(f"unsplit d = {d} without the 8-wave key halves: {cfg}")
-        if s0["key_halves"]:
+        elif f16_256:
+            raise AssertionError(f"fp16 d = {d} without the key halves: {cfg}")
+        if f16_256:
+            assert s0["key_halves"] == 1, cfg
+        elif s0["key_halves"]:
             assert s0["pieces"] == 1 and ws0 == 0 and s0["merge_grid"] == 0, cfg
         if s0["pieces"] > 1:
-            assert ws0 > 0 and s0["merge_grid"] > 0 and s0["key_halves"] == 0, cfg
+            assert ws0 > 0 and s0["merge_grid"] > 0 and s0["key_halves"] == int(f16_256), cfg
             if D <= 128 and fp["key_halves"] == 1:
                 assert s0["pieces"] >= 6, cfg  # the key halves give way only to long splits
         else:

@@ -348,3 +348,26 @@ def test_padded_head_sizes_decode_strided(d):
                                   kv_split=kv_split)
         torch.cuda.synchronize()
         _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
+
+
+@pytest.mark.parametrize("d,Sq,Sk,causal,kv_split", [
+    (256, 700, 700, True, 1),
+    (256, 300, 2000, True, 3),
+    (248, 513, 1000, False, 1),
+    (200, 333, 1500, True, 0),
+])
+def test_f16_head_size_256_key_halves(d, Sq, Sk, causal, kv_split):
+    """fp16 at padded head size 256 runs the key halves (unsplit and in the
+    pieces of a key split)."""
+    from exact_attention_19_amd import attn_fwd_split, attn_fwd_split_plan
+    from exact_attention_19_amd.binding import ATTN_DTYPE_F16
+    w = _w(f"f16_hd{d}_kh_{Sq}_{Sk}", 2, 8, 2, Sq, Sk, d, "f16", causal)
+    plan = attn_fwd_split_plan(w.B, Sq, Sk, w.Hq, w.Hkv, d, int(causal), ATTN_DTYPE_F16, kv_split)
+    assert plan["key_halves"] == 1
+    q, k, v = make_inputs(w, seed=d + Sq + Sk)
+    _say(f"[gpu] attn_fwd_split fp16 head size {d} {w.name} kv_split={kv_split} "
+         f"(pieces {plan['pieces']})")
+    o, lse = attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, causal=causal,
+                            kv_split=kv_split)
+    torch.cuda.synchronize()
+    _check_full(w, q, k, v, o.cpu(), lse.cpu(), strict=False)
