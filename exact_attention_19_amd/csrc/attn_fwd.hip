@@ -1196,9 +1196,9 @@ struct SplitPlan {
 // key halves (kh = 2: 2 row waves x 2 key halves), key split as asked
 // (kv_split > 1), automatic (0) or none (1).
 SplitPlan make_split_plan_rows(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
-                               int kv_split, int off, int kh = 1) {
+                               int kv_split, int off, int kh = 1, int nw = 4) {
   SplitPlan sp{};
-  sp.base = make_plan(B, Sq, Sk, Hq, Hkv, d, causal, kh);
+  sp.base = make_plan(B, Sq, Sk, Hq, Hkv, d, causal, kh, nw);
   const Plan& pl = sp.base;
   sp.chunk = 0;
   sp.npieces = 1;
@@ -1273,14 +1273,19 @@ SplitPlan make_split_plan_rows(int B, int Sq, int Sk, int Hq, int Hkv, int d, in
 // beat one long chain of half tiles.
 constexpr int kSplitOverKeyHalves = 6;
 //
-// fp16 at padded head size 256 runs key halves, split or not: the 4-wave
-// kernel's hi + lo P halves leave it short of registers there, and it spilled
-// into scratch (measured on MI355X, 8K GQA heads at d = 256: 13.4 ms against
-// 1.95 ms with key halves; bf16 keeps the 4-wave kernel, 1.21 against 1.64 ms).
+// fp16 at padded head sizes 192 and 256 runs key halves (8 and 4 waves),
+// split or not: the 4-wave kernel's hi + lo P halves leave it short of
+// registers there, and it spilled into scratch (measured on MI355X, 8K GQA
+// heads at d = 256: 14.4 ms against 1.9 ms with key halves, bf16 keeping the
+// 4-wave kernel at 1.19 ms, against 1.64 with key halves; 1280 x 1536 causal
+// at d = 192 cut into 2 key pieces: 471 us against 50 us unsplit).
 SplitPlan make_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
                           int kv_split, int off, int dtype) {
-  const int kh0 = padded_head(d) == 256 && dtype == ATTN_DTYPE_F16 ? 2 : 1;
-  const SplitPlan sp = make_split_plan_rows(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, off, kh0);
+  const bool f16_wide = dtype == ATTN_DTYPE_F16 && padded_head(d) > 128;
+  const int kh0 = f16_wide ? 2 : 1;
+  const int nw0 = f16_wide && padded_head(d) == 192 ? 8 : 4;
+  const SplitPlan sp =
+      make_split_plan_rows(B, Sq, Sk, Hq, Hkv, d, causal, kv_split, off, kh0, nw0);
   if (sp.grid > 0 && sp.chunk == 0 && padded_head(d) == 192) {
     // unsplit at d = 192: the same grid in 8-wave workgroups of key halves
     SplitPlan e = sp;
@@ -1356,8 +1361,13 @@ hipError_t launch_t(const Plan& pl, long long nwg, const Params& p, hipStream_t 
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 1, 4>), grid, block, 0, st, p);
-  return hipGetLastError();
+  if constexpr (DT == ATTN_DTYPE_F16 && D > 128) {
+    // fp16 above 128 always plans key halves; the 4-wave kernel is not built
+    return hipErrorInvalidConfiguration;
+  } else {
+    hipLaunchKernelGGL((attn_fwd_pipe_kernel<DT, D, CAUSAL, 1, 1, 4>), grid, block, 0, st, p);
+    return hipGetLastError();
+  }
 }
 
 template <int DT, int D>

@@ -749,11 +749,13 @@ def test_two_group_workgroups_for_split_pieces():
 def test_plan_queries_agree_over_random_shapes():
     """For 3000 seeded random shapes (both dtypes, causal or not, GQA groups,
     head sizes 8..256): attn_fwd_plan equals the unsplit split plan; the
-    8-wave key halves appear exactly at padded head size 192 unsplit; the
-    4-wave key halves only at padded head sizes up to 128 and at most 256
-    four-row-wave workgroups; a plan with key halves never splits and needs
-    no workspace; a split plan needs a workspace and a merge; the automatic
-    split never takes 6 or more pieces where the key halves could run."""
+    8-wave key halves appear exactly at padded head size 192 unsplit (and at
+    192 split too for fp16); the 4-wave key halves only at padded head sizes
+    up to 128, at most 256 four-row-wave workgroups, and fp16 at padded 256,
+    split or not; apart from fp16 above 128, a plan with key halves never
+    splits and needs no workspace; a split plan needs a workspace and a
+    merge; the automatic split never takes 6 or more pieces where the key
+    halves could run."""
     import random
     _lib()
     rng = random.Random(1234)
@@ -776,7 +778,7 @@ def test_plan_queries_agree_over_random_shapes():
         assert s1["key_halves"] == fp["key_halves"], cfg
         if fp["decode"]:
             continue
-        f16_256 = D == 256 and dt == ATTN_DTYPE_F16  # key halves, split or not
+        f16_256 = D > 128 and dt == ATTN_DTYPE_F16  # key halves, split or not
         if fp["key_halves"]:
             if D == 192:
                 assert fp["threads"] == 512, cfg
@@ -787,7 +789,7 @@ def test_plan_queries_agree_over_random_shapes():
         elif f16_256:
             raise AssertionError(f"fp16 d = {d} without the key halves: {cfg}")
         if f16_256:
-            assert s0["key_halves"] == 1, cfg
+            assert s0["key_halves"] == 1 and s0["threads"] == (512 if D == 192 else 256), cfg
         elif s0["key_halves"]:
             assert s0["pieces"] == 1 and ws0 == 0 and s0["merge_grid"] == 0, cfg
         if s0["pieces"] > 1:

@@ -355,10 +355,14 @@ def test_padded_head_sizes_decode_strided(d):
     (256, 300, 2000, True, 3),
     (248, 513, 1000, False, 1),
     (200, 333, 1500, True, 0),
+    (192, 1280, 1536, True, 2),
+    (176, 300, 2000, True, 3),
+    (184, 513, 1000, False, 0),
+    (192, 64, 4096, False, 0),
 ])
 def test_f16_head_size_256_key_halves(d, Sq, Sk, causal, kv_split):
-    """fp16 at padded head size 256 runs the key halves (unsplit and in the
-    pieces of a key split)."""
+    """fp16 at padded head sizes 192 and 256 runs the key halves (unsplit and
+    in the pieces of a key split)."""
     from exact_attention_19_amd import attn_fwd_split, attn_fwd_split_plan
     from exact_attention_19_amd.binding import ATTN_DTYPE_F16
     w = _w(f"f16_hd{d}_kh_{Sq}_{Sk}", 2, 8, 2, Sq, Sk, d, "f16", causal)
