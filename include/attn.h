@@ -129,9 +129,9 @@ attn_status attn_fwd_check(const void* q, const void* k, const void* v,
  *       rows, one the first and one the second 32 keys of every tile, and
  *       their two partial states are merged in the workgroup.  With 4 waves
  *       (rows per workgroup halve, workgroups double) when the plain grid
- *       would leave most CUs with one workgroup; with 8 waves ([1] = 512,
- *       the plain grid) at padded head size 192, whose tile buffers leave
- *       one workgroup per CU
+ *       would leave most CUs with one workgroup, and always for fp16 at
+ *       padded head size 256; with 8 waves ([1] = 512, the plain grid) at
+ *       padded head size 192, whose tile buffers leave one workgroup per CU
  * Returns the status attn_fwd_check would return.
  */
 attn_status attn_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
@@ -304,9 +304,11 @@ attn_status attn_fwd_split_workspace(int B, int Sq, int Sk, int Hq, int Hkv,
  *   [3] first query row of a split block (Sq when nothing is split)
  *   [4] merge workgroups (0 when nothing is split)
  *   [5] threads per attention workgroup (512: two 4-wave groups that take
- *       alternate key tiles of the same rows, as attn_fwd_plan [1])
+ *       alternate key tiles of the same rows, or 8 waves of key halves at
+ *       padded head size 192, as attn_fwd_plan [1])
  *   [6] 1 if the waves take key halves (as attn_fwd_plan [10]; then nothing
- *       is split)
+ *       is split, except for fp16 above head size 128, whose pieces of a
+ *       split also run key halves)
  */
 attn_status attn_fwd_split_plan(int B, int Sq, int Sk, int Hq, int Hkv, int d,
                                 int causal, int dtype, int kv_split, int* out,
