@@ -15,7 +15,8 @@
 //
 // Three launches on one stream:
 //   prep   D_i and lse_i * log2(e) per query row (memory-bound),
-//   dq     query-row outer, like the forward: one wave owns 32 query rows,
+//   dq     query-row outer, like the forward: one wave owns 32 query rows
+//          (at d = 192 two waves, each over half the keys of every tile),
 //          K and V tiles stream through LDS, dQ^T = K^T dS^T accumulates in
 //          registers,
 //   dkdv   key outer: two waves own 32 keys of one kv head (each half of
@@ -111,12 +112,22 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ dQ
-template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdParams p) {
+// KH = 2 (at d = 192): 8 waves, 4 row waves x 2 key halves.  Wave w takes
+// the rows of row wave w & 3 and the 32 keys w >> 2 of every tile, so a wave
+// holds S and dP of one 32-key block: its Q and dO fragments, dQ sums and
+// one key block fit two waves per SIMD, where all 64 keys left one.  The
+// second half's dQ sums are added to the first's through LDS at the end.
+template <int DT, int D, bool CAUSAL, int KH>
+__global__ __launch_bounds__(256 * KH, D > 128 && KH == 1 ? 1 : 2) void attn_bwd_dq_kernel(
+    BwdParams p) {
   using T = Ty<DT>;
   constexpr int CB = D / 32;
   constexpr int KK = D / 16;
   constexpr int TB = 64 * D * 2;
+  constexpr int KB = 2 / KH;  // 32-key blocks per wave and tile
+  constexpr int NF = 2 * KB;  // 16-key dS fragments per wave and tile
+  static_assert(KH == 1 || KH == 2, "one or two key halves");
+  static_assert(KH == 1 || CB * 16 * 64 * 4 <= TB, "a half's dQ sums fit one tile buffer");
   __shared__ __attribute__((aligned(1024))) char lds_k0[TB], lds_k1[TB], lds_v0[TB], lds_v1[TB];
   ATTN_POISON_LDS_ARRAY(lds_k0);
   ATTN_POISON_LDS_ARRAY(lds_k1);
@@ -128,7 +139,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wv & 3;  // row wave
+  const int kh = KH == 2 ? wv >> 2 : 0;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -200,32 +213,50 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
+  // the tile loads: with key halves the first half's waves load K and the
+  // second half's V
+  auto load_kv = [&](int n) {
+    if (KH == 1 || kh == 0) load_tile<D>(kslice, rbkv, n, p.Sk, p.d, kbuf(n), wave, lane);
+    if (KH == 1 || kh == 1) load_tile<D>(vslice, rbkv, n, p.Sk, p.d, vbuf(n), wave, lane);
+  };
   if (n_end > 0) {
-    load_tile<D>(kslice, rbkv, 0, p.Sk, p.d, kbuf(0), wave, lane);
-    load_tile<D>(vslice, rbkv, 0, p.Sk, p.d, vbuf(0), wave, lane);
+    load_kv(0);
     for (int j = 0; j < n_end; ++j) {
       // tile j has landed (this wave's loads) and every wave is done with
       // tile j - 1, whose buffers now take tile j + 1
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (j + 1 < n_end) {
-        load_tile<D>(kslice, rbkv, j + 1, p.Sk, p.d, kbuf(j + 1), wave, lane);
-        load_tile<D>(vslice, rbkv, j + 1, p.Sk, p.d, vbuf(j + 1), wave, lane);
-      }
-      LDS_PTR(char) const kt = kbuf(j);
-      LDS_PTR(char) const vt = vbuf(j);
-      // S^T = K Q^T and dP^T = V dO^T for the 64 keys of the tile
+      if (j + 1 < n_end) load_kv(j + 1);
+      // this wave's key rows of the tile: 32 kh KB .. + 32 KB
+      LDS_PTR(char) const kt = kbuf(j) + kh * KB * 32 * 64;
+      LDS_PTR(char) const vt = vbuf(j) + kh * KB * 32 * 64;
+      // S^T = K Q^T and dP^T = V dO^T for the wave's keys of the tile
       // (the fragments of the next step are read during the current one)
-      f32x16 S[2], dP[2];
+      f32x16 S[KB], dP[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           S[kb][r] = 0.f;
           dP[kb][r] = 0.f;
         }
-      {
-        constexpr int NS = 2 * KK;  // steps (kb, kk)
+      if constexpr (KH == 2) {
+        // one fragment in flight (K for S, then V for dP of the same kk):
+        // the registers of two waves per SIMD leave no room for two
+        constexpr int NS = 2 * KK;  // steps (kk, S or dP)
+        auto rd = [&](int st) { return read_row_frag(st & 1 ? vt : kt, rbase, 0, st >> 1); };
+        i16x8 fa = rd(0), fb;
+#pragma unroll
+        for (int st = 0; st < NS; st += 2) {
+          fb = rd(st + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          S[0] = T::mfma(fa, qf[st >> 1], S[0]);
+          if (st + 2 < NS) fa = rd(st + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          dP[0] = T::mfma(fb, dof[st >> 1], dP[0]);
+        }
+      } else {
+        constexpr int NS = KB * KK;  // steps (kb, kk)
         auto rd = [&](int st, i16x8 (&f)[2]) {
           f[0] = read_row_frag(kt, rbase, st / KK, st % KK);
           f[1] = read_row_frag(vt, rbase, st / KK, st % KK);
@@ -246,8 +277,8 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
       }
       if (j >= n_full) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int L = lim_row - j * 64 - kb * 32 - 8 * hh;
+        for (int kb = 0; kb < KB; ++kb) {
+          const int L = lim_row - j * 64 - (kh * KB + kb) * 32 - 8 * hh;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (key_of_reg(r) > L) S[kb][r] = -INFINITY;
@@ -255,9 +286,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
       }
       // dS^T = P^T (dP^T - D), rounded to 16 bit: registers 8t'..8t'+7 are
       // keys 16t' + 8hh + 0..7, the B operand of the next product
-      i16x8 dsf[4];
+      i16x8 dsf[NF];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
+      for (int f = 0; f < NF; ++f) {
         f32x8 e;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -269,7 +300,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
       }
       // dQ^T += K^T dS^T (fragments one step ahead)
       {
-        constexpr int NS = 4 * CB;  // steps (f, cb)
+        constexpr int NS = NF * CB;  // steps (f, cb)
         i16x8 fa = read_tr_frag(kt, tbase, 0, 0), fb;
 #pragma unroll
         for (int st = 0; st < NS; st += 2) {
@@ -282,6 +313,28 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_bwd_dq_kernel(BwdPa
         }
       }
     }
+  }
+
+  if constexpr (KH == 2) {
+    // the second half's sums go through the tile buffer of its row wave
+    // (lane-major, conflict free), once every wave is done with the tiles
+    __syncthreads();
+    LDS_PTR(float) const xs = (LDS_PTR(float))(wave == 0   ? (LDS_PTR(char))lds_k0
+                                               : wave == 1 ? (LDS_PTR(char))lds_k1
+                                               : wave == 2 ? (LDS_PTR(char))lds_v0
+                                                           : (LDS_PTR(char))lds_v1);
+    if (kh == 1) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[(cb * 16 + r) * 64 + lane] = acc[cb][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cb][r] += xs[(cb * 16 + r) * 64 + lane];
   }
 
   if (ok) {
@@ -734,7 +787,10 @@ hipError_t launch_bwd_t(const Plan& pl, const BwdParams& p, hipStream_t st) {
   const long long rows = (long long)p.B * p.Sq * p.Hq;
   hipLaunchKernelGGL((attn_bwd_prep_kernel<DT, D>), dim3((unsigned)((rows + 31) / 32)), dim3(256),
                      0, st, p);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3(pl.grid), dim3(256), 0, st, p);
+  // key halves at d = 192 (8 waves, two per SIMD); one wave per SIMD at 256
+  constexpr int DQ_KH = D == 192 ? 2 : 1;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, DQ_KH>), dim3(pl.grid), dim3(256 * DQ_KH),
+                     0, st, p);
   // 8 waves over 32 keys per key group: 4 groups up to d = 128, 2 above
   constexpr int KG = D > 128 ? 2 : 4;
   const long long kgrid = (long long)p.B * p.Hkv * ((p.Sk + 32 * KG - 1) / (32 * KG));
