@@ -16,7 +16,8 @@
 // Three launches on one stream:
 //   prep   D_i and lse_i * log2(e) per query row (memory-bound),
 //   dq     query-row outer, like the forward: one wave owns 32 query rows
-//          (at d = 192 two waves, each over half the keys of every tile),
+//          (at d = 192, and up to 128 on grids of at most 256 workgroups,
+//          two waves, each over half the keys of every tile),
 //          K and V tiles stream through LDS, dQ^T = K^T dS^T accumulates in
 //          registers,
 //   dkdv   key outer: two waves own 32 keys of one kv head (each half of
@@ -112,7 +113,8 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ dQ
-// KH = 2 (at d = 192): 8 waves, 4 row waves x 2 key halves.  Wave w takes
+// KH = 2 (at d = 192, and up to 128 when the grid leaves each CU at most
+// one workgroup): 8 waves, 4 row waves x 2 key halves.  Wave w takes
 // the rows of row wave w & 3 and the 32 keys w >> 2 of every tile, so a wave
 // holds S and dP of one 32-key block: its Q and dO fragments, dQ sums and
 // one key block fit two waves per SIMD, where all 64 keys left one.  The
@@ -787,10 +789,24 @@ hipError_t launch_bwd_t(const Plan& pl, const BwdParams& p, hipStream_t st) {
   const long long rows = (long long)p.B * p.Sq * p.Hq;
   hipLaunchKernelGGL((attn_bwd_prep_kernel<DT, D>), dim3((unsigned)((rows + 31) / 32)), dim3(256),
                      0, st, p);
-  // key halves at d = 192 (8 waves, two per SIMD); one wave per SIMD at 256
-  constexpr int DQ_KH = D == 192 ? 2 : 1;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, DQ_KH>), dim3(pl.grid), dim3(256 * DQ_KH),
-                     0, st, p);
+  // dQ: key halves (8 waves, two per SIMD, each over half the keys) at
+  // d = 192, and up to 128 when the grid leaves each CU at most one
+  // workgroup; 4 waves otherwise (one per SIMD at 256)
+  bool dq_kh = false;
+  if constexpr (D == 192) dq_kh = true;
+  if constexpr (D <= 128) dq_kh = pl.grid <= 256;
+  if constexpr (D <= 192) {
+    if (dq_kh) {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, 2>), dim3(pl.grid), dim3(512), 0, st,
+                         p);
+    }
+  }
+  if (!dq_kh) {
+    if constexpr (D != 192) {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, 1>), dim3(pl.grid), dim3(256), 0, st,
+                         p);
+    }
+  }
   // 8 waves over 32 keys per key group: 4 groups up to d = 128, 2 above
   constexpr int KG = D > 128 ? 2 : 4;
   const long long kgrid = (long long)p.B * p.Hkv * ((p.Sk + 32 * KG - 1) / (32 * KG));
