@@ -16,8 +16,8 @@
 // Three launches on one stream:
 //   prep   D_i and lse_i * log2(e) per query row (memory-bound),
 //   dq     query-row outer, like the forward: one wave owns 32 query rows
-//          (at d = 192, and up to 128 on grids of at most 256 workgroups,
-//          two waves, each over half the keys of every tile),
+//          (at d = 192, and up to 128 on grids of at most 256 workgroups of
+//          128 rows, two waves, each over half the keys of every tile),
 //          K and V tiles stream through LDS, dQ^T = K^T dS^T accumulates in
 //          registers,
 //   dkdv   key outer: two waves own 32 keys of one kv head (each half of
@@ -113,14 +113,15 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ dQ
-// KH = 2 (at d = 192, and up to 128 when the grid leaves each CU at most
-// one workgroup): 8 waves, 4 row waves x 2 key halves.  Wave w takes
+// KH = 2, NWD = 8 (at d = 192): 8 waves, 4 row waves x 2 key halves.  Wave w takes
 // the rows of row wave w & 3 and the 32 keys w >> 2 of every tile, so a wave
 // holds S and dP of one 32-key block: its Q and dO fragments, dQ sums and
 // one key block fit two waves per SIMD, where all 64 keys left one.  The
 // second half's dQ sums are added to the first's through LDS at the end.
-template <int DT, int D, bool CAUSAL, int KH>
-__global__ __launch_bounds__(256 * KH, D > 128 && KH == 1 ? 1 : 2) void attn_bwd_dq_kernel(
+// With 4 waves and KH = 2 (up to d = 128): 2 row waves x 2 key halves over
+// 64-row workgroups (the forward's key-halves plan), twice as many.
+template <int DT, int D, bool CAUSAL, int KH, int NWD>
+__global__ __launch_bounds__(64 * NWD, D > 128 && KH == 1 ? 1 : 2) void attn_bwd_dq_kernel(
     BwdParams p) {
   using T = Ty<DT>;
   constexpr int CB = D / 32;
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(256 * KH, D > 128 && KH == 1 ? 1 : 2) void attn_bwd
   constexpr int KB = 2 / KH;  // 32-key blocks per wave and tile
   constexpr int NF = 2 * KB;  // 16-key dS fragments per wave and tile
   static_assert(KH == 1 || KH == 2, "one or two key halves");
+  static_assert(NWD == 4 * KH || (NWD == 4 && KH == 2 && D <= 128), "4 or 8 waves");
   static_assert(KH == 1 || CB * 16 * 64 * 4 <= TB, "a half's dQ sums fit one tile buffer");
   __shared__ __attribute__((aligned(1024))) char lds_k0[TB], lds_k1[TB], lds_v0[TB], lds_v1[TB];
   ATTN_POISON_LDS_ARRAY(lds_k0);
@@ -142,8 +144,9 @@ __global__ __launch_bounds__(256 * KH, D > 128 && KH == 1 ? 1 : 2) void attn_bwd
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave = wv & 3;  // row wave
-  const int kh = KH == 2 ? wv >> 2 : 0;
+  constexpr int RW = NWD / KH;  // row waves
+  const int wave = wv & (RW - 1);  // row wave
+  const int kh = KH == 2 ? wv / RW : 0;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -215,11 +218,11 @@ __global__ __launch_bounds__(256 * KH, D > 128 && KH == 1 ? 1 : 2) void attn_bwd
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-  // the tile loads: with key halves the first half's waves load K and the
-  // second half's V
+  // the tile loads, spread over 4 waves: with 8 waves the first half's
+  // waves load K and the second half's V
   auto load_kv = [&](int n) {
-    if (KH == 1 || kh == 0) load_tile<D>(kslice, rbkv, n, p.Sk, p.d, kbuf(n), wave, lane);
-    if (KH == 1 || kh == 1) load_tile<D>(vslice, rbkv, n, p.Sk, p.d, vbuf(n), wave, lane);
+    if (NWD == 4 || kh == 0) load_tile<D>(kslice, rbkv, n, p.Sk, p.d, kbuf(n), wv & 3, lane);
+    if (NWD == 4 || kh == 1) load_tile<D>(vslice, rbkv, n, p.Sk, p.d, vbuf(n), wv & 3, lane);
   };
   if (n_end > 0) {
     load_kv(0);
@@ -789,22 +792,36 @@ hipError_t launch_bwd_t(const Plan& pl, const BwdParams& p, hipStream_t st) {
   const long long rows = (long long)p.B * p.Sq * p.Hq;
   hipLaunchKernelGGL((attn_bwd_prep_kernel<DT, D>), dim3((unsigned)((rows + 31) / 32)), dim3(256),
                      0, st, p);
-  // dQ: key halves (8 waves, two per SIMD, each over half the keys) at
-  // d = 192, and up to 128 when the grid leaves each CU at most one
-  // workgroup; 4 waves otherwise (one per SIMD at 256)
-  bool dq_kh = false;
-  if constexpr (D == 192) dq_kh = true;
-  if constexpr (D <= 128) dq_kh = pl.grid <= 256;
-  if constexpr (D <= 192) {
-    if (dq_kh) {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, 2>), dim3(pl.grid), dim3(512), 0, st,
-                         p);
+  // dQ: key halves (two waves over the same rows, each over half the keys
+  // of every tile): at d = 192 8 waves (two per SIMD); up to 128, when the
+  // grid leaves each CU at most one workgroup, the forward's key-halves plan
+  // (64-row workgroups of 4 waves, twice as many); 4 waves otherwise (one per
+  // SIMD at 256)
+  if constexpr (D == 192) {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, 2, 8>), dim3(pl.grid), dim3(512), 0, st,
+                       p);
+  } else {
+    const Plan kp = D <= 128 && pl.grid <= 256
+                        ? make_plan(p.B, p.Sq, p.Sk, p.Hq, p.Hkv, p.d, CAUSAL, 2, 4)
+                        : Plan{};
+    bool launched = false;
+    if constexpr (D <= 128) {
+      if (kp.grid > 0) {
+        BwdParams pq = p;
+        pq.gh = kp.gh;
+        pq.hsub = pq.group / kp.gh;
+        pq.rows_wg = kp.rows_wg;
+        pq.qtiles = kp.qtiles;
+        pq.ncols = kp.ncols;
+        pq.xcd_cols = kp.xcd_cols;
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, 2, 4>), dim3(kp.grid), dim3(256), 0,
+                           st, pq);
+        launched = true;
+      }
     }
-  }
-  if (!dq_kh) {
-    if constexpr (D != 192) {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, 1>), dim3(pl.grid), dim3(256), 0, st,
-                         p);
+    if (!launched) {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, 1, 4>), dim3(pl.grid), dim3(256), 0,
+                         st, p);
     }
   }
   // 8 waves over 32 keys per key group: 4 groups up to d = 128, 2 above
